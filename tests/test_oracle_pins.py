@@ -1,0 +1,397 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself:
+closed forms, textbook constants, brute-force loops on tiny inputs, central
+finite differences, the sharding invariants the pages state, library routines
+used as cross-checks (tests only) and the pages' worked example."""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import bf16 as ob
+from tests import brute
+from workloads import CONFIGS, mlp_inputs, shard_cols, shard_rows
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- bf16 rounding
+class TestBf16:
+    def test_representable_values_are_fixed_points(self):
+        vals = np.array([0.0, 1.0, -2.5, 0.0078125, 3.0 * 2.0 ** -130,  # subnormal
+                         2.0 ** -126, (2 - 2.0 ** -7) * 2.0 ** 127, -96.0])
+        np.testing.assert_array_equal(ob.round_to_bf16(vals), vals)
+
+    def test_ties_to_even_and_carry(self):
+        # 1 + 2^-8 lies half-way between 1 (mantissa 0, even) and 1 + 2^-7 (odd).
+        assert ob.round_to_bf16(1.0 + 2.0 ** -8) == 1.0
+        # 1 + 3*2^-8 lies half-way between 1 + 2^-7 (odd) and 1 + 2^-6 (even).
+        assert ob.round_to_bf16(1.0 + 3 * 2.0 ** -8) == 1.0 + 2.0 ** -6
+        # just above a tie rounds up
+        assert ob.round_to_bf16(1.0 + 2.0 ** -8 + 2.0 ** -30) == 1.0 + 2.0 ** -7
+        # 2 - 2^-8 lies half-way between 2 - 2^-7 (mantissa 127, odd) and 2: carry.
+        assert ob.round_to_bf16(2.0 - 2.0 ** -8) == 2.0
+        # overflow: the midpoint of the largest finite bf16 and 2^128 goes to inf
+        big = (2 - 2.0 ** -7) * 2.0 ** 127
+        assert ob.round_to_bf16(big + 2.0 ** 119) == np.inf
+        assert ob.round_to_bf16(-(big + 2.0 ** 119)) == -np.inf
+        assert ob.round_to_bf16(big + 2.0 ** 118) == big
+
+    def test_bit_patterns(self):
+        assert ob.f64_to_bf16_bits(np.array([1.0]))[0] == 0x3F80
+        assert ob.f64_to_bf16_bits(np.array([-2.0]))[0] == 0xC000
+        assert ob.f64_to_bf16_bits(np.array([2.0 ** -133]))[0] == 0x0001
+        assert ob.f64_to_bf16_bits(np.array([np.inf]))[0] == 0x7F80
+
+    def test_all_patterns_roundtrip_and_decode(self):
+        bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+        vals = ob.bf16_bits_to_f64(bits)
+        finite = np.isfinite(vals)
+        # decode agrees with widening the pattern into the top half of a float32
+        widened = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        np.testing.assert_array_equal(vals[finite], widened[finite])
+        np.testing.assert_array_equal(ob.f64_to_bf16_bits(vals[finite]), bits[finite])
+
+    def test_matches_torch_conversion_on_float32(self):
+        rng = np.random.default_rng(7)
+        x = np.concatenate([rng.standard_normal(20000).astype(np.float32) * s
+                            for s in (1e-3, 1.0, 1e3, 1e-38)])
+        ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+        np.testing.assert_array_equal(ob.round_to_bf16(x.astype(np.float64)), ref)
+
+
+# ---------------------------------------------------------------- GeLU
+class TestGelu:
+    def test_closed_forms(self):
+        assert oracle.gelu(0.0) == 0.0
+        # Phi(1) = 0.841344746068542948..., a textbook constant
+        assert abs(oracle.gelu(1.0) - 0.8413447460685429) < 1e-15
+        assert abs(oracle.gelu_prime(0.0) - 0.5) < 1e-16
+        x = np.linspace(-6, 6, 1001)
+        # Phi(x) + Phi(-x) = 1  =>  GeLU(x) - GeLU(-x) = x
+        np.testing.assert_allclose(oracle.gelu(x) - oracle.gelu(-x), x, rtol=0, atol=1e-14)
+        assert abs(oracle.gelu(12.0) - 12.0) < 1e-20
+        assert abs(oracle.gelu(-12.0)) < 1e-30
+
+    def test_against_math_erf(self):
+        for x in np.linspace(-5, 5, 97):
+            assert abs(oracle.gelu(x) - brute.gelu(float(x))) <= 1e-15 * max(1, abs(x))
+
+    def test_derivative_by_central_difference(self):
+        x = np.linspace(-5, 5, 201)
+        eps = 1e-5
+        fd = (oracle.gelu(x + eps) - oracle.gelu(x - eps)) / (2 * eps)
+        np.testing.assert_allclose(oracle.gelu_prime(x), fd, rtol=0, atol=1e-9)
+
+
+# ---------------------------------------------------------------- MLP forward
+def _f64(a, dtype):
+    return a.astype(np.float64) if dtype == "f32" else ob.bf16_bits_to_f64(a)
+
+
+class TestMlpForward:
+    def test_config1_brute_force(self):
+        c = CONFIGS[1]
+        inp = mlp_inputs(c["b"] * c["s"], c["h"], c["f_full"], c["N"], c["dtype"], c["seed"],
+                         c["sigma_x"], c["sigma_w"], sigma_dz=None)
+        X = _f64(inp["X"], "f32")
+        Zsum = np.zeros((X.shape[0], c["h"]))
+        for A_i, B_i in inp["shards"]:
+            A_i, B_i = _f64(A_i, "f32"), _f64(B_i, "f32")
+            z = oracle.mlp_fwd_shard(X, A_i, B_i, matched=False)["Z"]
+            zb = np.array(brute.mlp(X.tolist(), A_i.tolist(), B_i.tolist()))
+            np.testing.assert_allclose(z, zb, rtol=1e-12, atol=1e-14)
+            Zsum += z
+        Zfull = np.array(brute.mlp(X.tolist(), _f64(inp["A"], "f32").tolist(),
+                                   _f64(inp["B"], "f32").tolist()))
+        np.testing.assert_allclose(Zsum, Zfull, rtol=1e-12, atol=1e-14)
+
+    @pytest.mark.parametrize("N", [1, 2, 4, 8])
+    def test_sum_of_partials_is_unsharded_mlp(self, N):
+        inp = mlp_inputs(24, 64, 256, N, "f32", 11, 1.0, 0.05, sigma_dz=None)
+        X, A, B = (inp[k].astype(np.float64) for k in "XAB")
+        Z = sum(oracle.mlp_fwd_shard(X, a.astype(np.float64), b.astype(np.float64),
+                                     matched=False)["Z"] for a, b in inp["shards"])
+        ref = oracle.mlp_fwd_full(X, A, B)
+        assert np.max(np.abs(Z - ref)) <= 1e-12 * np.max(np.abs(ref))
+        if N == 1:
+            np.testing.assert_array_equal(
+                oracle.mlp_fwd_shard(X, A, B, matched=False)["Z"], ref)
+
+    def test_column_shards_concatenate(self):
+        inp = mlp_inputs(16, 32, 128, 4, "f32", 12, 1.0, 0.1, sigma_dz=None)
+        X, A = inp["X"].astype(np.float64), inp["A"].astype(np.float64)
+        U = np.concatenate([oracle.mlp_fwd_shard(X, a.astype(np.float64),
+                                                 b.astype(np.float64), matched=False)["U"]
+                            for a, b in inp["shards"]], axis=1)
+        Ub = np.array(brute.matmul(X.tolist(), A.tolist()))
+        np.testing.assert_allclose(U, Ub, rtol=1e-13, atol=1e-13)
+
+    def test_linear_in_B(self):
+        rng = np.random.default_rng(3)
+        X, A = rng.standard_normal((8, 16)), rng.standard_normal((16, 32))
+        B1, B2 = rng.standard_normal((32, 16)), rng.standard_normal((32, 16))
+        z = lambda B: oracle.mlp_fwd_shard(X, A, B, matched=False)["Z"]
+        np.testing.assert_allclose(z(B1 + B2), z(B1) + z(B2), rtol=1e-12, atol=1e-12)
+
+    def test_matched_mode_rounds_only_storage_points(self):
+        inp = mlp_inputs(8, 64, 128, 1, "bf16", 13, 1.0, 0.05, sigma_dz=None, full=False)
+        X, A, B = (ob.bf16_bits_to_f64(inp[k]) for k in "XAB")
+        m = oracle.mlp_fwd_shard(X, A, B, matched=True)
+        np.testing.assert_array_equal(m["U"], ob.round_to_bf16(X @ A))
+        np.testing.assert_array_equal(m["Y"], ob.round_to_bf16(oracle.gelu(X @ A)))
+        np.testing.assert_allclose(m["Z"], m["Y"] @ B, rtol=1e-14)
+
+    def test_sampled_rows_equal_full(self):
+        inp = mlp_inputs(40, 64, 96, 1, "bf16", 14, 1.0, 0.05, sigma_dz=None, full=False)
+        X, A, B = (ob.bf16_bits_to_f64(inp[k]) for k in "XAB")
+        full = oracle.mlp_fwd_shard(X, A, B)
+        rows = np.array([0, 7, 39])
+        part = oracle.mlp_fwd_rows(X, A, B, rows)
+        for k in ("U", "Y", "Z"):
+            np.testing.assert_allclose(part[k], full[k][rows], rtol=1e-14, atol=1e-15)
+
+
+# ---------------------------------------------------------------- MLP backward
+class TestMlpBackward:
+    def _tiny(self, N=2, seed=21):
+        inp = mlp_inputs(6, 8, 32, N, "f32", seed, 1.0, 0.3, sigma_dz=1.0)
+        return {k: (v.astype(np.float64) if isinstance(v, np.ndarray) else v)
+                for k, v in inp.items()}
+
+    def test_finite_differences(self):
+        inp = self._tiny()
+        X, dZ = inp["X"], inp["dZ"]
+        eps = 1e-6
+        for A_i, B_i in inp["shards"]:
+            A_i, B_i = A_i.astype(np.float64), B_i.astype(np.float64)
+            f = oracle.mlp_fwd_shard(X, A_i, B_i, matched=False)
+            g = oracle.mlp_bwd_shard(X, A_i, B_i, f["U"], f["Y"], dZ, matched=False)
+
+            def L(Xp=X, Ap=A_i, Bp=B_i):  # the rank's share of <dZ, Z>
+                return float(np.sum(dZ * oracle.mlp_fwd_shard(Xp, Ap, Bp, matched=False)["Z"]))
+
+            for (arr, key, idx) in [(X, "dX", (1, 3)), (X, "dX", (5, 0)),
+                                    (A_i, "dA", (2, 7)), (A_i, "dA", (7, 0)),
+                                    (B_i, "dB", (3, 5)), (B_i, "dB", (15, 7))]:
+                p, m = arr.copy(), arr.copy()
+                p[idx] += eps
+                m[idx] -= eps
+                kw = {"dX": "Xp", "dA": "Ap", "dB": "Bp"}[key]
+                fd = (L(**{kw: p}) - L(**{kw: m})) / (2 * eps)
+                assert abs(fd - g[key][idx]) <= 1e-7 * max(1.0, abs(fd)), (key, idx, fd, g[key][idx])
+
+    @pytest.mark.parametrize("N", [1, 2, 4])
+    def test_shard_gradients_assemble_the_unsharded_ones(self, N):
+        inp = self._tiny(N=N, seed=22)
+        X, A, B, dZ = inp["X"], inp["A"], inp["B"], inp["dZ"]
+        full = oracle.mlp_bwd_full(X, A, B, dZ)
+        parts = []
+        for A_i, B_i in inp["shards"]:
+            A_i, B_i = A_i.astype(np.float64), B_i.astype(np.float64)
+            f = oracle.mlp_fwd_shard(X, A_i, B_i, matched=False)
+            parts.append(oracle.mlp_bwd_shard(X, A_i, B_i, f["U"], f["Y"], dZ, matched=False))
+        np.testing.assert_allclose(sum(p["dX"] for p in parts), full["dX"], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(np.concatenate([p["dA"] for p in parts], 1), full["dA"],
+                                   rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(np.concatenate([p["dB"] for p in parts], 0), full["dB"],
+                                   rtol=1e-12, atol=1e-13)
+
+    def test_against_torch_autograd(self):
+        inp = self._tiny(N=1, seed=23)
+        X, A, B, dZ = (torch.tensor(inp[k], dtype=torch.float64, requires_grad=True)
+                       for k in ("X", "A", "B", "dZ"))
+        Z = torch.nn.functional.gelu(X @ A) @ B  # exact (erf) GeLU by default
+        Z.backward(dZ.detach())
+        full = oracle.mlp_bwd_full(inp["X"], inp["A"], inp["B"], inp["dZ"])
+        for key, t in (("dX", X), ("dA", A), ("dB", B)):
+            np.testing.assert_allclose(full[key], t.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+    def test_sampled_backward_equals_full(self):
+        inp = mlp_inputs(24, 32, 48, 1, "bf16", 24, 1.0, 0.1, sigma_dz=1.0, full=False)
+        X, A, B, dZ = (ob.bf16_bits_to_f64(inp[k]) for k in ("X", "A", "B", "dZ"))
+        f = oracle.mlp_fwd_shard(X, A, B)
+        g = oracle.mlp_bwd_shard(X, A, B, f["U"], f["Y"], dZ)
+        rows, cols = np.array([0, 5, 23]), np.array([1, 30, 47])
+        s = oracle.mlp_bwd_cols(X, A, B, dZ, rows, cols)
+        np.testing.assert_allclose(s["dU_cols"], g["dU"][:, cols], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(s["dA_cols"], g["dA"][:, cols], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(s["dB_rows"], g["dB"][cols, :], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(s["dX_rows"], g["dX"][rows, :], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- shard sum
+class TestShardSum:
+    def test_integer_valued_partials_sum_exactly(self):
+        rng = np.random.default_rng(31)
+        parts = [rng.integers(-1000, 1000, 777).astype(np.float32) for _ in range(8)]
+        exact = np.sum(np.stack(parts).astype(np.int64), axis=0)
+        np.testing.assert_array_equal(oracle.shard_sum_f32_ordered(parts), exact)
+        np.testing.assert_array_equal(oracle.shard_sum_f64(parts), exact)
+
+    def test_single_partial_is_a_copy(self):
+        p = np.random.default_rng(32).standard_normal(100).astype(np.float32)
+        np.testing.assert_array_equal(oracle.shard_sum_f32_ordered([p]), p)
+
+    def test_order_is_left_to_right_in_float32(self):
+        # (1e8 + 1) rounds back to 1e8 in float32, so the ordered sum loses the 1.
+        parts = [np.array([1e8], np.float32), np.array([1.0], np.float32),
+                 np.array([-1e8], np.float32)]
+        assert oracle.shard_sum_f32_ordered(parts)[0] == 0.0
+        assert oracle.shard_sum_f64(parts)[0] == 1.0
+        rev = oracle.shard_sum_f32_ordered(parts[::-1])
+        assert rev[0] == 0.0 and oracle.shard_sum_f32_ordered([parts[0], parts[2], parts[1]])[0] == 1.0
+
+    def test_bf16_disjoint_supports_are_exact(self):
+        rng = np.random.default_rng(33)
+        full = ob.f64_to_bf16_bits(rng.standard_normal(64))
+        owner = rng.integers(0, 4, 64)
+        parts = [np.where(owner == i, full, np.uint16(0)).astype(np.uint16) for i in range(4)]
+        np.testing.assert_array_equal(oracle.shard_sum_bf16_ordered(parts), full)
+
+
+# ---------------------------------------------------------------- attention
+def _rand(rng, *shape, scale=1.0):
+    return rng.standard_normal(shape) * scale
+
+
+class TestAttention:
+    def test_brute_force(self):
+        rng = np.random.default_rng(41)
+        b, s, H, d, h = 2, 5, 2, 4, 8
+        X, Wqkv, Wo = _rand(rng, b * s, h), _rand(rng, h, 3 * H * d, scale=0.5), _rand(rng, H * d, h)
+        for causal in (True, False):
+            r = oracle.attn_shard(X, Wqkv, Wo, b, s, H, d, causal, matched=False)
+            QKV = brute.matmul(X.tolist(), Wqkv.tolist())
+            O = [[0.0] * (H * d) for _ in range(b * s)]
+            for bi in range(b):
+                for j in range(H):
+                    q = [row[j * d:(j + 1) * d] for row in QKV[bi * s:(bi + 1) * s]]
+                    k = [row[H * d + j * d:H * d + (j + 1) * d] for row in QKV[bi * s:(bi + 1) * s]]
+                    v = [row[2 * H * d + j * d:2 * H * d + (j + 1) * d] for row in QKV[bi * s:(bi + 1) * s]]
+                    o = brute.attention_head(q, k, v, causal)
+                    for t in range(s):
+                        O[bi * s + t][j * d:(j + 1) * d] = o[t]
+            out = brute.matmul(O, Wo.tolist())
+            np.testing.assert_allclose(r["out"], np.array(out), rtol=1e-12, atol=1e-12)
+
+    def test_first_row_sees_only_itself(self):
+        rng = np.random.default_rng(42)
+        b, s, H, d, h = 1, 7, 3, 4, 12
+        X, Wqkv, Wo = _rand(rng, s, h), _rand(rng, h, 3 * H * d), _rand(rng, H * d, h)
+        r = oracle.attn_shard(X, Wqkv, Wo, b, s, H, d, True, matched=False)
+        np.testing.assert_allclose(r["O"][0], r["V"][0], rtol=1e-14, atol=1e-14)
+
+    def test_zero_queries_give_prefix_means(self):
+        rng = np.random.default_rng(43)
+        b, s, H, d, h = 2, 6, 2, 4, 8
+        X, Wqkv, Wo = _rand(rng, b * s, h), _rand(rng, h, 3 * H * d), _rand(rng, H * d, h)
+        Wqkv[:, :H * d] = 0.0
+        r = oracle.attn_shard(X, Wqkv, Wo, b, s, H, d, True, matched=False)
+        V = r["V"]
+        for bi in range(b):
+            Vs = V[bi * s:(bi + 1) * s]
+            pref = np.cumsum(Vs, axis=0) / np.arange(1, s + 1)[:, None]
+            np.testing.assert_allclose(r["O"][bi * s:(bi + 1) * s], pref, rtol=1e-13, atol=1e-13)
+
+    @pytest.mark.parametrize("N", [2, 4, 8])
+    def test_head_shards_sum_to_full_mha(self, N):
+        rng = np.random.default_rng(44 + N)
+        b, s, H, d = 2, 9, 8, 8
+        h = H * d
+        X = _rand(rng, b * s, h)
+        Wq, Wk, Wv = (_rand(rng, h, h, scale=h ** -0.5) for _ in range(3))
+        Wo = _rand(rng, h, h, scale=h ** -0.5)
+        full = oracle.mha_full(X, Wq, Wk, Wv, Wo, b, s, H, d)
+        Hl = H // N
+        tot = np.zeros_like(full)
+        for i in range(N):
+            cols = slice(i * Hl * d, (i + 1) * Hl * d)
+            Wqkv_i = np.concatenate([Wq[:, cols], Wk[:, cols], Wv[:, cols]], axis=1)
+            tot += oracle.attn_shard(X, Wqkv_i, Wo[cols, :], b, s, Hl, d, matched=False)["out"]
+        np.testing.assert_allclose(tot, full, rtol=1e-12, atol=1e-12)
+
+    def test_head_permutation_invariance(self):
+        rng = np.random.default_rng(45)
+        b, s, H, d, h = 1, 8, 4, 4, 16
+        X, Wqkv, Wo = _rand(rng, s, h), _rand(rng, h, 3 * H * d, scale=0.3), _rand(rng, H * d, h)
+        perm = [2, 0, 3, 1]
+        cols = np.concatenate([np.arange(j * d, (j + 1) * d) for j in perm])
+        Wqkv_p = np.concatenate([Wqkv[:, blk * H * d + cols] for blk in range(3)], axis=1)
+        a = oracle.attn_shard(X, Wqkv, Wo, b, s, H, d, matched=False)["out"]
+        p = oracle.attn_shard(X, Wqkv_p, Wo[cols, :], b, s, H, d, matched=False)["out"]
+        np.testing.assert_allclose(a, p, rtol=1e-12, atol=1e-12)
+
+    def test_against_torch_sdpa(self):
+        rng = np.random.default_rng(46)
+        b, s, H, d = 2, 16, 3, 8
+        Q, K, V = (_rand(rng, b * s, H * d) for _ in range(3))
+        O = oracle.attn_core(Q, K, V, b, s, H, d, causal=True)
+        t = lambda A: torch.tensor(A).reshape(b, s, H, d).transpose(1, 2)
+        ref = torch.nn.functional.scaled_dot_product_attention(t(Q), t(K), t(V), is_causal=True)
+        np.testing.assert_allclose(O, ref.transpose(1, 2).reshape(b * s, H * d).numpy(),
+                                   rtol=1e-12, atol=1e-12)
+
+    def test_sampled_rows_equal_full(self):
+        rng = np.random.default_rng(47)
+        b, s, H, d, h = 2, 12, 2, 8, 16
+        X = ob.round_to_bf16(_rand(rng, b * s, h))
+        Wqkv, Wo = ob.round_to_bf16(_rand(rng, h, 3 * H * d, scale=0.2)), ob.round_to_bf16(_rand(rng, H * d, h))
+        full = oracle.attn_shard(X, Wqkv, Wo, b, s, H, d)
+        rows = np.array([0, 5, 12, 23])
+        part = oracle.attn_shard_rows(X, Wqkv, Wo, b, s, H, d, rows)
+        np.testing.assert_allclose(part["out"], full["out"][rows], rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- embedding
+def _read_golden_split():
+    ids, vocab, ranks = None, None, []
+    with open(os.path.join(GOLDEN, "vocab_split_example.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *rest = line.split()
+            if key == "ids":
+                ids = [int(x) for x in rest]
+            elif key == "vocab":
+                vocab = int(rest[0])
+            elif key == "rank":
+                lo, hi, colon, *rows = rest
+                assert colon == ":"
+                ranks.append((int(lo), int(hi), [int(r) for r in rows]))
+    return ids, vocab, ranks
+
+
+class TestEmbedding:
+    def test_pages_worked_example(self):
+        ids, vocab, ranks = _read_golden_split()
+        h = 3
+        E = np.arange(vocab * h, dtype=np.int64).reshape(vocab, h) + 1  # no zero rows
+        total = np.zeros((len(ids), h), np.int64)
+        for lo, hi, rows in ranks:
+            out = oracle.vocab_embed_shard(ids, E[lo:hi], lo, hi)
+            for t, r in enumerate(rows):
+                want = np.zeros(h, np.int64) if r < 0 else E[lo:hi][r]
+                np.testing.assert_array_equal(out[t], want)
+            total += out
+        np.testing.assert_array_equal(total, E[ids])
+
+    def test_shards_assemble_lookup_and_misses_are_zero(self):
+        rng = np.random.default_rng(51)
+        v, h, N = 96, 5, 8
+        E = ob.f64_to_bf16_bits(rng.standard_normal((v, h)) * 0.02)
+        assert not np.any(E == 0x8000)  # no -0.0 entries (so adding +0.0 rows is exact)
+        ids = rng.integers(-10, v + 10, 200).astype(np.int32)
+        outs = [oracle.vocab_embed_shard(ids, E[i * v // N:(i + 1) * v // N], i * v // N, (i + 1) * v // N)
+                for i in range(N)]
+        got = np.zeros((ids.size, h), np.uint16)
+        for o in outs:
+            nz = o != 0
+            assert not np.any(nz & (got != 0))  # at most one rank contributes a row
+            got = np.where(nz, o, got)
+        inr = (ids >= 0) & (ids < v)
+        np.testing.assert_array_equal(got[inr], E[ids[inr]])
+        assert not np.any(got[~inr])
