@@ -1,0 +1,23 @@
+"""attention_shard_math_amd — Python binding of libtpshard, one tensor-parallel
+rank's shard of a Megatron-style Transformer layer on MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels of libtpshard.so
+(built in-tree by ``attention_shard_math_amd.build``). Torch tensors supply
+device memory and the current stream. There is no CPU fallback: importing the
+package without the built library raises.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    TpError,
+    lib,
+    column_linear,
+    row_linear,
+    mlp_fwd,
+    mlp_bwd,
+    mlp_bwd_workspace,
+    attn_core,
+    attn_fwd,
+    attn_fwd_workspace,
+    vocab_embed,
+    shard_sum,
+)

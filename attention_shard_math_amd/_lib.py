@@ -1,0 +1,171 @@
+"""ctypes binding of the libtpshard C ABI (include/tpshard.h).
+
+Each function takes torch tensors, checks dtype/shape/contiguity/device (the C
+side cannot see tensor metadata), passes raw device pointers plus the current
+HIP stream, and raises TpError on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtpshard.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python attention_shard_math_amd/build.py` "
+                      "(or __graft_entry__.build()) first")
+lib = C.CDLL(LIB_PATH)
+
+TP_F32, TP_BF16 = 0, 1
+TP_ACT_NONE, TP_ACT_GELU = 0, 1
+_i64, _vp, _sz = C.c_int64, C.c_void_p, C.c_size_t
+
+_SIGS = {
+    "tp_column_linear": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, C.c_int, _vp],
+    "tp_row_linear": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
+    "tp_mlp_fwd": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_mlp_bwd": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "tp_attn_core": [_i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp],
+    "tp_attn_fwd": [_i64, _i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "tp_vocab_embed": [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp],
+    "tp_shard_sum": [C.c_int, C.POINTER(_vp), C.c_int, _i64, _vp, _vp],
+}
+for _name, _args in _SIGS.items():
+    _f = getattr(lib, _name)
+    _f.argtypes = _args
+    _f.restype = C.c_int
+lib.tp_mlp_bwd_workspace.argtypes = [_i64, _i64, _i64]
+lib.tp_mlp_bwd_workspace.restype = _sz
+lib.tp_attn_fwd_workspace.argtypes = [_i64, _i64, _i64, _i64]
+lib.tp_attn_fwd_workspace.restype = _sz
+lib.tp_status_string.argtypes = [C.c_int]
+lib.tp_status_string.restype = C.c_char_p
+lib.tp_last_error.argtypes = []
+lib.tp_last_error.restype = C.c_char_p
+
+
+class TpError(RuntimeError):
+    def __init__(self, status: int, fn: str):
+        self.status = status
+        msg = lib.tp_last_error().decode()
+        super().__init__(f"{fn}: {lib.tp_status_string(status).decode()}: {msg}")
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        raise TpError(status, fn)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return TP_F32
+    if t.dtype == torch.bfloat16:
+        return TP_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t, shape=None, dtype=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    return t.data_ptr()
+
+
+def column_linear(X, W, Y, U=None, act="gelu", stream=None):
+    """Y = act(X W) (and U = X W when act is GeLU and U is given)."""
+    M, K = X.shape
+    N = W.shape[1]
+    dt = X.dtype
+    a = TP_ACT_GELU if act == "gelu" else TP_ACT_NONE
+    _check(lib.tp_column_linear(_dt(X), M, K, N, _ptr(X, (M, K), dt, "X"), _ptr(W, (K, N), dt, "W"),
+                                _ptr(U, (M, N), dt, "U"), _ptr(Y, (M, N), dt, "Y"), a, _stream(stream)),
+           "tp_column_linear")
+
+
+def row_linear(Y, W, Z, stream=None):
+    """Z (float32) = Y W."""
+    M, K = Y.shape
+    N = W.shape[1]
+    dt = Y.dtype
+    _check(lib.tp_row_linear(_dt(Y), M, K, N, _ptr(Y, (M, K), dt, "Y"), _ptr(W, (K, N), dt, "W"),
+                             _ptr(Z, (M, N), torch.float32, "Z"), _stream(stream)), "tp_row_linear")
+
+
+def mlp_fwd(X, A_i, B_i, Y_i, Z_i, U_i=None, stream=None):
+    M, h = X.shape
+    f = A_i.shape[1]
+    dt = X.dtype
+    _check(lib.tp_mlp_fwd(_dt(X), M, h, f, _ptr(X, (M, h), dt, "X"), _ptr(A_i, (h, f), dt, "A_i"),
+                          _ptr(B_i, (f, h), dt, "B_i"), _ptr(U_i, (M, f), dt, "U_i"), _ptr(Y_i, (M, f), dt, "Y_i"),
+                          _ptr(Z_i, (M, h), torch.float32, "Z_i"), _stream(stream)), "tp_mlp_fwd")
+
+
+def mlp_bwd_workspace(M, h, f) -> int:
+    return int(lib.tp_mlp_bwd_workspace(M, h, f))
+
+
+def mlp_bwd(X, A_i, B_i, U_i, Y_i, dZ, dX_i, dA_i, dB_i, ws, stream=None):
+    M, h = X.shape
+    f = A_i.shape[1]
+    bf = torch.bfloat16
+    f32 = torch.float32
+    wsp = _ptr(ws, name="ws") if ws is not None else None
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib.tp_mlp_bwd(M, h, f, _ptr(X, (M, h), bf, "X"), _ptr(A_i, (h, f), bf, "A_i"),
+                          _ptr(B_i, (f, h), bf, "B_i"), _ptr(U_i, (M, f), bf, "U_i"), _ptr(Y_i, (M, f), bf, "Y_i"),
+                          _ptr(dZ, (M, h), bf, "dZ"), _ptr(dX_i, (M, h), f32, "dX_i"),
+                          _ptr(dA_i, (h, f), f32, "dA_i"), _ptr(dB_i, (f, h), f32, "dB_i"), wsp, wsb,
+                          _stream(stream)), "tp_mlp_bwd")
+
+
+def attn_core(QKV, O, b, s, n_heads_local, d_head, causal=True, stream=None):
+    w = n_heads_local * d_head
+    bf = torch.bfloat16
+    _check(lib.tp_attn_core(b, s, n_heads_local, d_head, int(causal), _ptr(QKV, (b * s, 3 * w), bf, "QKV"),
+                            _ptr(O, (b * s, w), bf, "O"), _stream(stream)), "tp_attn_core")
+
+
+def attn_fwd_workspace(b, s, n_heads_local, d_head) -> int:
+    return int(lib.tp_attn_fwd_workspace(b, s, n_heads_local, d_head))
+
+
+def attn_fwd(X, Wqkv_i, Wo_i, out, ws, b, s, n_heads_local, d_head, causal=True, stream=None):
+    h = X.shape[1]
+    w = n_heads_local * d_head
+    bf = torch.bfloat16
+    wsp = _ptr(ws, name="ws") if ws is not None else None
+    wsb = ws.numel() * ws.element_size() if ws is not None else 0
+    _check(lib.tp_attn_fwd(b, s, h, n_heads_local, d_head, int(causal), _ptr(X, (b * s, h), bf, "X"),
+                           _ptr(Wqkv_i, (h, 3 * w), bf, "Wqkv_i"), _ptr(Wo_i, (w, h), bf, "Wo_i"),
+                           _ptr(out, (b * s, h), torch.float32, "out"), wsp, wsb, _stream(stream)), "tp_attn_fwd")
+
+
+def vocab_embed(ids, E_i, lo, hi, out, stream=None):
+    n = ids.numel()
+    h = E_i.shape[1]
+    _check(lib.tp_vocab_embed(_ptr(ids, dtype=torch.int32, name="ids"), n, _ptr(E_i, (hi - lo, h), None, "E_i"),
+                              lo, hi, h, _ptr(out, (n, h), E_i.dtype, "out"), _stream(stream)), "tp_vocab_embed")
+
+
+def shard_sum(partials, out, stream=None):
+    n = len(partials)
+    numel = out.numel()
+    arr = (_vp * max(n, 1))(*[_ptr(p, dtype=out.dtype, name=f"partials[{i}]") for i, p in enumerate(partials)])
+    for i, p in enumerate(partials):
+        if p.numel() != numel:
+            raise ValueError(f"partials[{i}] has {p.numel()} elements, out has {numel}")
+    _check(lib.tp_shard_sum(_dt(out), arr, n, numel, _ptr(out, name="out"), _stream(stream)), "tp_shard_sum")

@@ -1,0 +1,320 @@
+// C-ABI entry points of libtpshard: argument validation on the host, then kernel
+// launches on the caller's stream. No allocation, no synchronisation, no
+// exceptions across the interface. The operations and their citations are
+// documented in include/tpshard.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "attn.hpp"
+#include "bandwidth.hpp"
+#include "gemm_bf16.hpp"
+#include "gemm_f32.hpp"
+#include "tpshard.h"
+
+#define TP_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+tp_status fail(tp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tp_status ok() {
+  g_last_error.clear();
+  return TP_OK;
+}
+
+tp_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(TP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validation helpers return TP_OK or an error (with the message set).
+tp_status check_dims(const char* fn, int64_t M, int64_t K, int64_t N) {
+  if (M < 0 || K <= 0 || N <= 0)
+    return fail(TP_ERR_INVALID_ARG, "%s: sizes must satisfy M >= 0, K > 0, N > 0 (got M=%lld K=%lld N=%lld)", fn,
+                (long long)M, (long long)K, (long long)N);
+  if (M > kMaxDim || K > kMaxDim || N > kMaxDim)
+    return fail(TP_ERR_UNSUPPORTED, "%s: a dimension exceeds 2^31-1", fn);
+  if (K % 8 || N % 8)
+    return fail(TP_ERR_UNSUPPORTED, "%s: K and N must be multiples of 8 (got K=%lld N=%lld)", fn, (long long)K,
+                (long long)N);
+  return TP_OK;
+}
+
+tp_status check_ptr(const char* fn, const char* name, const void* p) {
+  if (!p) return fail(TP_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+  if (!aligned16(p)) return fail(TP_ERR_UNSUPPORTED, "%s: %s is not 16-byte aligned", fn, name);
+  return TP_OK;
+}
+
+tp_status check_opt_ptr(const char* fn, const char* name, const void* p) {
+  if (p && !aligned16(p)) return fail(TP_ERR_UNSUPPORTED, "%s: %s is not 16-byte aligned", fn, name);
+  return TP_OK;
+}
+
+#define TRY(expr)                      \
+  do {                                 \
+    const tp_status _s = (expr);       \
+    if (_s != TP_OK) return _s;        \
+  } while (0)
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+tps::GemmArgs make_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
+                        void* C, int64_t ldc) {
+  tps::GemmArgs g{};
+  g.A = static_cast<const uint16_t*>(A);
+  g.B = static_cast<const uint16_t*>(B);
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = (int)M;
+  g.N = (int)N;
+  g.K = (int)K;
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+TP_API const char* tp_status_string(tp_status s) {
+  switch (s) {
+    case TP_OK: return "TP_OK";
+    case TP_ERR_INVALID_ARG: return "TP_ERR_INVALID_ARG";
+    case TP_ERR_UNSUPPORTED: return "TP_ERR_UNSUPPORTED";
+    case TP_ERR_WORKSPACE: return "TP_ERR_WORKSPACE";
+    case TP_ERR_HIP: return "TP_ERR_HIP";
+  }
+  return "TP_ERR_UNKNOWN";
+}
+
+TP_API const char* tp_last_error(void) { return g_last_error.c_str(); }
+
+TP_API tp_status tp_column_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N, const void* X, const void* W,
+                                  void* U_out, void* Y_out, int act, void* stream) {
+  const char* fn = "tp_column_linear";
+  if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  if (act != TP_ACT_NONE && act != TP_ACT_GELU) return fail(TP_ERR_INVALID_ARG, "%s: unknown activation %d", fn, act);
+  if (act == TP_ACT_NONE && U_out)
+    return fail(TP_ERR_INVALID_ARG, "%s: U_out must be NULL without an activation", fn);
+  TRY(check_dims(fn, M, K, N));
+  TRY(check_ptr(fn, "X", X));
+  TRY(check_ptr(fn, "W", W));
+  TRY(check_ptr(fn, "Y_out", Y_out));
+  TRY(check_opt_ptr(fn, "U_out", U_out));
+  if (M == 0) return ok();
+  if (dt == TP_F32)
+    return hip_status(tps::gemm_f32(static_cast<const float*>(X), static_cast<const float*>(W), (int)M, (int)N, (int)K,
+                                    static_cast<float*>(Y_out), static_cast<float*>(U_out), act == TP_ACT_GELU,
+                                    as_stream(stream)),
+                      fn);
+  tps::GemmArgs g = make_args(X, K, W, N, M, N, K, Y_out, N);
+  g.U = static_cast<uint16_t*>(U_out);
+  g.ldu = N;
+  return hip_status(tps::gemm_bf16(g, true, false, act == TP_ACT_GELU ? tps::EPI_GELU : tps::EPI_BF16,
+                                   as_stream(stream)),
+                    fn);
+}
+
+TP_API tp_status tp_row_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N, const void* Y, const void* W,
+                               float* Z_out, void* stream) {
+  const char* fn = "tp_row_linear";
+  if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  TRY(check_dims(fn, M, K, N));
+  TRY(check_ptr(fn, "Y", Y));
+  TRY(check_ptr(fn, "W", W));
+  TRY(check_ptr(fn, "Z_out", Z_out));
+  if (M == 0) return ok();
+  if (dt == TP_F32)
+    return hip_status(tps::gemm_f32(static_cast<const float*>(Y), static_cast<const float*>(W), (int)M, (int)N, (int)K,
+                                    Z_out, nullptr, false, as_stream(stream)),
+                      fn);
+  tps::GemmArgs g = make_args(Y, K, W, N, M, N, K, Z_out, N);
+  return hip_status(tps::gemm_bf16(g, true, false, tps::EPI_F32, as_stream(stream)), fn);
+}
+
+TP_API tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f, const void* X, const void* A_i,
+                            const void* B_i, void* U_i, void* Y_i, float* Z_i, void* stream) {
+  const char* fn = "tp_mlp_fwd";
+  if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  TRY(check_dims(fn, M, h, f));
+  TRY(check_ptr(fn, "X", X));
+  TRY(check_ptr(fn, "A_i", A_i));
+  TRY(check_ptr(fn, "B_i", B_i));
+  TRY(check_ptr(fn, "Y_i", Y_i));
+  TRY(check_ptr(fn, "Z_i", Z_i));
+  TRY(check_opt_ptr(fn, "U_i", U_i));
+  TRY(tp_column_linear(dt, M, h, f, X, A_i, U_i, Y_i, TP_ACT_GELU, stream));
+  return tp_row_linear(dt, M, f, h, Y_i, B_i, Z_i, stream);
+}
+
+TP_API size_t tp_mlp_bwd_workspace(int64_t M, int64_t h, int64_t f) {
+  (void)h;
+  if (M < 0 || f < 0) return 0;
+  return round256((size_t)M * (size_t)f * 2);
+}
+
+TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, const void* A_i, const void* B_i,
+                            const void* U_i, const void* Y_i, const void* dZ, float* dX_i, float* dA_i, float* dB_i,
+                            void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "tp_mlp_bwd";
+  TRY(check_dims(fn, M, h, f));
+  TRY(check_ptr(fn, "X", X));
+  TRY(check_ptr(fn, "A_i", A_i));
+  TRY(check_ptr(fn, "B_i", B_i));
+  if (!U_i) return fail(TP_ERR_UNSUPPORTED, "%s: U_i is required (the saved pre-activation)", fn);
+  TRY(check_ptr(fn, "U_i", U_i));
+  TRY(check_ptr(fn, "Y_i", Y_i));
+  TRY(check_ptr(fn, "dZ", dZ));
+  TRY(check_opt_ptr(fn, "dX_i", dX_i));
+  TRY(check_opt_ptr(fn, "dA_i", dA_i));
+  TRY(check_opt_ptr(fn, "dB_i", dB_i));
+  const size_t need = tp_mlp_bwd_workspace(M, h, f);
+  if (need && (!ws || ws_bytes < need))
+    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
+                ws ? "" : " (NULL)");
+  TRY(check_opt_ptr(fn, "ws", ws));
+  hipStream_t s = as_stream(stream);
+  uint16_t* dU = static_cast<uint16_t*>(ws);
+  if (M > 0) {
+    // dU = (dZ B_i^T) * GeLU'(U_i): A = dZ [M,h] (K-contig), B(k,n) = B_i[n, k] (K-contig).
+    tps::GemmArgs g = make_args(dZ, h, B_i, h, M, f, h, dU, f);
+    g.Uin = static_cast<const uint16_t*>(U_i);
+    g.ldu = f;
+    TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_DGELU, s), fn));
+  }
+  if (dB_i) {  // dB = Y^T dZ: A(m,k) = Y[k, m] (M-contig), B(k,n) = dZ[k, n] (N-contig)
+    tps::GemmArgs g = make_args(Y_i, f, dZ, h, f, h, M, dB_i, h);
+    TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, s), fn));
+  }
+  if (dA_i) {  // dA = X^T dU: A(m,k) = X[k, m], B(k,n) = dU[k, n]
+    tps::GemmArgs g = make_args(X, h, dU, f, h, f, M, dA_i, f);
+    TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, s), fn));
+  }
+  if (dX_i && M > 0) {  // dX = dU A_i^T: A = dU [M,f] (K-contig), B(k,n) = A_i[n, k] (K-contig)
+    tps::GemmArgs g = make_args(dU, f, A_i, f, M, h, f, dX_i, h);
+    TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_F32, s), fn));
+  }
+  return ok();
+}
+
+namespace {
+tp_status check_attn_shape(const char* fn, int64_t b, int64_t s, int64_t Hl, int64_t d) {
+  if (b < 0 || s < 0 || Hl <= 0 || d <= 0)
+    return fail(TP_ERR_INVALID_ARG, "%s: need b >= 0, s >= 0, n_heads_local > 0, d_head > 0", fn);
+  if (d != 64 && d != 128) return fail(TP_ERR_UNSUPPORTED, "%s: d_head must be 64 or 128 (got %lld)", fn, (long long)d);
+  if (b * s > kMaxDim || 3 * Hl * d > kMaxDim || b * Hl * ((s + 127) / 128) > kMaxDim)
+    return fail(TP_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  return TP_OK;
+}
+}  // namespace
+
+TP_API tp_status tp_attn_core(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
+                              const void* QKV, void* O, void* stream) {
+  const char* fn = "tp_attn_core";
+  TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  TRY(check_ptr(fn, "QKV", QKV));
+  TRY(check_ptr(fn, "O", O));
+  if (b * s == 0) return ok();
+  return hip_status(tps::attn_fwd(static_cast<const uint16_t*>(QKV), static_cast<uint16_t*>(O), (int)b, (int)s,
+                                  (int)n_heads_local, (int)d_head, causal != 0, as_stream(stream)),
+                    fn);
+}
+
+TP_API size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head) {
+  if (b < 0 || s < 0 || n_heads_local < 0 || d_head < 0) return 0;
+  const size_t t = (size_t)b * (size_t)s, w = (size_t)n_heads_local * (size_t)d_head;
+  return round256(t * 3 * w * 2) + round256(t * w * 2);
+}
+
+TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head, int causal,
+                             const void* X, const void* Wqkv_i, const void* Wo_i, float* out_partial, void* ws,
+                             size_t ws_bytes, void* stream) {
+  const char* fn = "tp_attn_fwd";
+  TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  TRY(check_dims(fn, b * s, h, 3 * n_heads_local * d_head));
+  TRY(check_ptr(fn, "X", X));
+  TRY(check_ptr(fn, "Wqkv_i", Wqkv_i));
+  TRY(check_ptr(fn, "Wo_i", Wo_i));
+  TRY(check_ptr(fn, "out_partial", out_partial));
+  const size_t need = tp_attn_fwd_workspace(b, s, n_heads_local, d_head);
+  if (need && (!ws || ws_bytes < need))
+    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
+                ws ? "" : " (NULL)");
+  TRY(check_opt_ptr(fn, "ws", ws));
+  const int64_t M = b * s, w = n_heads_local * d_head;
+  if (M == 0) return ok();
+  hipStream_t st = as_stream(stream);
+  uint16_t* qkv = static_cast<uint16_t*>(ws);
+  uint16_t* O = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + round256((size_t)M * 3 * w * 2));
+  {
+    tps::GemmArgs g = make_args(X, h, Wqkv_i, 3 * w, M, 3 * w, h, qkv, 3 * w);
+    TRY(hip_status(tps::gemm_bf16(g, true, false, tps::EPI_BF16, st), fn));
+  }
+  TRY(hip_status(tps::attn_fwd(qkv, O, (int)b, (int)s, (int)n_heads_local, (int)d_head, causal != 0, st), fn));
+  {
+    tps::GemmArgs g = make_args(O, w, Wo_i, h, M, h, w, out_partial, h);
+    TRY(hip_status(tps::gemm_bf16(g, true, false, tps::EPI_F32, st), fn));
+  }
+  return ok();
+}
+
+TP_API tp_status tp_vocab_embed(const int32_t* ids, int64_t n_tokens, const void* E_i, int64_t lo, int64_t hi,
+                                int64_t h, void* out, void* stream) {
+  const char* fn = "tp_vocab_embed";
+  if (n_tokens < 0) return fail(TP_ERR_INVALID_ARG, "%s: n_tokens < 0", fn);
+  if (lo < 0 || lo >= hi) return fail(TP_ERR_INVALID_ARG, "%s: need 0 <= lo < hi (got lo=%lld hi=%lld)", fn,
+                                      (long long)lo, (long long)hi);
+  if (h <= 0) return fail(TP_ERR_INVALID_ARG, "%s: h must be > 0", fn);
+  if (h % 8) return fail(TP_ERR_UNSUPPORTED, "%s: h must be a multiple of 8 (got %lld)", fn, (long long)h);
+  if (n_tokens > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "%s: n_tokens exceeds 2^31-1", fn);
+  if (!ids) return fail(TP_ERR_INVALID_ARG, "%s: ids is NULL", fn);
+  TRY(check_ptr(fn, "E_i", E_i));
+  TRY(check_ptr(fn, "out", out));
+  if (n_tokens == 0) return ok();
+  return hip_status(tps::vocab_gather(ids, n_tokens, static_cast<const uint16_t*>(E_i), lo, hi, h,
+                                      static_cast<uint16_t*>(out), as_stream(stream)),
+                    fn);
+}
+
+TP_API tp_status tp_shard_sum(tp_dtype dt, const void* const* partials, int n_partials, int64_t numel, void* out,
+                              void* stream) {
+  const char* fn = "tp_shard_sum";
+  if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
+  if (n_partials < 1 || n_partials > tps::kMaxPartials)
+    return fail(TP_ERR_INVALID_ARG, "%s: n_partials must be in [1, %d] (got %d)", fn, tps::kMaxPartials, n_partials);
+  if (numel < 0) return fail(TP_ERR_INVALID_ARG, "%s: numel < 0", fn);
+  if (!partials) return fail(TP_ERR_INVALID_ARG, "%s: partials is NULL", fn);
+  tps::SumArgs a{};
+  for (int i = 0; i < n_partials; ++i) {
+    char name[32];
+    snprintf(name, sizeof name, "partials[%d]", i);
+    TRY(check_ptr(fn, name, partials[i]));
+    a.p[i] = partials[i];
+  }
+  TRY(check_ptr(fn, "out", out));
+  a.n = n_partials;
+  a.numel = numel;
+  a.out = out;
+  if (numel == 0) return ok();
+  return hip_status(tps::shard_sum(a, dt == TP_BF16, as_stream(stream)), fn);
+}

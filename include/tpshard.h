@@ -1,0 +1,171 @@
+/*
+ * libtpshard — one tensor-parallel rank's shard of a Megatron-style
+ * Transformer layer, as hand-written HIP kernels for AMD Instinct MI355X (gfx950).
+ *
+ * The method (pages cited by title and section):
+ *   "Megatron-LM：张量并行与大规模训练", §2.1 MLP 层的张量并行 — the MLP
+ *     Z = GeLU(X A) B with A split by columns into A_i [h, 4h/N] and B by rows
+ *     into B_i [4h/N, h]; each rank forms the partial Z_i = GeLU(X A_i) B_i with no
+ *     communication and one all-reduce adds the Z_i.
+ *   same page, §2.2 Self-Attention 的张量并行 — heads split across ranks, the
+ *     output projection split by rows, one all-reduce after it.
+ *   m.youleyou.com/wenzhang/3143730, 一、切分权重 §1.1/§1.2 and 二、MLP层 §2.1 — the
+ *     row/column splits with their backward (g's backward copies dZ to every rank,
+ *     f's backward adds the ranks' input gradients); 三、Self-Attention层 §3.1 —
+ *     column split of the Q, K, V weights by whole heads, head count divisible
+ *     by the rank count; 四、Embedding层 §4.1 — vocabulary-parallel input
+ *     embedding that zeroes ids a rank does not hold.
+ *   "Megatron-LM 介绍" (apxml.com), 核心贡献 item 1 — ColumnParallelLinear.
+ *
+ * Common conventions for every call:
+ *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *     contiguous, 16-byte aligned. Nothing is allocated or freed by the library.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the null stream of
+ *     the current device. Work is enqueued asynchronously on it; the call returns
+ *     after the launches, not after the kernels finish.
+ *   - Every argument is checked on the host before any launch. On a bad argument
+ *     nothing is launched and TP_ERR_INVALID_ARG / TP_ERR_UNSUPPORTED /
+ *     TP_ERR_WORKSPACE is returned; a failed launch returns TP_ERR_HIP. A
+ *     non-OK return sets a per-thread message readable with tp_last_error().
+ *     Nothing aborts or throws across this interface.
+ *   - bf16 means bfloat16 (1 sign, 8 exponent, 7 mantissa bits); every
+ *     float32 -> bf16 store rounds to nearest, ties to even. Products are
+ *     accumulated in float32.
+ *   - Matrix dimensions named h, f, K, N below must be multiples of 8 (16-byte
+ *     vectors); token counts M may be any value >= 0 (M = 0 launches nothing).
+ */
+#ifndef TPSHARD_H
+#define TPSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum tp_status {
+  TP_OK = 0,
+  TP_ERR_INVALID_ARG = 1, /* null pointer, negative or inconsistent size, lo > hi, ... */
+  TP_ERR_UNSUPPORTED = 2, /* well-formed but outside what the kernels handle (alignment, dims % 8) */
+  TP_ERR_WORKSPACE = 3,   /* workspace missing or smaller than the *_workspace() size */
+  TP_ERR_HIP = 4          /* the HIP runtime reported an error at launch */
+} tp_status;
+
+typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
+
+typedef enum tp_activation { TP_ACT_NONE = 0, TP_ACT_GELU = 1 } tp_activation;
+
+/* Column-parallel linear layer of one rank: Y = act(X W).
+ * [Megatron-LM 介绍, 核心贡献 item 1 (ColumnParallelLinear); Megatron-LM：张量并行与
+ *  大规模训练, §2.1, 列并行 — the rank holds a column block W = A_i of A.]
+ *   dt     TP_BF16: X, W, U_out, Y_out are bf16. TP_F32: all float32.
+ *   X      [M, K]   the replicated layer input.
+ *   W      [K, N]   the rank's column block, stored [in, out].
+ *   U_out  [M, N]   nullable; receives X W (before the activation) when act is
+ *                   TP_ACT_GELU. Must be NULL when act is TP_ACT_NONE.
+ *   Y_out  [M, N]   act(X W). GeLU is the exact form u * Phi(u).
+ * K and N must be multiples of 8. */
+tp_status tp_column_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N,
+                           const void* X, const void* W, void* U_out, void* Y_out,
+                           int act, void* stream);
+
+/* Row-parallel linear layer of one rank: the float32 partial Z = Y W that the
+ * all-reduce adds over ranks.
+ * [Megatron-LM：张量并行与大规模训练, §2.1, 行并行 — Z_i = Y_i B_i.]
+ *   Y [M, K] (dt), W [K, N] (dt) the rank's row block, Z_out [M, N] float32.
+ * K and N must be multiples of 8. */
+tp_status tp_row_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N,
+                        const void* Y, const void* W, float* Z_out, void* stream);
+
+/* MLP forward of one rank: U_i = X A_i, Y_i = GeLU(U_i), Z_i = Y_i B_i.
+ * [Megatron-LM：张量并行与大规模训练, §2.1 MLP 层的张量并行 and its pseudo-code;
+ *  m.youleyou.com/wenzhang/3143730, 二、MLP层 §2.1.]
+ *   X [M, h], A_i [h, f], B_i [f, h] (dt); f is the rank's share 4h/N.
+ *   U_i [M, f] (dt) nullable — saved pre-activation for the backward.
+ *   Y_i [M, f] (dt) required — the activation, also needed by the backward.
+ *   Z_i [M, h] float32 — this rank's partial of Z (sum over ranks with
+ *   tp_shard_sum in place of the all-reduce).
+ * h and f must be multiples of 8. Two kernels: column GEMM + GeLU epilogue,
+ * then row GEMM. */
+tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f,
+                     const void* X, const void* A_i, const void* B_i,
+                     void* U_i, void* Y_i, float* Z_i, void* stream);
+
+/* MLP backward of one rank, bf16 inputs, float32 outputs. With the replicated
+ * upstream gradient dZ (g's backward is the identity):
+ *   dU_i = (dZ B_i^T) * GeLU'(U_i)   -> bf16 [M, f] in the workspace
+ *   dB_i = Y_i^T dZ                  -> float32 [f, h]
+ *   dA_i = X^T dU_i                  -> float32 [h, f]
+ *   dX_i = dU_i A_i^T                -> float32 [M, h], the partial that f's
+ *                                       backward adds over ranks.
+ * [m.youleyou.com/wenzhang/3143730, 一、切分权重 §1.1/§1.2 (backward of the row and
+ *  column splits) and 二、MLP层 §2.1 (g's and f's backward).]
+ *   X [M,h], A_i [h,f], B_i [f,h], U_i [M,f], Y_i [M,f], dZ [M,h]: bf16.
+ *   Any of dX_i, dA_i, dB_i may be NULL to skip that product.
+ *   ws: device workspace of at least tp_mlp_bwd_workspace(M, h, f) bytes.
+ * Kernels run in the order dU, dB, dA, dX on `stream`. */
+tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f,
+                     const void* X, const void* A_i, const void* B_i,
+                     const void* U_i, const void* Y_i, const void* dZ,
+                     float* dX_i, float* dA_i, float* dB_i,
+                     void* ws, size_t ws_bytes, void* stream);
+size_t tp_mlp_bwd_workspace(int64_t M, int64_t h, int64_t f);
+
+/* Causal (or full) softmax attention over one rank's local heads, bf16.
+ * [Megatron-LM：张量并行与大规模训练, §2.2; m.youleyou.com/wenzhang/3143730,
+ *  三、Self-Attention层 §3.1.]
+ *   QKV [b*s, 3*Hl*d] bf16: per token [Q heads | K heads | V heads], local head j
+ *       at columns j*d .. (j+1)*d of each block.
+ *   O   [b*s, Hl*d] bf16: O_j = softmax(Q_j K_j^T / sqrt(d)) V_j per sequence;
+ *       with causal != 0 query t sees keys u <= t.
+ * d must be 64 or 128. Softmax in float32, P rounded to bf16 for the P V product. */
+tp_status tp_attn_core(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head,
+                       int causal, const void* QKV, void* O, void* stream);
+
+/* One rank's attention block: QKV = X Wqkv_i (bf16), O = tp_attn_core(QKV),
+ * out_partial = O Wo_i (float32 partial added by the all-reduce).
+ * [Megatron-LM：张量并行与大规模训练, §2.2 (QKV projection split by heads,
+ *  row-parallel output projection); m.youleyou.com/wenzhang/3143730, 三、
+ *  Self-Attention层 §3.1 (column split of Q, K, V by heads; B split by rows).]
+ *   X [b*s, h] bf16; Wqkv_i [h, 3*Hl*d] bf16; Wo_i [Hl*d, h] bf16;
+ *   out_partial [b*s, h] float32.
+ *   ws: at least tp_attn_fwd_workspace(b, s, Hl, d) bytes; on return it holds
+ *   QKV bf16 [b*s, 3*Hl*d] followed (at a 256-byte aligned offset) by O bf16
+ *   [b*s, Hl*d]. */
+tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_local,
+                      int64_t d_head, int causal, const void* X, const void* Wqkv_i,
+                      const void* Wo_i, float* out_partial, void* ws, size_t ws_bytes,
+                      void* stream);
+size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head);
+
+/* Vocabulary-parallel input embedding of one rank (bit copy, no arithmetic):
+ *   out[t, :] = E_i[ids[t] - lo, :] if lo <= ids[t] < hi, else zeros.
+ * [m.youleyou.com/wenzhang/3143730, 四、Embedding层 §4.1.] Ids outside [lo, hi) —
+ * including ids outside the whole vocabulary — give zero rows; that is not an error.
+ *   ids [n_tokens] int32; E_i [hi-lo, h] bf16; out [n_tokens, h] bf16.
+ *   Requires 0 <= lo < hi and h a multiple of 8. */
+tp_status tp_vocab_embed(const int32_t* ids, int64_t n_tokens, const void* E_i,
+                         int64_t lo, int64_t hi, int64_t h, void* out, void* stream);
+
+/* Shard-sum standing in for the all-reduce of N partials on one GPU:
+ *   out = ((P_0 + P_1) + P_2) + ... + P_{N-1}, elementwise, in float32, in this
+ *   fixed order (so the result is reproducible bit for bit).
+ * [Megatron-LM：张量并行与大规模训练, §2.1, 行并行 (Z = Z_1 + ... + Z_N);
+ *  m.youleyou.com/wenzhang/3143730, 二、MLP层 §2.1 (g's forward adds the partials).]
+ *   partials: HOST array of n_partials device pointers, 1 <= n_partials <= 16.
+ *   dt TP_F32: float32 partials and out. TP_BF16: bf16 partials widened to
+ *   float32, summed in order, the sum rounded once to bf16.
+ *   out may alias partials[0]. numel >= 0. */
+tp_status tp_shard_sum(tp_dtype dt, const void* const* partials, int n_partials,
+                       int64_t numel, void* out, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* tp_status_string(tp_status s);
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* tp_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TPSHARD_H */

@@ -32,17 +32,11 @@ def round_to_bf16(x) -> np.ndarray:
 
 
 def bf16_bits_to_f64(bits) -> np.ndarray:
-    """Exact value of bfloat16 bit patterns: sign, 8-bit exponent, 7-bit mantissa,
-    decoded field by field (no float32 reinterpretation)."""
-    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
-    sign = np.where(b >> 15, -1.0, 1.0)
-    expo = (b >> 7) & 0xFF
-    mant = (b & 0x7F).astype(np.float64)
-    normal = sign * np.ldexp(1.0 + mant / 128.0, expo - 127)
-    sub = sign * np.ldexp(mant / 128.0, -126)
-    val = np.where(expo == 0, sub, normal)
-    val = np.where(expo == 0xFF, np.where(mant == 0, sign * np.inf, np.nan), val)
-    return val
+    """Exact value of bfloat16 bit patterns. A bf16 pattern is the upper half of
+    the float32 with the same sign, exponent and leading mantissa bits, so the
+    value is read by placing the 16 bits in the top of a 32-bit word."""
+    b = np.asarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
 def f64_to_bf16_bits(x) -> np.ndarray:

@@ -1,0 +1,106 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch (every
+call below fails validation, so no HIP work is ever started)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tpshard.h")
+
+tp = pytest.importorskip("attention_shard_math_amd", reason="libtpshard.so not built")
+lib = tp.lib
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+P = 0x10000          # a fake, 16-byte aligned "device" pointer: never dereferenced
+MIS = 0x10002        # misaligned
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_function_is_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in tpshard.h but not exported"
+
+
+def test_status_strings():
+    assert lib.tp_status_string(0) == b"TP_OK"
+    assert lib.tp_status_string(3) == b"TP_ERR_WORKSPACE"
+    assert lib.tp_status_string(99) == b"TP_ERR_UNKNOWN"
+
+
+def _err():
+    return lib.tp_last_error().decode()
+
+
+class TestValidation:
+    def test_column_linear(self):
+        f = lib.tp_column_linear
+        assert f(7, 4, 8, 8, P, P, None, P, 1, None) == INVALID            # dtype
+        assert f(1, 4, 8, 8, P, P, None, P, 5, None) == INVALID            # activation
+        assert f(1, 4, 8, 8, P, P, P, P, 0, None) == INVALID               # U_out without act
+        assert f(1, -1, 8, 8, P, P, None, P, 1, None) == INVALID           # M < 0
+        assert f(1, 4, 0, 8, P, P, None, P, 1, None) == INVALID            # K == 0
+        assert f(1, 4, 12, 8, P, P, None, P, 1, None) == UNSUPPORTED       # K % 8
+        assert f(1, 4, 8, 20, P, P, None, P, 1, None) == UNSUPPORTED       # N % 8
+        assert f(1, 4, 8, 8, None, P, None, P, 1, None) == INVALID         # X NULL
+        assert "X is NULL" in _err()
+        assert f(1, 4, 8, 8, P, MIS, None, P, 1, None) == UNSUPPORTED      # alignment
+        assert f(1, 4, 8, 8, P, P, MIS, P, 1, None) == UNSUPPORTED
+        assert f(1, 1 << 31, 8, 8, P, P, None, P, 1, None) == UNSUPPORTED  # too large
+
+    def test_row_linear_and_mlp_fwd(self):
+        assert lib.tp_row_linear(1, 4, 8, 8, P, P, None, None) == INVALID
+        assert lib.tp_mlp_fwd(1, 4, 16, 24, P, P, P, None, None, P, None) == INVALID  # Y_i NULL
+        assert lib.tp_mlp_fwd(1, 4, 16, 20, P, P, P, None, P, P, None) == UNSUPPORTED
+
+    def test_mlp_bwd(self):
+        M, h, f = 32, 64, 128
+        need = lib.tp_mlp_bwd_workspace(M, h, f)
+        assert need == M * f * 2 and need % 256 == 0
+        assert lib.tp_mlp_bwd_workspace(3, 8, 8) == 256
+        b = lib.tp_mlp_bwd
+        assert b(M, h, f, P, P, P, None, P, P, P, P, P, P, need, None) == UNSUPPORTED  # U_i missing
+        assert b(M, h, f, P, P, P, P, P, P, P, P, P, P, need - 1, None) == WORKSPACE
+        assert b(M, h, f, P, P, P, P, P, P, P, P, P, None, need, None) == WORKSPACE
+        assert "workspace" in _err()
+        assert b(M, h, f, P, P, P, P, P, None, P, P, P, P, need, None) == INVALID      # dZ NULL
+
+    def test_attention(self):
+        assert lib.tp_attn_core(1, 16, 2, 96, 1, P, P, None) == UNSUPPORTED  # d_head
+        assert lib.tp_attn_core(1, 16, 0, 128, 1, P, P, None) == INVALID
+        assert lib.tp_attn_core(-1, 16, 2, 128, 1, P, P, None) == INVALID
+        ws = lib.tp_attn_fwd_workspace(2, 100, 3, 64)
+        assert ws == 2 * 100 * 9 * 64 * 2 + 2 * 100 * 3 * 64 * 2 + (-(2 * 100 * 9 * 64 * 2) % 256) + (-(2 * 100 * 3 * 64 * 2) % 256)
+        assert lib.tp_attn_fwd(2, 100, 256, 3, 64, 1, P, P, P, P, P, ws - 16, None) == WORKSPACE
+        assert lib.tp_attn_fwd(2, 100, 260, 3, 64, 1, P, P, P, P, P, ws, None) == UNSUPPORTED  # h % 8
+
+    def test_vocab_embed(self):
+        e = lib.tp_vocab_embed
+        assert e(P, 4, P, 10, 10, 8, P, None) == INVALID   # lo == hi
+        assert e(P, 4, P, -1, 10, 8, P, None) == INVALID   # lo < 0
+        assert e(P, -4, P, 0, 10, 8, P, None) == INVALID
+        assert e(P, 4, P, 0, 10, 12, P, None) == UNSUPPORTED
+        assert e(None, 4, P, 0, 10, 8, P, None) == INVALID
+        assert e(P, 4, P, 0, 10, 8, MIS, None) == UNSUPPORTED
+
+    def test_shard_sum(self):
+        arr = (C.c_void_p * 17)(*([P] * 17))
+        s = lib.tp_shard_sum
+        assert s(0, arr, 0, 16, P, None) == INVALID
+        assert s(0, arr, 17, 16, P, None) == INVALID
+        assert s(0, arr, 4, -1, P, None) == INVALID
+        assert s(5, arr, 4, 16, P, None) == INVALID
+        bad = (C.c_void_p * 2)(P, None)
+        assert s(0, bad, 2, 16, P, None) == INVALID
+        mis = (C.c_void_p * 2)(P, MIS)
+        assert s(0, mis, 2, 16, P, None) == UNSUPPORTED
+        assert "partials[1]" in _err()

@@ -1,0 +1,62 @@
+"""GPU parity of the attention shard (QKV GEMM, fused causal attention, row-
+parallel output projection) against the float64 oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.bf16 import bf16_bits_to_f64
+from tests.gpu_util import DEV, assert_bf16_close, bf16_dev, f64_host, note
+from workloads import CONFIGS, attn_inputs, bf16_bits, draw_normal_f32
+
+pytestmark = pytest.mark.gpu
+
+tp = pytest.importorskip("attention_shard_math_amd")
+
+
+@pytest.mark.parametrize("b,s,Hl,d,causal", [(2, 300, 2, 128, True), (1, 77, 3, 64, True),
+                                              (2, 200, 2, 128, False), (1, 1, 1, 128, True),
+                                              (3, 129, 1, 64, False)])
+def test_attn_core(b, s, Hl, d, causal):
+    note(f"attn_core b={b} s={s} Hl={Hl} d={d} causal={causal}")
+    rng = np.random.default_rng(71 + s)
+    qkv = bf16_bits(draw_normal_f32(rng, (b * s, 3 * Hl * d), 1.0))
+    O = torch.empty(b * s, Hl * d, dtype=torch.bfloat16, device=DEV)
+    tp.attn_core(bf16_dev(qkv), O, b, s, Hl, d, causal)
+    torch.cuda.synchronize()
+    q = bf16_bits_to_f64(qkv)
+    w = Hl * d
+    ref = oracle.attn_core(q[:, :w], q[:, w:2 * w], q[:, 2 * w:], b, s, Hl, d, causal)
+    assert_bf16_close(f64_host(O), ref, "O")
+
+
+@pytest.mark.parametrize("b,s,h,Hl,d", [(2, 300, 512, 2, 128), (1, 150, 256, 4, 64)])
+def test_attn_fwd_ragged(b, s, h, Hl, d):
+    note(f"attn_fwd b={b} s={s} h={h} Hl={Hl} d={d}")
+    ai = attn_inputs(b, s, h, Hl, d, 80 + s, 1.0, 0.05)
+    out = torch.empty(b * s, h, dtype=torch.float32, device=DEV)
+    ws = torch.empty(tp.attn_fwd_workspace(b, s, Hl, d), dtype=torch.uint8, device=DEV)
+    tp.attn_fwd(*(bf16_dev(ai[k]) for k in ("X", "Wqkv", "Wo")), out, ws, b, s, Hl, d, True)
+    torch.cuda.synchronize()
+    r = oracle.attn_shard(*(bf16_bits_to_f64(ai[k]) for k in ("X", "Wqkv", "Wo")), b, s, Hl, d)
+    assert_bf16_close(f64_host(out), r["out"], "out_partial")
+    qkv = ws[: b * s * 3 * Hl * d * 2].view(torch.bfloat16).view(b * s, 3 * Hl * d)
+    w = Hl * d
+    assert_bf16_close(f64_host(qkv[:, :w]), r["Q"], "Q")
+    assert_bf16_close(f64_host(qkv[:, 2 * w:]), r["V"], "V")
+
+
+def test_config4_full_size_sampled_rows():
+    c = CONFIGS[4]
+    b, s, h, d = c["b"], c["s"], c["h"], c["d_head"]
+    Hl = c["n_heads"] // c["N"]
+    ai = attn_inputs(b, s, h, Hl, d, c["seed"], c["sigma_x"], c["sigma_w"])
+    note("attn_fwd config 4 full size")
+    out = torch.empty(b * s, h, dtype=torch.float32, device=DEV)
+    ws = torch.empty(tp.attn_fwd_workspace(b, s, Hl, d), dtype=torch.uint8, device=DEV)
+    tp.attn_fwd(*(bf16_dev(ai[k]) for k in ("X", "Wqkv", "Wo")), out, ws, b, s, Hl, d, True)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+    rows = np.array([0, 1, 63, 64, 127, 128, 1000, 2047])
+    r = oracle.attn_shard_rows(*(bf16_bits_to_f64(ai[k]) for k in ("X", "Wqkv", "Wo")), b, s, Hl, d, rows)
+    assert_bf16_close(f64_host(out[torch.from_numpy(rows).to(DEV)]), r["out"], "out rows")

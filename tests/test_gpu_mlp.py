@@ -1,0 +1,176 @@
+"""GPU parity of the MLP shard (column GEMM + GeLU, row GEMM, backward) against
+the float64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle.bf16 import bf16_bits_to_f64
+from tests.gpu_util import (DEV, assert_bf16_close, assert_f32_close, bf16_dev, f32_dev, f64_host, note)
+from workloads import CONFIGS, mlp_inputs, shard_sum_inputs
+
+pytestmark = pytest.mark.gpu
+
+tp = pytest.importorskip("attention_shard_math_amd")
+
+
+def _alloc(M, h, f, dt):
+    U = torch.empty(M, f, dtype=dt, device=DEV)
+    Y = torch.empty(M, f, dtype=dt, device=DEV)
+    Z = torch.empty(M, h, dtype=torch.float32, device=DEV)
+    return U, Y, Z
+
+
+def _run_bwd(X, A, B, U, Y, dZ, M, h, f):
+    ws = torch.empty(max(tp.mlp_bwd_workspace(M, h, f), 1), dtype=torch.uint8, device=DEV)
+    dX = torch.full((M, h), float("nan"), dtype=torch.float32, device=DEV)
+    dA = torch.full((h, f), float("nan"), dtype=torch.float32, device=DEV)
+    dB = torch.full((f, h), float("nan"), dtype=torch.float32, device=DEV)
+    tp.mlp_bwd(X, A, B, U, Y, dZ, dX, dA, dB, ws)
+    return dX, dA, dB, ws
+
+
+def test_config1_fp32_two_shards():
+    c = CONFIGS[1]
+    M = c["b"] * c["s"]
+    inp = mlp_inputs(M, c["h"], c["f_full"], c["N"], "f32", c["seed"], c["sigma_x"], c["sigma_w"], None)
+    note("config 1 fp32 mlp_fwd, 2 shards")
+    X = f32_dev(inp["X"])
+    Zs = []
+    for i, (A_i, B_i) in enumerate(inp["shards"]):
+        f = A_i.shape[1]
+        U, Y, Z = _alloc(M, c["h"], f, torch.float32)
+        tp.mlp_fwd(X, f32_dev(A_i), f32_dev(B_i), Y, Z, U_i=U)
+        torch.cuda.synchronize()
+        r = oracle.mlp_fwd_shard(inp["X"].astype(np.float64), A_i.astype(np.float64), B_i.astype(np.float64),
+                                 matched=False)
+        assert_f32_close(f64_host(U), r["U"], f"U_{i}")
+        assert_f32_close(f64_host(Y), r["Y"], f"Y_{i}")
+        assert_f32_close(f64_host(Z), r["Z"], f"Z_{i}")
+        Zs.append(Z)
+    tot = torch.empty_like(Zs[0])
+    tp.shard_sum(Zs, tot)
+    torch.cuda.synchronize()
+    full = oracle.mlp_fwd_full(*(inp[k].astype(np.float64) for k in "XAB"))
+    assert_f32_close(f64_host(tot), full, "Z_1 + Z_2")
+
+
+def _bf16_mlp_case(M, h, f_full, N, seed, sigma_w, check_unsharded=True):
+    inp = mlp_inputs(M, h, f_full, N, "bf16", seed, 1.0, sigma_w, 1.0)
+    X, dZ = bf16_dev(inp["X"]), bf16_dev(inp["dZ"])
+    Xo, dZo = bf16_bits_to_f64(inp["X"]), bf16_bits_to_f64(inp["dZ"])
+    Zs, dXs = [], []
+    for i, (A_i, B_i) in enumerate(inp["shards"]):
+        f = A_i.shape[1]
+        note(f"bf16 mlp M={M} h={h} f={f} shard {i}/{N}")
+        A, B = bf16_dev(A_i), bf16_dev(B_i)
+        U, Y, Z = _alloc(M, h, f, torch.bfloat16)
+        tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
+        dX, dA, dB, _ = _run_bwd(X, A, B, U, Y, dZ, M, h, f)
+        torch.cuda.synchronize()
+        Ao, Bo = bf16_bits_to_f64(A_i), bf16_bits_to_f64(B_i)
+        r = oracle.mlp_fwd_shard(Xo, Ao, Bo)
+        g = oracle.mlp_bwd_shard(Xo, Ao, Bo, r["U"], r["Y"], dZo)
+        assert_bf16_close(f64_host(U), r["U"], f"U_{i}")
+        assert_bf16_close(f64_host(Y), r["Y"], f"Y_{i}")
+        assert_bf16_close(f64_host(Z), r["Z"], f"Z_{i}")
+        assert_bf16_close(f64_host(dA), g["dA"], f"dA_{i}")
+        assert_bf16_close(f64_host(dB), g["dB"], f"dB_{i}")
+        assert_bf16_close(f64_host(dX), g["dX"], f"dX_{i}")
+        Zs.append((Z, r["Z"]))
+        dXs.append((dX, g["dX"]))
+    for name, parts in (("Z", Zs), ("dX", dXs)):
+        out = torch.empty_like(parts[0][0])
+        tp.shard_sum([p[0] for p in parts], out)
+        torch.cuda.synchronize()
+        assert_bf16_close(f64_host(out), sum(p[1] for p in parts), f"sum of {name}_i")
+    if check_unsharded:
+        Ao, Bo = bf16_bits_to_f64(inp["A"]), bf16_bits_to_f64(inp["B"])
+        out = torch.empty_like(Zs[0][0])
+        tp.shard_sum([p[0] for p in Zs], out)
+        torch.cuda.synchronize()
+        assert_bf16_close(f64_host(out), oracle.mlp_fwd_full(Xo, Ao, Bo), "sum of Z_i vs unsharded")
+
+
+def test_config2_bf16_fwd_bwd_two_shards():
+    c = CONFIGS[2]
+    _bf16_mlp_case(c["b"] * c["s"], c["h"], c["f_full"], c["N"], c["seed"], c["sigma_w"])
+
+
+@pytest.mark.parametrize("M,h,f_full,N", [(300, 512, 1536, 2), (257, 384, 1024, 4), (1, 64, 128, 1),
+                                          (64, 8, 16, 2)])
+def test_ragged_multi_tile(M, h, f_full, N):
+    _bf16_mlp_case(M, h, f_full, N, 2000 + M, 0.05)
+
+
+def test_empty_batch():
+    note("mlp M=0")
+    h, f = 64, 128
+    X = torch.empty(0, h, dtype=torch.bfloat16, device=DEV)
+    A = torch.randn(h, f, device=DEV).to(torch.bfloat16)
+    B = torch.randn(f, h, device=DEV).to(torch.bfloat16)
+    U, Y, Z = _alloc(0, h, f, torch.bfloat16)
+    tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
+    dZ = torch.empty(0, h, dtype=torch.bfloat16, device=DEV)
+    dX, dA, dB, _ = _run_bwd(X, A, B, U, Y, dZ, 0, h, f)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dA) == 0 and torch.count_nonzero(dB) == 0
+
+
+def test_column_linear_without_activation():
+    note("column_linear bf16 no activation M=130 K=256 N=200")
+    rng = np.random.default_rng(5)
+    from workloads import bf16_bits
+    Xb = bf16_bits(rng.standard_normal((130, 256)).astype(np.float32))
+    Wb = bf16_bits((rng.standard_normal((256, 200)) * 0.05).astype(np.float32))
+    Y = torch.empty(130, 200, dtype=torch.bfloat16, device=DEV)
+    tp.column_linear(bf16_dev(Xb), bf16_dev(Wb), Y, act=None)
+    torch.cuda.synchronize()
+    from oracle.bf16 import round_to_bf16
+    ref = round_to_bf16(bf16_bits_to_f64(Xb) @ bf16_bits_to_f64(Wb))
+    assert_bf16_close(f64_host(Y), ref, "X W")
+
+
+class TestConfig3FullSize:
+    """GPT-3-shaped rank shard (M=2048, h=12288, f=6144) in the launch
+    configuration the benchmark times; sampled outputs from the oracle."""
+
+    ROWS = np.array([0, 1, 255, 256, 1023, 1500, 2046, 2047])
+    COLS = np.array([0, 191, 192, 3000, 6143])
+
+    @pytest.fixture(scope="class")
+    def case(self):
+        c = CONFIGS[3]
+        M, h, f = c["b"] * c["s"], c["h"], c["f"]
+        inp = mlp_inputs(M, h, f, 1, "bf16", c["seed"], c["sigma_x"], c["sigma_w"], c["sigma_dz"], full=False)
+        A_i, B_i = inp["shards"][0]
+        note("config 3 full-size mlp_fwd + mlp_bwd")
+        X, A, B, dZ = bf16_dev(inp["X"]), bf16_dev(A_i), bf16_dev(B_i), bf16_dev(inp["dZ"])
+        U, Y, Z = _alloc(M, h, f, torch.bfloat16)
+        tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
+        dX, dA, dB, _ = _run_bwd(X, A, B, U, Y, dZ, M, h, f)
+        torch.cuda.synchronize()
+        o = dict(X=bf16_bits_to_f64(inp["X"]), A=bf16_bits_to_f64(A_i), B=bf16_bits_to_f64(B_i),
+                 dZ=bf16_bits_to_f64(inp["dZ"]))
+        g = dict(U=U, Y=Y, Z=Z, dX=dX, dA=dA, dB=dB)
+        return o, g
+
+    def test_forward_rows(self, case):
+        o, g = case
+        r = oracle.mlp_fwd_rows(o["X"], o["A"], o["B"], self.ROWS)
+        for k in ("U", "Y", "Z"):
+            assert_bf16_close(f64_host(g[k][torch.from_numpy(self.ROWS).to(DEV)]), r[k], f"{k} rows")
+
+    def test_backward_samples(self, case):
+        o, g = case
+        s = oracle.mlp_bwd_cols(o["X"], o["A"], o["B"], o["dZ"], self.ROWS, self.COLS)
+        rows = torch.from_numpy(self.ROWS).to(DEV)
+        cols = torch.from_numpy(self.COLS).to(DEV)
+        assert_bf16_close(f64_host(g["dA"][:, cols]), s["dA_cols"], "dA columns")
+        assert_bf16_close(f64_host(g["dB"][cols, :]), s["dB_rows"], "dB rows")
+        assert_bf16_close(f64_host(g["dX"][rows, :]), s["dX_rows"], "dX rows")
+
+    def test_outputs_finite(self, case):
+        _, g = case
+        for k, t in g.items():
+            assert torch.isfinite(t.float()).all(), k

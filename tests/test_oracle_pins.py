@@ -48,10 +48,16 @@ class TestBf16:
     def test_all_patterns_roundtrip_and_decode(self):
         bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
         vals = ob.bf16_bits_to_f64(bits)
-        finite = np.isfinite(vals)
-        # decode agrees with widening the pattern into the top half of a float32
-        widened = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
-        np.testing.assert_array_equal(vals[finite], widened[finite])
+        # field-by-field decode: sign, 8-bit exponent (bias 127), 7-bit mantissa
+        b = bits.astype(np.int64)
+        sign = np.where(b >> 15, -1.0, 1.0)
+        expo, mant = (b >> 7) & 0xFF, (b & 0x7F).astype(np.float64)
+        ref = np.where(expo == 0, sign * np.ldexp(mant / 128.0, -126),
+                       sign * np.ldexp(1.0 + mant / 128.0, expo - 127))
+        finite = expo != 0xFF
+        np.testing.assert_array_equal(vals[finite], ref[finite])
+        assert np.all(np.isinf(vals[(expo == 0xFF) & (mant == 0)]))
+        assert np.all(np.isnan(vals[(expo == 0xFF) & (mant != 0)]))
         np.testing.assert_array_equal(ob.f64_to_bf16_bits(vals[finite]), bits[finite])
 
     def test_matches_torch_conversion_on_float32(self):
