@@ -117,11 +117,11 @@ TP_API tp_status tp_column_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N, 
   if (act == TP_ACT_NONE && U_out)
     return fail(TP_ERR_INVALID_ARG, "%s: U_out must be NULL without an activation", fn);
   TRY(check_dims(fn, M, K, N));
+  if (M == 0) return ok();  // nothing to compute; empty tensors may carry NULL
   TRY(check_ptr(fn, "X", X));
   TRY(check_ptr(fn, "W", W));
   TRY(check_ptr(fn, "Y_out", Y_out));
   TRY(check_opt_ptr(fn, "U_out", U_out));
-  if (M == 0) return ok();
   if (dt == TP_F32)
     return hip_status(tps::gemm_f32(static_cast<const float*>(X), static_cast<const float*>(W), (int)M, (int)N, (int)K,
                                     static_cast<float*>(Y_out), static_cast<float*>(U_out), act == TP_ACT_GELU,
@@ -140,10 +140,10 @@ TP_API tp_status tp_row_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N, con
   const char* fn = "tp_row_linear";
   if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   TRY(check_dims(fn, M, K, N));
+  if (M == 0) return ok();
   TRY(check_ptr(fn, "Y", Y));
   TRY(check_ptr(fn, "W", W));
   TRY(check_ptr(fn, "Z_out", Z_out));
-  if (M == 0) return ok();
   if (dt == TP_F32)
     return hip_status(tps::gemm_f32(static_cast<const float*>(Y), static_cast<const float*>(W), (int)M, (int)N, (int)K,
                                     Z_out, nullptr, false, as_stream(stream)),
@@ -157,6 +157,7 @@ TP_API tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f, const 
   const char* fn = "tp_mlp_fwd";
   if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   TRY(check_dims(fn, M, h, f));
+  if (M == 0) return ok();
   TRY(check_ptr(fn, "X", X));
   TRY(check_ptr(fn, "A_i", A_i));
   TRY(check_ptr(fn, "B_i", B_i));
@@ -178,16 +179,18 @@ TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, cons
                             void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "tp_mlp_bwd";
   TRY(check_dims(fn, M, h, f));
-  TRY(check_ptr(fn, "X", X));
-  TRY(check_ptr(fn, "A_i", A_i));
-  TRY(check_ptr(fn, "B_i", B_i));
-  if (!U_i) return fail(TP_ERR_UNSUPPORTED, "%s: U_i is required (the saved pre-activation)", fn);
-  TRY(check_ptr(fn, "U_i", U_i));
-  TRY(check_ptr(fn, "Y_i", Y_i));
-  TRY(check_ptr(fn, "dZ", dZ));
-  TRY(check_opt_ptr(fn, "dX_i", dX_i));
   TRY(check_opt_ptr(fn, "dA_i", dA_i));
   TRY(check_opt_ptr(fn, "dB_i", dB_i));
+  if (M > 0) {  // with M == 0 only the (zero) weight gradients are written
+    TRY(check_ptr(fn, "X", X));
+    TRY(check_ptr(fn, "A_i", A_i));
+    TRY(check_ptr(fn, "B_i", B_i));
+    if (!U_i) return fail(TP_ERR_UNSUPPORTED, "%s: U_i is required (the saved pre-activation)", fn);
+    TRY(check_ptr(fn, "U_i", U_i));
+    TRY(check_ptr(fn, "Y_i", Y_i));
+    TRY(check_ptr(fn, "dZ", dZ));
+    TRY(check_opt_ptr(fn, "dX_i", dX_i));
+  }
   const size_t need = tp_mlp_bwd_workspace(M, h, f);
   if (need && (!ws || ws_bytes < need))
     return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
@@ -232,9 +235,9 @@ TP_API tp_status tp_attn_core(int64_t b, int64_t s, int64_t n_heads_local, int64
                               const void* QKV, void* O, void* stream) {
   const char* fn = "tp_attn_core";
   TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  if (b * s == 0) return ok();
   TRY(check_ptr(fn, "QKV", QKV));
   TRY(check_ptr(fn, "O", O));
-  if (b * s == 0) return ok();
   return hip_status(tps::attn_fwd(static_cast<const uint16_t*>(QKV), static_cast<uint16_t*>(O), (int)b, (int)s,
                                   (int)n_heads_local, (int)d_head, causal != 0, as_stream(stream)),
                     fn);
@@ -252,6 +255,7 @@ TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   const char* fn = "tp_attn_fwd";
   TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
   TRY(check_dims(fn, b * s, h, 3 * n_heads_local * d_head));
+  if (b * s == 0) return ok();
   TRY(check_ptr(fn, "X", X));
   TRY(check_ptr(fn, "Wqkv_i", Wqkv_i));
   TRY(check_ptr(fn, "Wo_i", Wo_i));
@@ -262,7 +266,6 @@ TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
                 ws ? "" : " (NULL)");
   TRY(check_opt_ptr(fn, "ws", ws));
   const int64_t M = b * s, w = n_heads_local * d_head;
-  if (M == 0) return ok();
   hipStream_t st = as_stream(stream);
   uint16_t* qkv = static_cast<uint16_t*>(ws);
   uint16_t* O = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + round256((size_t)M * 3 * w * 2));
@@ -287,10 +290,10 @@ TP_API tp_status tp_vocab_embed(const int32_t* ids, int64_t n_tokens, const void
   if (h <= 0) return fail(TP_ERR_INVALID_ARG, "%s: h must be > 0", fn);
   if (h % 8) return fail(TP_ERR_UNSUPPORTED, "%s: h must be a multiple of 8 (got %lld)", fn, (long long)h);
   if (n_tokens > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "%s: n_tokens exceeds 2^31-1", fn);
+  if (n_tokens == 0) return ok();
   if (!ids) return fail(TP_ERR_INVALID_ARG, "%s: ids is NULL", fn);
   TRY(check_ptr(fn, "E_i", E_i));
   TRY(check_ptr(fn, "out", out));
-  if (n_tokens == 0) return ok();
   return hip_status(tps::vocab_gather(ids, n_tokens, static_cast<const uint16_t*>(E_i), lo, hi, h,
                                       static_cast<uint16_t*>(out), as_stream(stream)),
                     fn);
@@ -303,6 +306,7 @@ TP_API tp_status tp_shard_sum(tp_dtype dt, const void* const* partials, int n_pa
   if (n_partials < 1 || n_partials > tps::kMaxPartials)
     return fail(TP_ERR_INVALID_ARG, "%s: n_partials must be in [1, %d] (got %d)", fn, tps::kMaxPartials, n_partials);
   if (numel < 0) return fail(TP_ERR_INVALID_ARG, "%s: numel < 0", fn);
+  if (numel == 0) return ok();
   if (!partials) return fail(TP_ERR_INVALID_ARG, "%s: partials is NULL", fn);
   tps::SumArgs a{};
   for (int i = 0; i < n_partials; ++i) {
@@ -315,6 +319,5 @@ TP_API tp_status tp_shard_sum(tp_dtype dt, const void* const* partials, int n_pa
   a.n = n_partials;
   a.numel = numel;
   a.out = out;
-  if (numel == 0) return ok();
   return hip_status(tps::shard_sum(a, dt == TP_BF16, as_stream(stream)), fn);
 }

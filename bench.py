@@ -1,0 +1,247 @@
+"""Benchmark of one tensor-parallel rank's hot path on one MI355X.
+
+A step is one pass of every step of the rank-shard path over one batch of
+synthetic input already resident in HBM:
+  MLP forward      column GEMM + erf-GeLU, row GEMM -> fp32 partial
+                   (GPT-3 175B shard: X [2048, 12288], A_i [12288, 6144], B_i [6144, 12288])
+  MLP backward     dU, dB_i, dA_i, dX_i
+  shard-sum        8 fp32 partials [2048, 12288] summed in fixed order (all-reduce stand-in)
+  attention shard  QKV GEMM, fused causal attention over 12 local heads of 128,
+                   row-parallel Wo GEMM -> fp32 partial
+  vocab gather     one rank's shard (6288 rows of 12288) for 8 x 2048 token ids
+
+The reported value is the metric: TFLOP/s of the MLP forward + backward
+(1855.43 GFLOP per step), timed with HIP events on the launch stream over the
+timed steps. ms_per_step is the wall time of whole steps. Per-kernel times and
+roofline fractions are in "breakdown"; "roofline" is for the dominant kernel.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "TFLOP/s and % bf16 MFMA peak, rank-shard TP MLP fwd+bwd at h=12288,N=8"
+
+# GPT-3 175B layer, one rank of TP = 8
+M, H, F = 2048, 12288, 6144
+N_PARTIALS = 8
+ATT_B, ATT_S, ATT_HL, ATT_D = 1, 2048, 12, 128
+V, VN, EMB_TOK = 50304, 8, 8 * 2048
+
+
+def gemm_flops(m, n, k):
+    return 2.0 * m * n * k
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    return p.parse_args()
+
+
+def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 12):
+    """Time the float64 oracle (as it stands) on the GPT-3 MLP shard's forward +
+    backward: full passes over the whole batch (M = 2048) of one shard, the same
+    work as the GPU's MLP step, repeated until about min_seconds have elapsed."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    from oracle.bf16 import bf16_bits_to_f64
+    from workloads import CONFIGS, mlp_inputs
+
+    c = CONFIGS[3]
+    Ms = c["b"] * c["s"]
+    inp = mlp_inputs(Ms, c["h"], c["f"], 1, "bf16", c["seed"], c["sigma_x"], c["sigma_w"], c["sigma_dz"],
+                     full=False)
+    A_i, B_i = inp["shards"][0]
+    X, A, B, dZ = (bf16_bits_to_f64(a) for a in (inp["X"], A_i, B_i, inp["dZ"]))
+    passes, dt = 0, 0.0
+    while passes < max_passes and (passes == 0 or dt < min_seconds):
+        t0 = time.perf_counter()
+        f = oracle.mlp_fwd_shard(X, A, B)
+        oracle.mlp_bwd_shard(X, A, B, f["U"], f["Y"], dZ)
+        dt += time.perf_counter() - t0
+        passes += 1
+    flops = passes * 6 * gemm_flops(Ms, c["f"], c["h"])
+    threads = max([d.get("num_threads", 1) for d in threadpool_info() if d.get("user_api") == "blas"] or [1])
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"float64 oracle MLP fwd+bwd of the GPT-3 rank shard (M=2048, h=12288, f=6144), "
+                      f"{passes} full pass(es) in {dt:.2f} s; bf16 storage rounding as on the GPU"}
+
+
+def traffic_from_profiles(kernel_src: str, launches_bytes_key: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if the summary is missing or was taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+        src = open(os.path.join(ROOT, "attention_shard_math_amd", "csrc", kernel_src), "rb").read()
+        if rec.get("source_sha256", {}).get(kernel_src) != hashlib.sha256(src).hexdigest():
+            return None
+        return rec["kernels"][launches_bytes_key]["hbm_bytes_per_launch"]
+    except Exception:
+        return None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build runs the rank shard on a single MI355X "
+              "(no collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import attention_shard_math_amd as tp
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    g = torch.Generator(device=dev)
+
+    def randn(shape, sigma, seed, dtype=torch.bfloat16):
+        g.manual_seed(seed)
+        return (torch.randn(shape, generator=g, device=dev, dtype=torch.float32) * sigma).to(dtype)
+
+    # ---- MLP shard
+    X = randn((M, H), 1.0, 1)
+    A = randn((H, F), 0.006, 2)
+    B = randn((F, H), 0.006, 3)
+    dZ = randn((M, H), 1.0, 4)
+    U = torch.empty(M, F, dtype=torch.bfloat16, device=dev)
+    Y = torch.empty_like(U)
+    Z = torch.empty(M, H, dtype=torch.float32, device=dev)
+    dX = torch.empty(M, H, dtype=torch.float32, device=dev)
+    dA = torch.empty(H, F, dtype=torch.float32, device=dev)
+    dB = torch.empty(F, H, dtype=torch.float32, device=dev)
+    ws = torch.empty(tp.mlp_bwd_workspace(M, H, F), dtype=torch.uint8, device=dev)
+    # ---- shard-sum partials
+    parts = [randn((M * H,), 1.0, 10 + i, torch.float32) for i in range(N_PARTIALS)]
+    Zsum = torch.empty(M * H, dtype=torch.float32, device=dev)
+    # ---- attention shard
+    w = ATT_HL * ATT_D
+    Xa = randn((ATT_B * ATT_S, H), 1.0, 20)
+    Wqkv = randn((H, 3 * w), 0.006, 21)
+    Wo = randn((w, H), 0.006, 22)
+    QKV = torch.empty(ATT_B * ATT_S, 3 * w, dtype=torch.bfloat16, device=dev)
+    O = torch.empty(ATT_B * ATT_S, w, dtype=torch.bfloat16, device=dev)
+    out_att = torch.empty(ATT_B * ATT_S, H, dtype=torch.float32, device=dev)
+    # ---- vocab shard 0 of 8
+    per = V // VN
+    E0 = randn((per, H), 0.02, 30)
+    g.manual_seed(31)
+    ids = torch.randint(0, V, (EMB_TOK,), generator=g, device=dev, dtype=torch.int32)
+    emb = torch.empty(EMB_TOK, H, dtype=torch.bfloat16, device=dev)
+    hits = int(((ids >= 0) & (ids < per)).sum().item())
+
+    rows = [
+        ("mlp_col_gemm_gelu", lambda: tp.column_linear(X, A, Y, U=U, act="gelu")),
+        ("mlp_row_gemm", lambda: tp.row_linear(Y, B, Z)),
+        ("mlp_bwd", lambda: tp.mlp_bwd(X, A, B, U, Y, dZ, dX, dA, dB, ws)),
+        ("shard_sum", lambda: tp.shard_sum(parts, Zsum)),
+        ("attn_qkv_gemm", lambda: tp.column_linear(Xa, Wqkv, QKV, act=None)),
+        ("attn_core", lambda: tp.attn_core(QKV, O, ATT_B, ATT_S, ATT_HL, ATT_D, True)),
+        ("attn_wo_gemm", lambda: tp.row_linear(O, Wo, out_att)),
+        ("vocab_gather", lambda: tp.vocab_embed(ids, E0, 0, per, emb)),
+    ]
+    flops = {
+        "mlp_col_gemm_gelu": gemm_flops(M, F, H),
+        "mlp_row_gemm": gemm_flops(M, H, F),
+        "mlp_bwd": 4 * gemm_flops(M, F, H),
+        "attn_qkv_gemm": gemm_flops(ATT_B * ATT_S, 3 * w, H),
+        "attn_core": 2 * 2.0 * ATT_HL * ATT_D * ATT_B * (ATT_S * (ATT_S + 1) / 2),
+        "attn_wo_gemm": gemm_flops(ATT_B * ATT_S, H, w),
+    }
+    hbm_bytes = {
+        "shard_sum": (N_PARTIALS + 1) * M * H * 4.0,
+        "vocab_gather": EMB_TOK * H * 2.0 + hits * H * 2.0 + EMB_TOK * 4.0,
+    }
+
+    stream = torch.cuda.current_stream()
+    ev = {name: [] for name, _ in rows}
+
+    def step(record):
+        for name, fn in rows:
+            if record:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                ev[name].append((e0, e1))
+            else:
+                fn()
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    ms = {name: sum(a.elapsed_time(b) for a, b in ev[name]) / args.steps for name in ev}
+    mlp_ms = ms["mlp_col_gemm_gelu"] + ms["mlp_row_gemm"] + ms["mlp_bwd"]
+    mlp_flops = flops["mlp_col_gemm_gelu"] + flops["mlp_row_gemm"] + flops["mlp_bwd"]
+    value = mlp_flops / (mlp_ms * 1e-3) / 1e12
+
+    breakdown = {}
+    for name in ms:
+        d = {"ms": round(ms[name], 4)}
+        if name in flops:
+            tf = flops[name] / (ms[name] * 1e-3) / 1e12
+            d.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        if name in hbm_bytes:
+            gbs = hbm_bytes[name] / (ms[name] * 1e-3) / 1e9
+            d.update(gbs=round(gbs, 1), frac_hbm_peak=round(gbs / PEAK_HBM_GBS, 4))
+        breakdown[name] = d
+
+    dom = "mlp_col_gemm_gelu"
+    dom_tf = flops[dom] / (ms[dom] * 1e-3) / 1e12
+    traffic = traffic_from_profiles("gemm_bf16.hip", dom)
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded normal inputs at the stated shapes and sigmas; uniform token ids)",
+        "config": {"workload": "gpt3-175b rank shard, TP=8: MLP fwd+bwd (M=2048, h=12288, f=6144); "
+                               "shard-sum 8x[2048,12288] fp32; causal attention 12 heads x 128, s=2048; "
+                               "vocab gather 16384 ids into a 6288x12288 shard",
+                   "M": M, "h": H, "f": F, "tp": 8, "pct_bf16_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+                   "mlp_fwd_bwd_gflop": round(mlp_flops / 1e9, 2), "mlp_fwd_bwd_ms": round(mlp_ms, 4)},
+        "roofline": {"kernel": "gemm_bf16 column GEMM + erf-GeLU (2048x6144x12288)", "bound": "mfma",
+                     "achieved": round(dom_tf, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "breakdown": breakdown,
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

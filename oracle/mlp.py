@@ -68,9 +68,11 @@ def mlp_bwd_shard(X, A_i, B_i, U_s, Y_s, dZ, matched=True):
     return dict(dU=dU, dB=Y_s.T @ dZ, dA=X.T @ dU, dX=dU @ A_i.T)
 
 
-def mlp_fwd_full(X, A, B):
-    """Unsharded Z = GeLU(X A) B in float64 (the all-reduced result)."""
-    return gelu(X @ A) @ B
+def mlp_fwd_full(X, A, B, matched=False):
+    """Unsharded Z = GeLU(X A) B in float64 (the all-reduced result). With
+    matched=True the activation is rounded to bf16 before the second product,
+    exactly as each rank stores its own column block of it."""
+    return _r(gelu(X @ A), matched) @ B
 
 
 def mlp_bwd_full(X, A, B, dZ):

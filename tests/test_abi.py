@@ -98,6 +98,7 @@ class TestValidation:
         assert s(0, arr, 0, 16, P, None) == INVALID
         assert s(0, arr, 17, 16, P, None) == INVALID
         assert s(0, arr, 4, -1, P, None) == INVALID
+        assert s(0, None, 4, 0, None, None) == OK  # empty: nothing to touch
         assert s(5, arr, 4, 16, P, None) == INVALID
         bad = (C.c_void_p * 2)(P, None)
         assert s(0, bad, 2, 16, P, None) == INVALID

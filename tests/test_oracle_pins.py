@@ -126,6 +126,17 @@ class TestMlpForward:
             np.testing.assert_array_equal(
                 oracle.mlp_fwd_shard(X, A, B, matched=False)["Z"], ref)
 
+    def test_matched_partials_sum_to_matched_unsharded(self):
+        # bf16 rounding of GeLU(XA) is elementwise, so splitting the columns
+        # before or after rounding gives the same rounded activations.
+        inp = mlp_inputs(24, 64, 256, 4, "bf16", 15, 1.0, 0.05, sigma_dz=None)
+        X, A, B = (ob.bf16_bits_to_f64(inp[k]) for k in "XAB")
+        Z = sum(oracle.mlp_fwd_shard(X, ob.bf16_bits_to_f64(a), ob.bf16_bits_to_f64(b))["Z"]
+                for a, b in inp["shards"])
+        ref = oracle.mlp_fwd_full(X, A, B, matched=True)
+        assert np.max(np.abs(Z - ref)) <= 1e-12 * np.max(np.abs(ref))
+        assert np.max(np.abs(ref - oracle.mlp_fwd_full(X, A, B))) > 0  # the rounding is visible
+
     def test_column_shards_concatenate(self):
         inp = mlp_inputs(16, 32, 128, 4, "f32", 12, 1.0, 0.1, sigma_dz=None)
         X, A = inp["X"].astype(np.float64), inp["A"].astype(np.float64)

@@ -118,12 +118,17 @@ def embed_inputs(v: int, h: int, n_tokens: int, seed: int, sigma_w: float = 0.02
                  chunk_rows: int = 4096):
     """Vocab-parallel embedding workload: full table E [v, h] (bf16 bits) drawn
     first, then token ids int32 uniform in [0, v). The table is drawn in row
-    chunks to bound host memory; the stream of samples equals one big draw."""
+    chunks to bound host memory; the stream of samples equals one big draw.
+    Signed zeros are stored as +0.0."""
     rng = np.random.default_rng(seed)
     E = np.empty((v, h), np.uint16)
     for r0 in range(0, v, chunk_rows):
         r1 = min(v, r0 + chunk_rows)
         E[r0:r1] = bf16_bits(draw_normal_f32(rng, (r1 - r0, h), sigma_w))
+    # numpy's float32 normal sampler returns exact zeros (with either sign) about
+    # once per 2^23 draws; keep them as +0.0 so the sum of shards (which adds
+    # +0.0 rows from the ranks that miss) reproduces the table bit for bit.
+    E[E == 0x8000] = 0
     ids = rng.integers(0, v, size=n_tokens, dtype=np.int32)
     return dict(E=E, ids=ids)
 
