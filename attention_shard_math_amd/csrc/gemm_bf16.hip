@@ -7,16 +7,19 @@
 //   epilogues         float32 store | bf16 store | erf-GeLU (store U and GeLU(U) as
 //                     bf16) | GeLU' (dU = acc * GeLU'(U) as bf16)
 //
-// Tiling: a 256-thread workgroup (4 waves, 2 x 2) owns a BM x BN tile of C and
-// walks K in steps of BK = 64. Both operands are staged in LDS as [row][k] with
-// k contiguous, 128 bytes per row, 16-byte chunks XOR-swizzled by the row so that
-// the MFMA fragment reads (32 rows, same chunk) and the transposed stores (8 rows
-// apart, same chunk) spread over all banks. LDS is double-buffered: the global
-// loads of step t+1 are in flight in registers while the MFMAs of step t run;
-// one barrier per step. Operands stored MN-contiguous are read as 8x8 blocks
-// (8 k-rows x 16 bytes) and transposed in registers before the LDS store, so
-// every global read is a coalesced 16-byte load.
+// Data path (no register staging): operand tiles go from HBM straight into LDS
+// with buffer_load_dwordx4 ... lds, into a ring of NS stages of BK = 32 k-values;
+// NS-1 stages are in flight while the MFMAs of the current one run. Each
+// operand keeps its global orientation in LDS:
+//   K-contiguous  -> LDS [row][k]  (64 bytes per row), fragments by ds_read_b128;
+//   MN-contiguous -> LDS [k][row]  (2*R bytes per k), fragments by two
+//                    ds_read_b64_tr_b16, which transpose 4x4 blocks of 16-bit
+//                    values across each 16-lane group into the MFMA layout.
+// A DMA lane always writes the next 16 LDS bytes of its wave's 1 KiB, so the
+// bank swizzles below are applied by choosing which global chunk each lane
+// fetches; both are conflict-free for the fragment reads.
 //
+// Workgroup: 256 threads = 4 waves (2 x 2), one wave per SIMD, BM x BN tile.
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 // remapped so each XCD owns a contiguous range of tiles (shared operand panels
 // stay in that XCD's L2).
@@ -27,105 +30,108 @@ namespace tps {
 
 namespace {
 
-constexpr int BK = 64;          // k per LDS stage (128 bytes per row)
-constexpr int NT = 256;         // threads per workgroup
-constexpr int CHUNKS = BK / 8;  // 16-byte chunks per LDS row
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+#define TPS_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+constexpr int BK = 32;                  // k per LDS stage
+constexpr int NT = 256;                 // threads per workgroup
+constexpr int NS = 5;                   // LDS ring depth
+constexpr uint32_t kOOB = 0x7ffffff0u;  // buffer offset that reads as zero
 
-// Element offset of 16-byte chunk `kc` of LDS row `row`.
-__device__ __forceinline__ int lds_off(int row, int kc) { return row * BK + ((kc ^ swz(row)) << 3); }
+// s_waitcnt immediate that waits until at most n vector-memory operations are
+// outstanding (expcnt and lgkmcnt left unconstrained): vmcnt in bits [3:0] and
+// [15:14], expcnt [6:4], lgkmcnt [11:8].
+constexpr int vmcnt_imm(int n) { return (n & 0xf) | (((n >> 4) & 3) << 14) | (0x7 << 4) | (0xf << 8); }
 
-// ---------------------------------------------------------------- tile loaders
-// K-contiguous source: element (r, k) at src[r * ld + k]. R rows x BK.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0): base address, size in bytes for the range
+// check (reads past it return zero), and the default data format word.
+__device__ __forceinline__ i32x4 make_rsrc(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// ---- K-contiguous operand: LDS [row][k], 4 chunks of 16 bytes per row.
+// Physical chunk = logical chunk ^ swk(row): distinct for rows {0,2,4,6} mod 8
+// and for rows {j, j+4, j+8, j+12} mod 16, i.e. conflict-free ds_read_b128 of
+// 32 consecutive rows whether the LDS serves 8 or 16 lanes per cycle.
+__device__ __forceinline__ int swk(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+__device__ __forceinline__ int kc_off(int row, int c) { return row * BK + ((c ^ swk(row)) << 3); }
+
+// ---- MN-contiguous operand: LDS [k][r], R/8 chunks per k-row. Physical chunk =
+// logical chunk ^ (2 * (k & 3)), which spreads the 4 k-rows read by one 16-lane
+// group (and the 4 x 64 bytes read by 32 lanes) over distinct banks.
 template <int R>
-struct LoaderK {
-  static constexpr int PER = R * CHUNKS / NT;  // 16-byte chunks per thread
-  static_assert(R * CHUNKS % NT == 0, "tile rows must be a multiple of 32");
-  u32x4 v[PER];
+__device__ __forceinline__ int mn_off(int k, int r) {
+  return k * R + ((((r >> 3) ^ ((k & 3) << 1))) << 3) + (r & 7);
+}
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t ld, int row0,
-                                       int rows, int k0, int K, int tid) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = tid + p * NT;
-      const int r = c >> 3, kc = c & 7;
-      const int gr = row0 + r, gk = k0 + kc * 8;
-      if (gr < rows && gk < K)
-        v[p] = *reinterpret_cast<const u32x4*>(src + (int64_t)gr * ld + gk);
-      else
-        v[p] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int c = tid + p * NT;
-      const int r = c >> 3, kc = c & 7;
-      *reinterpret_cast<u32x4*>(lds + lds_off(r, kc)) = v[p];
-    }
-  }
-};
-
-// MN-contiguous source: element (r, k) at src[k * ld + r]. Each active thread
-// reads an 8(k) x 8(r) block as eight 16-byte row loads and transposes it.
-template <int R>
-struct LoaderMN {
-  static constexpr int RB = R / 8;                    // 8-wide blocks along r
-  static constexpr int NBLK = RB * CHUNKS;            // blocks per stage (= R)
-  static constexpr int PER = (NBLK + NT - 1) / NT;    // blocks per thread
-  static_assert(R % 8 == 0, "tile rows must be a multiple of 8");
-  u32x4 v[PER][8];
-
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int64_t ld, int row0,
-                                       int rows, int k0, int K, int tid) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int b = tid + p * NT;
-      const int kb = b / RB, rb = b % RB;
-      const int gr = row0 + rb * 8;
-      const bool ok = (b < NBLK) && (gr < rows);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int gk = k0 + kb * 8 + j;
-        if (ok && gk < K)
-          v[p][j] = *reinterpret_cast<const u32x4*>(src + (int64_t)gk * ld + gr);
-        else
-          v[p][j] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int b = tid + p * NT;
-      if (b >= NBLK) break;
-      const int kb = b / RB, rb = b % RB;
-      // v[p][j] holds r = 0..7 of k-row j (two bf16 per dword). Row r of the
-      // transposed block gathers element r of each of the 8 k-rows.
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 lo, hi;  // r = 2q and r = 2q+1
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a = v[p][2 * w][q], c = v[p][2 * w + 1][q];
-          lo[w] = (a & 0xffffu) | (c << 16);
-          hi[w] = (a >> 16) | (c & 0xffff0000u);
-        }
-        const int r0 = rb * 8 + 2 * q;
-        *reinterpret_cast<u32x4*>(lds + lds_off(r0, kb)) = lo;
-        *reinterpret_cast<u32x4*>(lds + lds_off(r0 + 1, kb)) = hi;
-      }
-    }
-  }
-};
-
+// Issues the DMA of one stage of one operand. R = tile rows (M or N extent).
+// Stage bytes = 64 * R; each wave issues R/64 instructions of 1 KiB.
 template <int R, bool KCONTIG>
-struct LoaderSel;
-template <int R>
-struct LoaderSel<R, true> { using type = LoaderK<R>; };
-template <int R>
-struct LoaderSel<R, false> { using type = LoaderMN<R>; };
+struct Dma {
+  static constexpr int OPS = R / 64;  // wave instructions per wave per stage
+  static_assert(R % 64 == 0, "tile extent must be a multiple of 64");
+  uint32_t base[OPS];  // per-lane element offset at k0 = 0 (kOOB if the row is out of range)
+  int kofs[OPS];       // per-lane k offset inside the stage (for the k bound)
+
+  __device__ __forceinline__ void init(int row0, int rows, int64_t ld, int wave, int lane) {
+#pragma unroll
+    for (int o = 0; o < OPS; ++o) {
+      const int q = (wave * OPS + o) * 64 + lane;  // physical chunk inside the stage
+      if constexpr (KCONTIG) {
+        const int r = q >> 2, kc = (q & 3) ^ swk(r);
+        kofs[o] = kc * 8;
+        base[o] = (row0 + r < rows) ? (uint32_t)((int64_t)(row0 + r) * ld + kc * 8) : kOOB;
+      } else {
+        constexpr int CPR = R / 8;  // chunks per k-row
+        const int k = q / CPR, c = (q % CPR) ^ ((k & 3) << 1);
+        kofs[o] = k;
+        base[o] = (row0 + c * 8 < rows) ? (uint32_t)((int64_t)k * ld + row0 + c * 8) : kOOB;
+      }
+    }
+  }
+  // k0: first k of the stage; ld: leading dimension (elements). The DMA is
+  // issued as inline asm so the compiler's wait insertion does not treat it as
+  // an LDS store it must wait for before every fragment read; completion is
+  // awaited explicitly with s_waitcnt vmcnt before the stage barrier.
+  __device__ __forceinline__ void issue(const i32x4& rs, uint32_t stage_lds, int64_t ld, int k0, int K,
+                                        int wave) const {
+#pragma unroll
+    for (int o = 0; o < OPS; ++o) {
+      const bool kok = k0 + kofs[o] < K;
+      const int64_t add = KCONTIG ? (int64_t)k0 : (int64_t)k0 * ld;
+      const uint32_t off = (base[o] != kOOB && kok) ? (uint32_t)((base[o] + add) * 2) : kOOB;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(stage_lds + (uint32_t)((wave * OPS + o) * 1024));
+      asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs), "{m0}"(dst) : "memory");
+    }
+  }
+};
+
+// MFMA operand fragment for rows [rb, rb+32) of the tile and k-slice kk (16 k):
+// lane l gets row rb + l%32 and k = 16*kk + 8*(l/32) + 0..7.
+template <int R, bool KCONTIG>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* stage, int rb, int kk, int lane) {
+  if constexpr (KCONTIG) {
+    const int row = rb + (lane & 31);
+    return *reinterpret_cast<const bf16x8*>(stage + kc_off(row, 2 * kk + (lane >> 5)));
+  } else {
+    const int g = lane >> 4, s = lane & 15;
+    const int r = rb + 16 * (g & 1) + 4 * (s & 3);
+    const int k = 16 * kk + 8 * (g >> 1) + (s >> 2);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(stage + mn_off<R>(k, r)));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) s16x4*)(stage + mn_off<R>(k + 4, r)));
+    const s16x4 v[2] = {lo, hi};
+    return __builtin_bit_cast(bf16x8, v);
+  }
+}
 
 // ---------------------------------------------------------------- epilogue
 // 32x32 accumulator layout: lane l, register e holds row 8*(e/4) + 4*(l/32) + e%4
@@ -160,11 +166,13 @@ void gemm_bf16_kernel(GemmArgs g) {
   constexpr int WM = 2, WN = 2;                // wave grid
   constexpr int WTM = BM / WM, WTN = BN / WN;  // per-wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
+  constexpr int SA = BM * BK, SB = BN * BK;    // stage sizes (elements)
+  constexpr int DMA_OPS = BM / 64 + BN / 64;   // DMA instructions per wave per stage
+  static_assert((NS - 2) * DMA_OPS < 64, "vmcnt range");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
 
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][BN * BK];
-
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[NS][SA];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[NS][SB];
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
@@ -180,8 +188,16 @@ void gemm_bf16_kernel(GemmArgs g) {
   const int tm = w % tiles_m, tn = w / tiles_m;
   const int m0 = tm * BM, n0 = tn * BN;
 
-  typename LoaderSel<BM, A_K>::type la;
-  typename LoaderSel<BN, B_K>::type lb;
+  // Buffer resources cover each operand exactly; the host checks sizes < 2 GiB.
+  const int64_t a_elems = A_K ? (int64_t)g.M * g.lda : (int64_t)g.K * g.lda;
+  const int64_t b_elems = B_K ? (int64_t)g.N * g.ldb : (int64_t)g.K * g.ldb;
+  const i32x4 ra = make_rsrc(g.A, (uint32_t)(a_elems * 2));
+  const i32x4 rb = make_rsrc(g.B, (uint32_t)(b_elems * 2));
+
+  Dma<BM, A_K> da;
+  Dma<BN, B_K> db;
+  da.init(m0, g.M, g.lda, wave, lane);
+  db.init(n0, g.N, g.ldb, wave, lane);
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -192,49 +208,61 @@ void gemm_bf16_kernel(GemmArgs g) {
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   const int nk = (g.K + BK - 1) / BK;
-  la.load(g.A, g.lda, m0, g.M, 0, g.K, tid);
-  lb.load(g.B, g.ldb, n0, g.N, 0, g.K, tid);
-  la.store(sA[0], tid);
-  lb.store(sB[0], tid);
-  __syncthreads();
-
-  const int fr = lane & 31, fk = lane >> 5;  // fragment row, k-chunk parity
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(g.A, g.lda, m0, g.M, (kt + 1) * BK, g.K, tid);
-      lb.load(g.B, g.ldb, n0, g.N, (kt + 1) * BK, g.K, tid);
+  // prologue: stages 0 .. NS-2 in flight
+  const uint32_t a_lds = lds_addr(&sA[0][0]), b_lds = lds_addr(&sB[0][0]);
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st) {
+    if (st < nk) {
+      da.issue(ra, a_lds + st * SA * 2, g.lda, st * BK, g.K, wave);
+      db.issue(rb, b_lds + st * SB * 2, g.ldb, st * BK, g.K, wave);
     }
-    const uint16_t* a_s = sA[cur];
-    const uint16_t* b_s = sB[cur];
+  }
+
+  const int am = wm * WTM, bn = wn * WTN;
+  int slot = 0;
+  for (int t = 0; t < nk; ++t) {
+    // Stage t complete for this wave: at most the DMA of the (NS-2) later stages
+    // may still be outstanding. Then one barrier makes every wave's part visible
+    // and guarantees everyone is done reading the slot refilled below.
+    if (t + NS - 2 < nk)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * DMA_OPS));
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    // A bare barrier: a workgroup fence would also wait for the later stages'
+    // DMA. The empty asm keeps the compiler from moving LDS reads across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (t + NS - 1 < nk) {
+      const int ws = slot == 0 ? NS - 1 : slot - 1;
+      da.issue(ra, a_lds + ws * SA * 2, g.lda, (t + NS - 1) * BK, g.K, wave);
+      db.issue(rb, b_lds + ws * SB * 2, g.ldb, (t + NS - 1) * BK, g.K, wave);
+    }
+    const uint16_t* a_s = sA[slot];
+    const uint16_t* b_s = sB[slot];
 #pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 af[TM], bfr[TN];
+      bf16x8 fa[TM], fb[TN];
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(a_s + lds_off(wm * WTM + i * 32 + fr, kk * 2 + fk));
+      for (int i = 0; i < TM; ++i) fa[i] = frag<BM, A_K>(a_s, am + i * 32, kk, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(b_s + lds_off(wn * WTN + j * 32 + fr, kk * 2 + fk));
+      for (int j = 0; j < TN; ++j) fb[j] = frag<BN, B_K>(b_s, bn + j * 32, kk, lane);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) {
-      la.store(sA[cur ^ 1], tid);
-      lb.store(sB[cur ^ 1], tid);
-    }
-    __syncthreads();
+    slot = slot == NS - 1 ? 0 : slot + 1;
   }
 
   // ---- epilogue
+  const int fk = lane >> 5, fr = lane & 31;
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      store_tile<EPI>(acc[i][j], g, m0 + wm * WTM + i * 32 + 4 * fk, n0 + wn * WTN + j * 32 + fr);
+      store_tile<EPI>(acc[i][j], g, m0 + am + i * 32 + 4 * fk, n0 + bn + j * 32 + fr);
 }
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
@@ -249,6 +277,10 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 
 hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, int epi, hipStream_t s) {
   constexpr int BM = 256, BN = 192;
+  // buffer loads address each operand with 32-bit byte offsets
+  const int64_t a_bytes = 2 * (a_kcontig ? (int64_t)g.M * g.lda : (int64_t)g.K * g.lda);
+  const int64_t b_bytes = 2 * (b_kcontig ? (int64_t)g.N * g.ldb : (int64_t)g.K * g.ldb);
+  if (a_bytes >= (int64_t)kOOB || b_bytes >= (int64_t)kOOB) return hipErrorInvalidValue;
   if (a_kcontig && !b_kcontig) {
     if (epi == EPI_GELU) return launch<BM, BN, true, false, EPI_GELU>(g, s);
     if (epi == EPI_BF16) return launch<BM, BN, true, false, EPI_BF16>(g, s);
