@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--copy-probe", action="store_true",
+                   help="after the timed steps, run a plain 256 MiB device-to-device copy three times, "
+                        "the calibration kernel for HBM byte counters")
     return p.parse_args()
 
 
@@ -83,18 +86,21 @@ def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 12):
                       f"{passes} full pass(es) in {dt:.2f} s; bf16 storage rounding as on the GPU"}
 
 
-def traffic_from_profiles(kernel_src: str, launches_bytes_key: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if the summary is missing or was taken on a different kernel source."""
+def traffic_from_profiles(key: str):
+    """HBM bytes per launch of one kernel from the committed rocprofv3 counter record
+    (profiles/hbm_traffic.json, FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel
+    calibration), or None when the record is missing or any kernel source it was
+    taken on has changed since."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
-        src = open(os.path.join(ROOT, "attention_shard_math_amd", "csrc", kernel_src), "rb").read()
-        if rec.get("source_sha256", {}).get(kernel_src) != hashlib.sha256(src).hexdigest():
-            return None
-        return rec["kernels"][launches_bytes_key]["hbm_bytes_per_launch"]
+        for name, digest in rec["source_sha256"].items():
+            src = open(os.path.join(ROOT, "attention_shard_math_amd", "csrc", name), "rb").read()
+            if hashlib.sha256(src).hexdigest() != digest:
+                return None
+        return round(rec["kernels"][key]["hbm_bytes_per_launch"])
     except Exception:
         return None
 
@@ -214,7 +220,7 @@ def main():
 
     dom = "mlp_col_gemm_gelu"
     dom_tf = flops[dom] / (ms[dom] * 1e-3) / 1e12
-    traffic = traffic_from_profiles("gemm_bf16.hip", dom)
+    traffic = traffic_from_profiles(dom)
     rec = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -240,6 +246,14 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
+    if args.copy_probe:
+        # Known traffic: 256 MiB read + 256 MiB written per copy (the runtime's blit kernel).
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        rec["copy_probe_bytes_each_way"] = src.numel() * 4
     print(json.dumps(rec), flush=True)
 
 
