@@ -12,19 +12,35 @@
 namespace tps {
 namespace {
 
+// Each thread sums U vectors (256 apart) per partial per iteration, so every
+// thread has N*U 16-byte loads in flight (the kernel is HBM-bound); U shrinks for
+// large N to keep the loads within 128 VGPRs.
+template <int N>
+constexpr int sum_unroll() { return N <= 8 ? 4 : 2; }
+
 template <int N>
 __global__ __launch_bounds__(256) void shard_sum_f32_kernel(SumArgs a) {
+  constexpr int kSumU = sum_unroll<N>();
   const int64_t nvec = a.numel >> 2;
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t stride = (int64_t)gridDim.x * 256 * kSumU;
   f32x4* out = static_cast<f32x4*>(a.out);
-  for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
-    f32x4 x[N];
+  for (int64_t v0 = (int64_t)blockIdx.x * 256 * kSumU + threadIdx.x; v0 < nvec; v0 += stride) {
+    f32x4 x[kSumU][N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) x[i] = __builtin_nontemporal_load(static_cast<const f32x4*>(a.p[i]) + v);
-    f32x4 s = x[0];
+    for (int u = 0; u < kSumU; ++u) {
+      const int64_t v = v0 + u * 256;
 #pragma unroll
-    for (int i = 1; i < N; ++i) s = s + x[i];
-    __builtin_nontemporal_store(s, out + v);
+      for (int i = 0; i < N; ++i)
+        x[u][i] = v < nvec ? __builtin_nontemporal_load(static_cast<const f32x4*>(a.p[i]) + v) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kSumU; ++u) {
+      const int64_t v = v0 + u * 256;
+      f32x4 s = x[u][0];
+#pragma unroll
+      for (int i = 1; i < N; ++i) s = s + x[u][i];
+      if (v < nvec) __builtin_nontemporal_store(s, out + v);
+    }
   }
   // tail (numel % 4 elements), one thread each
   const int64_t t = (nvec << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -71,8 +87,9 @@ template <int N>
 hipError_t launch_sum(const SumArgs& a, bool bf16, hipStream_t s) {
   const int64_t per = bf16 ? 8 : 4;
   const int64_t nvec = a.numel / per;
-  int64_t blocks = (nvec + 255) / 256;
-  const int64_t cap = 256 * 16;  // CUs x resident workgroups worth of waves
+  const int64_t chunk = bf16 ? 256 : 256 * sum_unroll<N>();  // vectors per workgroup per iteration
+  int64_t blocks = (nvec + chunk - 1) / chunk;
+  const int64_t cap = bf16 ? 256 * 16 : 256 * 8;  // enough workgroups to keep every CU busy
   if (blocks > cap) blocks = cap;
   if (blocks < 1) blocks = 1;
   if (bf16)
