@@ -227,6 +227,9 @@ tp_status check_attn_shape(const char* fn, int64_t b, int64_t s, int64_t Hl, int
   if (d != 64 && d != 128) return fail(TP_ERR_UNSUPPORTED, "%s: d_head must be 64 or 128 (got %lld)", fn, (long long)d);
   if (b * s > kMaxDim || 3 * Hl * d > kMaxDim || b * Hl * ((s + 127) / 128) > kMaxDim)
     return fail(TP_ERR_UNSUPPORTED, "%s: problem too large", fn);
+  // The kernel addresses one sequence's K and V rows with 32-bit byte offsets.
+  if ((s + 128) * 3 * Hl * d * 2 >= (int64_t)1 << 31)
+    return fail(TP_ERR_UNSUPPORTED, "%s: s * 3 * n_heads_local * d_head too large for one sequence", fn);
   return TP_OK;
 }
 }  // namespace

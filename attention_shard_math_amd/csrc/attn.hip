@@ -4,55 +4,169 @@
 // not, with the online (running max / running sum) softmax so the s x s score
 // matrix never leaves registers.
 //
-// Work split: one 256-thread workgroup per (sequence, head, 128-query block);
-// each of its 4 waves owns 32 queries. Key/value blocks of 64 keys are staged in
-// LDS (double-buffered, the next block's global loads in flight during the
-// current block's MFMAs): K as [key][d] and V transposed to [d][key] through an
-// 8x8 register transpose. The kernel computes the transposed scores
-// S^T = K Q^T and the transposed output O^T = V^T P^T with
-// v_mfma_f32_32x32x16_bf16, so that in both accumulators a lane owns one query
-// column: the row max, row sum and the rescaling of O stay per lane (one
-// cross-half exchange per block), and P feeds the second product straight from
-// registers. Causal blocks wholly above a wave's queries are skipped; the
-// heaviest query blocks are scheduled first.
+// Work split: one 512-thread workgroup per (sequence, head, 128-query block).
+// Waves 0-3 compute, 32 queries each, over every key of the block; waves 4-7
+// only move data: they load the next 64-key stage from global memory into
+// registers (buffer loads, which read as zero past the last key) and write it
+// to LDS, K as [key][d] and V transposed to [d][key] through a register
+// transpose, while the compute waves work on the current stage (two LDS slots,
+// one barrier per stage). Each SIMD thus runs one compute wave, whose MFMAs and
+// softmax arithmetic overlap with the other wave's loads and LDS writes.
+//
+// The compute wave forms the transposed scores S^T = K Q^T and the transposed
+// output O^T = V^T P^T with v_mfma_f32_32x32x16_bf16, so that in both
+// accumulators a lane owns one query column: the row max, row sum and the
+// rescaling of O stay per lane (one exchange between the two 32-lane halves
+// per stage), and P feeds the second product straight from registers. V^T rows
+// keep each 16-key group in the order 0-3, 8-11, 4-7, 12-15 so that one 16-byte
+// LDS read yields the 8 keys a P^T operand lane holds.
+//
+// The running maximum used as the exponent reference is only raised when a
+// row's maximum exceeds it by more than kTau (log2 units); until then P is
+// formed against the older reference (values up to 2^kTau) and O is not
+// rescaled. Numerator and denominator share the reference, so the result is
+// the same softmax up to rounding.
+//
+// Causal stages wholly above a wave's queries are skipped. Workgroup i runs on
+// XCD i % 8; each XCD takes a contiguous, head-major range of (head, query
+// block) items, heaviest query block first, so the K and V of a head are read
+// from one L2.
 #include "attn.hpp"
 #include "common.hpp"
 
 namespace tps {
 namespace {
 
-constexpr int AQ = 128;  // queries per workgroup
-constexpr int AKV = 64;  // keys per LDS block
+constexpr int AQ = 128;   // queries per workgroup: 4 compute waves x 32
+constexpr int KVB = 64;   // keys per LDS stage: 2 tiles of 32
+constexpr int NT = 512;   // waves 0-3 compute, waves 4-7 load
+constexpr int NP = 256;   // loader threads
 constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kTau = 8.0f;
 
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+// Exchange between lanes l and l ^ 32: max / sum of the two halves' values.
+__device__ __forceinline__ float xhalf_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
+  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
+  const bf2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Returns x unchanged but hides its value from the optimizer, so address math
+// built on it is redone where used instead of occupying registers throughout.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// K stage rows [key][d]: 16-byte chunk c of row key sits at c ^ swz_k(key).
+template <int D>
+__device__ __forceinline__ int swz_k(int key) { return D == 128 ? (key & 15) : ((key >> 1) & 7); }
+// V^T stage rows [d][key'] of 64 keys: 16-byte chunk c of row d sits at c ^ swz_v(d).
+__device__ __forceinline__ int swz_v(int d) { return (d ^ (d >> 3)) & 7; }
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ O,
-                                                       int b, int s, int Hl, float scale_log2) {
-  constexpr int DCH = D / 8;           // 16-byte chunks per K row
-  constexpr int KS = D / 16;           // MFMA k-steps over d
-  constexpr int DT = D / 32;           // O^T tiles along d
-  constexpr int KPER = AKV * DCH / 256;
-  constexpr int VBLK = (AKV / 8) * (D / 8);
-  static_assert(AKV * DCH % 256 == 0 && VBLK <= 256, "tile shape");
+__global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ O, int s,
+                                                      int Hl, int nqb, int per_xcd, int n_items, float scale_log2) {
+  constexpr int DCH = D / 8;                // 16-byte chunks per K row
+  constexpr int KS = D / 16;                // k-steps of S^T over d
+  constexpr int DT = D / 32;                // O^T tiles along d
+  constexpr int KPER = KVB * DCH / NP;      // K chunks each loader thread stages
+  constexpr int NVT = (KVB / 8) * (D / 4);  // V tasks of 8 keys x 4 d
+  constexpr int SK = KVB * D;               // elements per K (and per V^T) stage
+  static_assert(KPER >= 1 && NVT <= NP && NVT % 64 == 0, "stage shape");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * SK];  // [slot][K | V^T]
 
-  __shared__ __attribute__((aligned(16))) uint16_t sK[2][AKV * D];  // [key][d]
-  __shared__ __attribute__((aligned(16))) uint16_t sV[2][D * AKV];  // [d][key]
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int hh = lane >> 5, lr = lane & 31;
-  const int nqb = (s + AQ - 1) / AQ;
-  const int bh = blockIdx.x % (b * Hl);
-  const int qb = nqb - 1 - (int)(blockIdx.x / (b * Hl));
+  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int bh = item / nqb, qb = nqb - 1 - item % nqb;
+  const int tid = threadIdx.x, wave = tid >> 6;
   const int bi = bh / Hl, head = bh % Hl;
   const int64_t ld = 3LL * Hl * D;
   const uint16_t* Qg = qkv + (int64_t)bi * s * ld + (int64_t)head * D;
-  const uint16_t* Kg = Qg + (int64_t)Hl * D;
-  const uint16_t* Vg = Qg + 2LL * Hl * D;
   const int q0 = qb * AQ;
-  const int qw = q0 + wave * 32;
-  const int qrow = qw + lr;
+  const int kv_end = CAUSAL ? min(s, q0 + AQ) : s;
+  const int nkv = (kv_end + KVB - 1) / KVB;
+
+  if (wave >= 4) {
+    // ---------------- loader waves ----------------
+    const int ptid = tid - (NT - NP);
+    // Range of one sequence's K (or V) rows: a load past the last key returns zeros.
+    const int seq_bytes = (s - 1) * (int)ld * 2 + D * 2;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + (int64_t)Hl * D), (short)0, seq_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + 2LL * Hl * D), (short)0, seq_bytes, 0x00020000);
+    const int row_b = (int)ld * 2;
+    u32x4 kreg[KPER];
+    uint2 vreg[8];
+    auto load_kv = [&](int kv0) __attribute__((always_inline)) {
+      const int pt = opaque(ptid);
+#pragma unroll
+      for (int p = 0; p < KPER; ++p) {
+        const int c = pt + p * NP;
+        kreg[p] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (kv0 + c / DCH) * row_b + (c % DCH) * 16, 0, 0));
+      }
+      if (NVT == NP || pt < NVT) {
+        // Task (vd4, vg8): d = 4*vd4 .. 4*vd4+3 of the 8 keys that V^T chunk vg8 holds.
+        const int vd4 = pt % (D / 4), vg8 = pt / (D / 4);
+        const int vbase = (kv0 + 16 * (vg8 >> 1) + 4 * (vg8 & 1)) * row_b + vd4 * 8;
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+          vreg[kk] = __builtin_bit_cast(
+              uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vbase + ((kk & 3) + 8 * (kk >> 2)) * row_b, 0, 0));
+      }
+    };
+    auto store_kv = [&](int buf) __attribute__((always_inline)) {
+      const int pt = opaque(ptid);
+      uint16_t* sK = smem + buf * 2 * SK;
+      uint16_t* sV = sK + SK;
+#pragma unroll
+      for (int p = 0; p < KPER; ++p) {
+        const int c = pt + p * NP, key = c / DCH, ch = c % DCH;
+        *reinterpret_cast<u32x4*>(sK + key * D + ((ch ^ swz_k<D>(key)) << 3)) = kreg[p];
+      }
+      if (NVT == NP || pt < NVT) {
+        const int vd4 = pt % (D / 4), vg8 = pt / (D / 4);
+        // V^T chunk vg8 of row d: keys 16*(vg8/2) + 4*(vg8%2) + {0..3, 8..11}.
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int d = vd4 * 4 + r;
+          u32x4 w;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t a = (r < 2) ? vreg[2 * j].x : vreg[2 * j].y;
+            const uint32_t b = (r < 2) ? vreg[2 * j + 1].x : vreg[2 * j + 1].y;
+            w[j] = __builtin_amdgcn_perm(b, a, (r & 1) ? 0x07060302u : 0x05040100u);
+          }
+          *reinterpret_cast<u32x4*>(sV + d * KVB + ((vg8 ^ swz_v(d)) << 3)) = w;
+        }
+      }
+    };
+    load_kv(0);
+    store_kv(0);
+    if (nkv > 1) load_kv(KVB);
+    __syncthreads();
+    for (int it = 0; it < nkv; ++it) {
+      if (it + 1 < nkv) store_kv((it + 1) & 1);
+      if (it + 2 < nkv) load_kv((it + 2) * KVB);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- compute waves ----------------
+  const int lane = tid & 63, qg = wave;
+  const int hh = lane >> 5, lr = lane & 31;
+  const int qw = q0 + qg * 32, qrow = qw + lr;
 
   // Q^T fragments (B operand of S^T = K Q^T): query qrow, d chunk 2*ks + hh.
   bf16x8 qf[KS];
@@ -62,163 +176,131 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
     if (qrow < s) v = *reinterpret_cast<const u32x4*>(Qg + (int64_t)qrow * ld + (2 * ks + hh) * 8);
     qf[ks] = __builtin_bit_cast(bf16x8, v);
   }
-
   f32x16 ot[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) ot[i][e] = 0.f;
-  float m_i = kNegInf, l_i = 0.f;
+  float m_i = kNegInf;  // exponent reference of the row (scaled scores, log2 units)
+  float l_i = 0.f;      // this lane-half's share of the row sum
 
-  const int kv_end = CAUSAL ? min(s, q0 + AQ) : s;
-  const int nkv = (kv_end + AKV - 1) / AKV;
-
-  u32x4 kreg[KPER];
-  u32x4 vreg[8];
-  auto load_kv = [&](int kv0) {
-#pragma unroll
-    for (int p = 0; p < KPER; ++p) {
-      const int c = tid + p * 256, r = c / DCH, ch = c % DCH, key = kv0 + r;
-      kreg[p] = key < s ? *reinterpret_cast<const u32x4*>(Kg + (int64_t)key * ld + ch * 8) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (tid < VBLK) {
-      const int kb = tid / (D / 8), db = tid % (D / 8);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = kv0 + kb * 8 + j;
-        vreg[j] = key < s ? *reinterpret_cast<const u32x4*>(Vg + (int64_t)key * ld + db * 8) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto store_kv = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < KPER; ++p) {
-      const int c = tid + p * 256, r = c / DCH, ch = c % DCH;
-      *reinterpret_cast<u32x4*>(sK[buf] + r * D + ((ch ^ (r & (DCH - 1))) << 3)) = kreg[p];
-    }
-    if (tid < VBLK) {
-      const int kb = tid / (D / 8), db = tid % (D / 8);
-      // vreg[j] holds d = db*8 + 0..7 of key kb*8 + j; row d of V^T gathers
-      // element d of each of the 8 keys.
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        u32x4 lo, hi;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-          const uint32_t a = vreg[2 * w][q], c = vreg[2 * w + 1][q];
-          lo[w] = (a & 0xffffu) | (c << 16);
-          hi[w] = (a >> 16) | (c & 0xffff0000u);
-        }
-        const int d0 = db * 8 + 2 * q;
-        *reinterpret_cast<u32x4*>(sV[buf] + d0 * AKV + ((kb ^ swz8(d0)) << 3)) = lo;
-        *reinterpret_cast<u32x4*>(sV[buf] + (d0 + 1) * AKV + ((kb ^ swz8(d0 + 1)) << 3)) = hi;
-      }
-    }
-  };
-
-  load_kv(0);
-  store_kv(0);
   __syncthreads();
-
   for (int it = 0; it < nkv; ++it) {
-    const int cur = it & 1, kv0 = it * AKV;
-    if (it + 1 < nkv) load_kv(kv0 + AKV);
-    const bool active = !CAUSAL || kv0 <= qw + 31;
-    if (active) {
-      const uint16_t* kS = sK[cur];
-      const uint16_t* vS = sV[cur];
-      // S^T block: 2 tiles of 32 keys x 32 queries. Accumulator lane l, reg e:
-      // key 32t + 8*(e/4) + 4*hh + e%4, query lr.
-      f32x16 st[2];
+    const int kv0 = it * KVB;
+    const uint16_t* sK = smem + (it & 1) * 2 * SK;
+    const uint16_t* sV = sK + SK;
+    // Wave-uniform: skip the stage if its first key is above the diagonal or past the end.
+    if (!((CAUSAL && kv0 > qw) || kv0 >= s)) {
+      // K fragments of both 32-key tiles, then S^T = K Q^T.
+      bf16x8 kf[2][KS];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st[t][e] = 0.f;
         const int kr = 32 * t + lr;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kS + kr * D + (((2 * ks + hh) ^ (kr & (DCH - 1))) << 3));
-          st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[t], 0, 0, 0);
-        }
+        for (int ks = 0; ks < KS; ++ks)
+          kf[t][ks] = *reinterpret_cast<const bf16x8*>(sK + kr * D + (((2 * ks + hh) ^ swz_k<D>(kr)) << 3));
       }
-      float mx = kNegInf;
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 st[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = kv0 + 32 * t + 8 * (e >> 2) + 4 * hh + (e & 3);
-          float v = st[t][e] * scale_log2;
-          if ((CAUSAL && key > qrow) || key >= s) v = kNegInf;
-          st[t][e] = v;
-          mx = fmaxf(mx, v);
+        for (int e = 0; e < 16; ++e) st[t][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][ks], qf[ks], st[t], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // V^T fragments of tile 0 (16-key groups 0 and 1).
+      bf16x8 vf[2][DT];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+          const int d = 32 * i + lr;
+          vf[s2][i] = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((2 * s2 + hh) ^ swz_v(d)) << 3));
         }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_i, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = exp2f(m_i - m_use);
+      __builtin_amdgcn_sched_barrier(0);
+      // S^T accumulator lane (lr, hh), reg e of tile t: key kv0 + 32t + 8(e/4) + 4hh + e%4, query qrow.
+      if ((CAUSAL && kv0 + KVB - 1 > qw) || kv0 + KVB > s) {
+        // key - (kv0 + 4hh) = 32t + 8(e/4) + e%4 may not exceed lim.
+        const int lim = (CAUSAL ? min(qrow, s - 1) : s - 1) - kv0 - 4 * hh;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * t + 8 * (e >> 2) + (e & 3) > lim) st[t][e] = kNegInf;
+      }
+      float mx = fmaxf(st[0][0], st[1][0]);
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(st[0][e], st[1][e]));
+      const float mt = xhalf_max(mx) * scale_log2;
+      // Raise the reference only when some row's maximum has passed it by more
+      // than kTau; rows that have not keep their reference (factor 1).
+      if (__builtin_amdgcn_ballot_w64(mt > m_i + kTau) != 0) {
+        const float mn = fmaxf(m_i, mt);
+        const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_i - mn);
+        l_i *= alpha;
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ot[i][e] *= alpha;
+        m_i = mn;
+      }
+      const float mref = m_i == kNegInf ? 0.f : m_i;
       float rs = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(st[t][e] - m_use);
-          st[t][e] = p;
-          rs += p;
-        }
-      rs += __shfl_xor(rs, 32);
-      l_i = l_i * alpha + rs;
-      m_i = m_new;
-#pragma unroll
-      for (int i = 0; i < DT; ++i)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ot[i][e] *= alpha;
-      // P^T as B operands: tile t, step s2 takes registers 8*s2 .. 8*s2+7, i.e.
-      // keys 32t + 16*s2 + {4hh + 0..3, 8 + 4hh + 0..3}.
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 pb[2];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           u32x4 u;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) u[w] = pack_bf16x2(st[t][8 * s2 + 2 * w], st[t][8 * s2 + 2 * w + 1]);
-          pb[t][s2] = __builtin_bit_cast(bf16x8, u);
-        }
-      // O^T += V^T P^T. A operand: d row 32i + lr, the same 8 keys as pb.
-#pragma unroll
-      for (int i = 0; i < DT; ++i) {
-        const int d = 32 * i + lr;
-        const uint16_t* vrow = vS + d * AKV;
-        const int sw = swz8(d);
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2) {
-            const int c0 = 4 * t + 2 * s2;
-            const uint2 x0 = *reinterpret_cast<const uint2*>(vrow + ((c0 ^ sw) << 3) + 4 * hh);
-            const uint2 x1 = *reinterpret_cast<const uint2*>(vrow + (((c0 + 1) ^ sw) << 3) + 4 * hh);
-            const u32x4 u = {x0.x, x0.y, x1.x, x1.y};
-            ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pb[t][s2], ot[i], 0, 0, 0);
+          for (int w = 0; w < 4; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][8 * s2 + 2 * w], scale_log2, -mref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][8 * s2 + 2 * w + 1], scale_log2, -mref));
+            rs += p0 + p1;
+            u[w] = cvt_bf16x2(p0, p1);
           }
+          pb[s2] = __builtin_bit_cast(bf16x8, u);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // O^T += V^T P^T over the 16-key groups 2t + s2; P^T lane (lr, hh) holds
+        // keys {4hh + 0..3, 8 + 4hh + 0..3} of the group = V^T chunk 2(2t + s2) + hh.
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int i = 0; i < DT; ++i) ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s2][i], pb[s2], ot[i], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (t == 0) {
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int i = 0; i < DT; ++i) {
+              const int d = 32 * i + lr;
+              vf[s2][i] = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((4 + 2 * s2 + hh) ^ swz_v(d)) << 3));
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
+      l_i += rs;
     }
-    if (it + 1 < nkv) store_kv(cur ^ 1);
     __syncthreads();
   }
 
-  // O^T accumulator: lane l, reg e holds d = 32i + 8*(e/4) + 4*hh + e%4 of query lr:
-  // four consecutive d per register group -> one 8-byte store each.
   if (qrow < s) {
-    const float inv = 1.f / l_i;
-    uint16_t* orow = O + ((int64_t)bi * s + qrow) * ((int64_t)Hl * D) + (int64_t)head * D;
+    const int ln = opaque(lane), lr2 = ln & 31, hh2 = ln >> 5;
+    const float inv = 1.f / xhalf_sum(l_i);
+    uint16_t* orow = O + ((int64_t)bi * s + qw + lr2) * ((int64_t)Hl * D) + (int64_t)head * D;
+    // O^T accumulator lane (lr, hh), reg e of tile i: d = 32i + 8(e/4) + 4hh + e%4.
 #pragma unroll
     for (int i = 0; i < DT; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 u;
-        u.x = pack_bf16x2(ot[i][4 * g] * inv, ot[i][4 * g + 1] * inv);
-        u.y = pack_bf16x2(ot[i][4 * g + 2] * inv, ot[i][4 * g + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * i + 8 * g + 4 * hh) = u;
+        u.x = cvt_bf16x2(ot[i][4 * g] * inv, ot[i][4 * g + 1] * inv);
+        u.y = cvt_bf16x2(ot[i][4 * g + 2] * inv, ot[i][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * i + 8 * g + 4 * hh2) = u;
       }
   }
 }
@@ -226,10 +308,14 @@ __global__ __launch_bounds__(256) void attn_fwd_kernel(const uint16_t* __restric
 template <int D, bool C>
 hipError_t launch_attn(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, hipStream_t st) {
   const int nqb = (s + AQ - 1) / AQ;
-  const int64_t blocks = (int64_t)b * Hl * nqb;
-  if (blocks == 0) return hipSuccess;
+  const int64_t items = (int64_t)b * Hl * nqb;
+  if (items == 0) return hipSuccess;
+  // Buffer offsets are 32-bit: the furthest key row read is s - 1 + 2 stages.
+  if (items > (1LL << 28) || (int64_t)(s + 2 * KVB) * 3 * Hl * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  const int per_xcd = (int)((items + 7) / 8);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, C>), dim3((unsigned)blocks), dim3(256), 0, st, qkv, O, b, s, Hl, scale_log2);
+  hipLaunchKernelGGL((attn_fwd_kernel<D, C>), dim3(8u * per_xcd), dim3(NT), 0, st, qkv, O, s, Hl, nqb, per_xcd,
+                     (int)items, scale_log2);
   return hipGetLastError();
 }
 

@@ -119,7 +119,9 @@ size_t tp_mlp_bwd_workspace(int64_t M, int64_t h, int64_t f);
  *       at columns j*d .. (j+1)*d of each block.
  *   O   [b*s, Hl*d] bf16: O_j = softmax(Q_j K_j^T / sqrt(d)) V_j per sequence;
  *       with causal != 0 query t sees keys u <= t.
- * d must be 64 or 128. Softmax in float32, P rounded to bf16 for the P V product. */
+ * d must be 64 or 128, and (s + 128) * 3 * n_heads_local * d * 2 < 2^31 (one
+ * sequence's rows are addressed with 32-bit byte offsets); otherwise
+ * TP_ERR_UNSUPPORTED. Softmax in float32, P rounded to bf16 for the P V product. */
 tp_status tp_attn_core(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head,
                        int causal, const void* QKV, void* O, void* stream);
 
