@@ -19,7 +19,12 @@
 // bank swizzles below are applied by choosing which global chunk each lane
 // fetches; both are conflict-free for the fragment reads.
 //
-// Workgroup: 256 threads = 4 waves (2 x 2), one wave per SIMD, BM x BN tile.
+// Workgroup: 768 threads = 12 waves for one BM x BN tile. Waves 0-7 only read
+// LDS and issue MFMAs (a 4 x 2 grid of 64 x 96 wave tiles, the next k-step's
+// fragments read while the current one's MFMAs run); waves 8-11 only issue the
+// DMA of the ring and wait for it. A wave blocked issuing memory instructions
+// (the texture unit accepts them at its own rate) thus never holds up the MFMA
+// stream of its SIMD; each SIMD runs two MFMA waves and one DMA wave.
 // Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
 // remapped so each XCD owns a contiguous range of tiles (shared operand panels
 // stay in that XCD's L2).
@@ -34,7 +39,9 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define TPS_LDS(p) ((__attribute__((address_space(3))) void*)(p))
 
 constexpr int BK = 32;                  // k per LDS stage
-constexpr int NT = 256;                 // threads per workgroup
+constexpr int NCW = 8;                  // MFMA waves (4 x 2 grid)
+constexpr int NPW = 4;                  // DMA waves
+constexpr int NT = 64 * (NCW + NPW);    // threads per workgroup
 constexpr int NS = 5;                   // LDS ring depth
 constexpr uint32_t kOOB = 0x7ffffff0u;  // buffer offset that reads as zero
 
@@ -72,11 +79,11 @@ __device__ __forceinline__ int mn_off(int k, int r) {
 }
 
 // Issues the DMA of one stage of one operand. R = tile rows (M or N extent).
-// Stage bytes = 64 * R; each wave issues R/64 instructions of 1 KiB.
+// Stage bytes = 64 * R = R/16 instructions of 1 KiB, split over the DMA waves.
 template <int R, bool KCONTIG>
 struct Dma {
-  static constexpr int OPS = R / 64;  // wave instructions per wave per stage
-  static_assert(R % 64 == 0, "tile extent must be a multiple of 64");
+  static constexpr int OPS = R / 16 / NPW;  // instructions per DMA wave per stage
+  static_assert(R % 64 == 0 && (R / 16) % NPW == 0, "tile extent must be a multiple of 64");
   uint32_t base[OPS];  // per-lane element offset at k0 = 0 (kOOB if the row is out of range)
   int kofs[OPS];       // per-lane k offset inside the stage (for the k bound)
 
@@ -161,13 +168,13 @@ __device__ __forceinline__ void store_tile(const f32x16 a, const GemmArgs& g, in
 
 // ---------------------------------------------------------------- kernel
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gemm_bf16_kernel(GemmArgs g) {
-  constexpr int WM = 2, WN = 2;                // wave grid
+  constexpr int WM = NCW / 2, WN = 2;          // MFMA wave grid
   constexpr int WTM = BM / WM, WTN = BN / WN;  // per-wave tile
   constexpr int TM = WTM / 32, TN = WTN / 32;  // 32x32 MFMA tiles per wave
   constexpr int SA = BM * BK, SB = BN * BK;    // stage sizes (elements)
-  constexpr int DMA_OPS = BM / 64 + BN / 64;   // DMA instructions per wave per stage
+  constexpr int DMA_OPS = (BM + BN) / 16 / NPW;  // DMA instructions per DMA wave per stage
   static_assert((NS - 2) * DMA_OPS < 64, "vmcnt range");
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be a multiple of 32");
 
@@ -194,11 +201,53 @@ void gemm_bf16_kernel(GemmArgs g) {
   const i32x4 ra = make_rsrc(g.A, (uint32_t)(a_elems * 2));
   const i32x4 rb = make_rsrc(g.B, (uint32_t)(b_elems * 2));
 
-  Dma<BM, A_K> da;
-  Dma<BN, B_K> db;
-  da.init(m0, g.M, g.lda, wave, lane);
-  db.init(n0, g.N, g.ldb, wave, lane);
+  const int nk = (g.K + BK - 1) / BK;
+  const uint32_t a_lds = lds_addr(&sA[0][0]), b_lds = lds_addr(&sB[0][0]);
+  if (wave >= NCW) {
+    // ---- DMA waves: stages 0 .. NS-2 in flight, then one refill per stage.
+    const int pw = wave - NCW;
+    Dma<BM, A_K> da;
+    Dma<BN, B_K> db;
+    da.init(m0, g.M, g.lda, pw, lane);
+    db.init(n0, g.N, g.ldb, pw, lane);
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st) {
+      if (st < nk) {
+        da.issue(ra, a_lds + st * SA * 2, g.lda, st * BK, g.K, pw);
+        db.issue(rb, b_lds + st * SB * 2, g.ldb, st * BK, g.K, pw);
+      }
+    }
+    int slot = 0;
+    for (int t = 0; t < nk; ++t) {
+      // Stage t complete for this wave: at most the DMA of the later stages
+      // already issued may be outstanding. The barrier then makes every DMA
+      // wave's part visible, and tells that the MFMA waves are done with stage
+      // t-1, whose slot is refilled below.
+      const int after = min(t + NS - 2, nk - 1) - t;
+      if (after >= 3)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA_OPS));
+      else if (after == 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_OPS));
+      else if (after == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_OPS));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      // A bare barrier: a workgroup fence would also wait for the later stages'
+      // DMA. The empty asm keeps the compiler from moving memory ops across it.
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + NS - 1 < nk) {
+        const int ws = slot == 0 ? NS - 1 : slot - 1;
+        da.issue(ra, a_lds + ws * SA * 2, g.lda, (t + NS - 1) * BK, g.K, pw);
+        db.issue(rb, b_lds + ws * SB * 2, g.ldb, (t + NS - 1) * BK, g.K, pw);
+      }
+      slot = slot == NS - 1 ? 0 : slot + 1;
+    }
+    return;
+  }
 
+  // ---- MFMA waves
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
@@ -207,51 +256,35 @@ void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int nk = (g.K + BK - 1) / BK;
-  // prologue: stages 0 .. NS-2 in flight
-  const uint32_t a_lds = lds_addr(&sA[0][0]), b_lds = lds_addr(&sB[0][0]);
-#pragma unroll
-  for (int st = 0; st < NS - 1; ++st) {
-    if (st < nk) {
-      da.issue(ra, a_lds + st * SA * 2, g.lda, st * BK, g.K, wave);
-      db.issue(rb, b_lds + st * SB * 2, g.ldb, st * BK, g.K, wave);
-    }
-  }
-
   const int am = wm * WTM, bn = wn * WTN;
   int slot = 0;
   for (int t = 0; t < nk; ++t) {
-    // Stage t complete for this wave: at most the DMA of the (NS-2) later stages
-    // may still be outstanding. Then one barrier makes every wave's part visible
-    // and guarantees everyone is done reading the slot refilled below.
-    if (t + NS - 2 < nk)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm((NS - 2) * DMA_OPS));
-    else
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    // A bare barrier: a workgroup fence would also wait for the later stages'
-    // DMA. The empty asm keeps the compiler from moving LDS reads across it.
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (t + NS - 1 < nk) {
-      const int ws = slot == 0 ? NS - 1 : slot - 1;
-      da.issue(ra, a_lds + ws * SA * 2, g.lda, (t + NS - 1) * BK, g.K, wave);
-      db.issue(rb, b_lds + ws * SB * 2, g.ldb, (t + NS - 1) * BK, g.K, wave);
-    }
     const uint16_t* a_s = sA[slot];
     const uint16_t* b_s = sB[slot];
+    // Fragments double-buffered over the stage's k-steps.
+    constexpr int NKK = BK / 16;
+    bf16x8 fa[2][TM], fb[2][TN];
 #pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      bf16x8 fa[TM], fb[TN];
+    for (int i = 0; i < TM; ++i) fa[0][i] = frag<BM, A_K>(a_s, am + i * 32, 0, lane);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) fa[i] = frag<BM, A_K>(a_s, am + i * 32, kk, lane);
+    for (int j = 0; j < TN; ++j) fb[0][j] = frag<BN, B_K>(b_s, bn + j * 32, 0, lane);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) fb[j] = frag<BN, B_K>(b_s, bn + j * 32, kk, lane);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int cb = kk & 1;
+      if (kk + 1 < NKK) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i) fa[cb ^ 1][i] = frag<BM, A_K>(a_s, am + i * 32, kk + 1, lane);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) fb[cb ^ 1][j] = frag<BN, B_K>(b_s, bn + j * 32, kk + 1, lane);
+      }
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
     }
     slot = slot == NS - 1 ? 0 : slot + 1;
   }
