@@ -15,6 +15,7 @@ from ._lib import (  # noqa: F401
     mlp_fwd,
     mlp_bwd,
     mlp_bwd_workspace,
+    mlp_bwd_recompute_workspace,
     attn_core,
     attn_fwd,
     attn_fwd_workspace,

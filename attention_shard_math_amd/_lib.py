@@ -37,6 +37,8 @@ for _name, _args in _SIGS.items():
     _f.restype = C.c_int
 lib.tp_mlp_bwd_workspace.argtypes = [_i64, _i64, _i64]
 lib.tp_mlp_bwd_workspace.restype = _sz
+lib.tp_mlp_bwd_recompute_workspace.argtypes = [_i64, _i64, _i64]
+lib.tp_mlp_bwd_recompute_workspace.restype = _sz
 lib.tp_attn_fwd_workspace.argtypes = [_i64, _i64, _i64, _i64]
 lib.tp_attn_fwd_workspace.restype = _sz
 lib.tp_status_string.argtypes = [C.c_int]
@@ -116,6 +118,10 @@ def mlp_fwd(X, A_i, B_i, Y_i, Z_i, U_i=None, stream=None):
 
 def mlp_bwd_workspace(M, h, f) -> int:
     return int(lib.tp_mlp_bwd_workspace(M, h, f))
+
+
+def mlp_bwd_recompute_workspace(M, h, f) -> int:
+    return int(lib.tp_mlp_bwd_recompute_workspace(M, h, f))
 
 
 def mlp_bwd(X, A_i, B_i, U_i, Y_i, dZ, dX_i, dA_i, dB_i, ws, stream=None):

@@ -174,6 +174,12 @@ TP_API size_t tp_mlp_bwd_workspace(int64_t M, int64_t h, int64_t f) {
   return round256((size_t)M * (size_t)f * 2);
 }
 
+TP_API size_t tp_mlp_bwd_recompute_workspace(int64_t M, int64_t h, int64_t f) {
+  (void)h;
+  if (M < 0 || f < 0) return 0;
+  return 3 * round256((size_t)M * (size_t)f * 2);
+}
+
 TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, const void* A_i, const void* B_i,
                             const void* U_i, const void* Y_i, const void* dZ, float* dX_i, float* dA_i, float* dB_i,
                             void* ws, size_t ws_bytes, void* stream) {
@@ -185,19 +191,29 @@ TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, cons
     TRY(check_ptr(fn, "X", X));
     TRY(check_ptr(fn, "A_i", A_i));
     TRY(check_ptr(fn, "B_i", B_i));
-    if (!U_i) return fail(TP_ERR_UNSUPPORTED, "%s: U_i is required (the saved pre-activation)", fn);
-    TRY(check_ptr(fn, "U_i", U_i));
-    TRY(check_ptr(fn, "Y_i", Y_i));
+    TRY(check_opt_ptr(fn, "U_i", U_i));
+    TRY(check_opt_ptr(fn, "Y_i", Y_i));
     TRY(check_ptr(fn, "dZ", dZ));
     TRY(check_opt_ptr(fn, "dX_i", dX_i));
   }
-  const size_t need = tp_mlp_bwd_workspace(M, h, f);
+  // Without a saved U_i or Y_i the column GEMM + GeLU is recomputed into the
+  // workspace, with the forward's kernel, so the bits equal the forward's.
+  const bool recompute = M > 0 && (!U_i || !Y_i);
+  const size_t need = recompute ? tp_mlp_bwd_recompute_workspace(M, h, f) : tp_mlp_bwd_workspace(M, h, f);
   if (need && (!ws || ws_bytes < need))
     return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
                 ws ? "" : " (NULL)");
   TRY(check_opt_ptr(fn, "ws", ws));
   hipStream_t s = as_stream(stream);
   uint16_t* dU = static_cast<uint16_t*>(ws);
+  if (recompute) {
+    const size_t act = round256((size_t)M * (size_t)f * 2);
+    uint16_t* U_re = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + act);
+    uint16_t* Y_re = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + 2 * act);
+    TRY(tp_column_linear(TP_BF16, M, h, f, X, A_i, U_re, Y_re, TP_ACT_GELU, stream));
+    if (!U_i) U_i = U_re;
+    if (!Y_i) Y_i = Y_re;
+  }
   if (M > 0) {
     // dU = (dZ B_i^T) * GeLU'(U_i): A = dZ [M,h] (K-contig), B(k,n) = B_i[n, k] (K-contig).
     tps::GemmArgs g = make_args(dZ, h, B_i, h, M, f, h, dU, f);

@@ -103,14 +103,21 @@ tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f,
  *  column splits) and 二、MLP层 §2.1 (g's and f's backward).]
  *   X [M,h], A_i [h,f], B_i [f,h], U_i [M,f], Y_i [M,f], dZ [M,h]: bf16.
  *   Any of dX_i, dA_i, dB_i may be NULL to skip that product.
- *   ws: device workspace of at least tp_mlp_bwd_workspace(M, h, f) bytes.
- * Kernels run in the order dU, dB, dA, dX on `stream`. */
+ *   U_i and Y_i may be NULL: activation recompute. U_i and Y_i are then formed
+ *   again from X and A_i by the forward's own column GEMM + GeLU (same bits),
+ *   at the cost of one more M x f x h product. [discosf.com/news/5875844, §2.3
+ *   序列并行与激活重计算 (activation recomputation).]
+ *   ws: device workspace of at least tp_mlp_bwd_workspace(M, h, f) bytes, or
+ *   tp_mlp_bwd_recompute_workspace(M, h, f) bytes when U_i or Y_i is NULL.
+ * Kernels run in the order [U/Y recompute], dU, dB, dA, dX on `stream`. */
 tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f,
                      const void* X, const void* A_i, const void* B_i,
                      const void* U_i, const void* Y_i, const void* dZ,
                      float* dX_i, float* dA_i, float* dB_i,
                      void* ws, size_t ws_bytes, void* stream);
 size_t tp_mlp_bwd_workspace(int64_t M, int64_t h, int64_t f);
+/* Workspace of tp_mlp_bwd when U_i or Y_i is NULL: dU_i, U_i and Y_i, bf16 [M, f] each. */
+size_t tp_mlp_bwd_recompute_workspace(int64_t M, int64_t h, int64_t f);
 
 /* Causal (or full) softmax attention over one rank's local heads, bf16.
  * [Megatron-LM：张量并行与大规模训练, §2.2; m.youleyou.com/wenzhang/3143730,

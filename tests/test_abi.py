@@ -68,7 +68,13 @@ class TestValidation:
         assert need == M * f * 2 and need % 256 == 0
         assert lib.tp_mlp_bwd_workspace(3, 8, 8) == 256
         b = lib.tp_mlp_bwd
-        assert b(M, h, f, P, P, P, None, P, P, P, P, P, P, need, None) == UNSUPPORTED  # U_i missing
+        # U_i (or Y_i) NULL selects activation recompute, which needs the larger workspace
+        need_re = lib.tp_mlp_bwd_recompute_workspace(M, h, f)
+        assert need_re == 3 * need
+        assert b(M, h, f, P, P, P, None, P, P, P, P, P, P, need, None) == WORKSPACE
+        assert b(M, h, f, P, P, P, P, None, P, P, P, P, P, need_re - 1, None) == WORKSPACE
+        assert b(M, h, f, P, P, P, None, None, None, P, P, P, P, need_re, None) == INVALID  # dZ NULL
+        assert b(M, h, f, P, P, P, MIS, P, P, P, P, P, P, need_re, None) == UNSUPPORTED  # misaligned U_i
         assert b(M, h, f, P, P, P, P, P, P, P, P, P, P, need - 1, None) == WORKSPACE
         assert b(M, h, f, P, P, P, P, P, P, P, P, P, None, need, None) == WORKSPACE
         assert "workspace" in _err()

@@ -174,3 +174,71 @@ class TestConfig3FullSize:
         _, g = case
         for k, t in g.items():
             assert torch.isfinite(t.float()).all(), k
+
+
+@pytest.mark.parametrize("M,h,f", [(32, 1024, 2048), (300, 512, 768), (1, 64, 128)])
+def test_backward_recompute_matches_saved(M, h, f):
+    """mlp_bwd without the saved U_i / Y_i recomputes them with the forward's own
+    kernel, so every gradient equals the saved-activation run bit for bit."""
+    note(f"mlp_bwd recompute vs saved M={M} h={h} f={f}")
+    inp = mlp_inputs(M, h, f, 1, "bf16", 4000 + M, 1.0, 0.02, 1.0, full=False)
+    A_i, B_i = inp["shards"][0]
+    X, A, B, dZ = bf16_dev(inp["X"]), bf16_dev(A_i), bf16_dev(B_i), bf16_dev(inp["dZ"])
+    U, Y, Z = _alloc(M, h, f, torch.bfloat16)
+    tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
+    saved = _run_bwd(X, A, B, U, Y, dZ, M, h, f)[:3]
+    ws = torch.empty(tp.mlp_bwd_recompute_workspace(M, h, f), dtype=torch.uint8, device=DEV)
+    for U_in, Y_in in ((None, None), (U, None), (None, Y)):
+        outs = [torch.full_like(t, float("nan")) for t in saved]
+        tp.mlp_bwd(X, A, B, U_in, Y_in, dZ, *outs, ws)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dX", "dA", "dB"), outs, saved):
+            assert torch.equal(a, b), f"{name} differs (U given: {U_in is not None}, Y given: {Y_in is not None})"
+
+
+class TestPalmShape:
+    """PaLM-shaped rank shard (M=2048, h=18432, f=9216): forward with saved U,
+    backward with activation recompute; sampled outputs from the oracle."""
+
+    ROWS = np.array([0, 255, 256, 1024, 2047])
+    COLS = np.array([0, 191, 192, 5000, 9215])
+
+    @pytest.fixture(scope="class")
+    def case(self):
+        c = CONFIGS[6]
+        M, h, f = c["b"] * c["s"], c["h"], c["f"]
+        inp = mlp_inputs(M, h, f, 1, "bf16", c["seed"], c["sigma_x"], c["sigma_w"], c["sigma_dz"], full=False)
+        A_i, B_i = inp["shards"][0]
+        note("PaLM-shaped mlp_fwd + mlp_bwd with recompute")
+        X, A, B, dZ = bf16_dev(inp["X"]), bf16_dev(A_i), bf16_dev(B_i), bf16_dev(inp["dZ"])
+        U, Y, Z = _alloc(M, h, f, torch.bfloat16)
+        tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
+        ws = torch.empty(tp.mlp_bwd_recompute_workspace(M, h, f), dtype=torch.uint8, device=DEV)
+        dX = torch.empty(M, h, dtype=torch.float32, device=DEV)
+        dA = torch.empty(h, f, dtype=torch.float32, device=DEV)
+        dB = torch.empty(f, h, dtype=torch.float32, device=DEV)
+        tp.mlp_bwd(X, A, B, None, None, dZ, dX, dA, dB, ws)
+        torch.cuda.synchronize()
+        o = dict(X=bf16_bits_to_f64(inp["X"]), A=bf16_bits_to_f64(A_i), B=bf16_bits_to_f64(B_i),
+                 dZ=bf16_bits_to_f64(inp["dZ"]))
+        return o, dict(U=U, Y=Y, Z=Z, dX=dX, dA=dA, dB=dB)
+
+    def test_forward_rows(self, case):
+        o, g = case
+        r = oracle.mlp_fwd_rows(o["X"], o["A"], o["B"], self.ROWS)
+        for k in ("U", "Y", "Z"):
+            assert_bf16_close(f64_host(g[k][torch.from_numpy(self.ROWS).to(DEV)]), r[k], f"{k} rows")
+
+    def test_backward_samples(self, case):
+        o, g = case
+        s = oracle.mlp_bwd_cols(o["X"], o["A"], o["B"], o["dZ"], self.ROWS, self.COLS)
+        rows = torch.from_numpy(self.ROWS).to(DEV)
+        cols = torch.from_numpy(self.COLS).to(DEV)
+        assert_bf16_close(f64_host(g["dA"][:, cols]), s["dA_cols"], "dA columns")
+        assert_bf16_close(f64_host(g["dB"][cols, :]), s["dB_rows"], "dB rows")
+        assert_bf16_close(f64_host(g["dX"][rows, :]), s["dX_rows"], "dX rows")
+
+    def test_outputs_finite(self, case):
+        _, g = case
+        for k, t in g.items():
+            assert torch.isfinite(t.float()).all(), k

@@ -31,6 +31,9 @@ CONFIGS = {
             d_head=128, dtype="bf16", sigma_x=1.0, sigma_w=0.006, seed=1004),
     5: dict(name="vocab_parallel_embed", v=50304, N=8, h=12288, b=8, s=2048,
             dtype="bf16", sigma_w=0.02, seed=1005),
+    # PaLM-shaped rank shard (h = 18432, TP = 8, f = 4h/8), a second MLP shape.
+    6: dict(name="palm_mlp_rank_shard", b=1, s=2048, h=18432, f=9216, N=8, dtype="bf16",
+            sigma_x=1.0, sigma_w=0.005, sigma_dz=1.0, seed=1006),
 }
 
 
