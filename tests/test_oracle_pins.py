@@ -412,3 +412,72 @@ class TestEmbedding:
         inr = (ids >= 0) & (ids < v)
         np.testing.assert_array_equal(got[inr], E[ids[inr]])
         assert not np.any(got[~inr])
+
+
+# ---------------------------------------------------------------- vocab-parallel cross-entropy
+class TestVocabCrossEntropy:
+    @staticmethod
+    def _case(seed, M=6, h=5, v=24):
+        rng = np.random.default_rng(seed)
+        H = rng.standard_normal((M, h))
+        E = rng.standard_normal((v, h)) * 0.5
+        t = rng.integers(0, v, M)
+        return H, E, t
+
+    def test_zero_table_gives_log_v_per_row(self):
+        # closed form: every logit is 0, so sum(e) = v and each row's loss is log v
+        M, h, v = 7, 4, 30
+        H = np.random.default_rng(60).standard_normal((M, h))
+        r = oracle.vocab_ce_sharded(H, np.zeros((v, h)), np.arange(M) % v, 3)
+        np.testing.assert_allclose(r["loss_rows"], np.log(v), rtol=0, atol=1e-14)
+        assert abs(r["loss"] - M * np.log(v)) < 1e-12
+
+    def test_brute_force_loops(self):
+        H, E, t = self._case(61, M=4, h=3, v=9)
+        N = 3
+        r = oracle.vocab_ce_sharded(H, E, t, N)
+        for m in range(H.shape[0]):
+            S = 0.0
+            for n in range(E.shape[0]):
+                dot = 0.0
+                for k in range(H.shape[1]):
+                    dot += H[m, k] * E[n, k]
+                S += math.exp(dot)
+            lt = sum(H[m, k] * E[t[m], k] for k in range(H.shape[1]))
+            assert abs(r["loss_rows"][m] - (math.log(S) - lt)) < 1e-12
+
+    @pytest.mark.parametrize("N", [1, 2, 4, 8])
+    def test_sharded_equals_full_log_softmax(self, N):
+        # library cross-check: full-vocabulary cross-entropy through scipy's
+        # max-shifted logsumexp (a different summation route)
+        from scipy.special import logsumexp
+        H, E, t = self._case(62 + N, M=10, h=6, v=40)
+        logits = H @ E.T
+        want = logsumexp(logits, axis=1) - logits[np.arange(10), t]
+        r = oracle.vocab_ce_sharded(H, E, t, N)
+        np.testing.assert_allclose(r["loss_rows"], want, rtol=1e-12, atol=1e-12)
+        assert abs(r["loss"] - want.sum()) < 1e-10
+
+    def test_shift_invariance(self):
+        # adding one vector u to every row of E adds H u to every logit of a row,
+        # which the softmax cancels
+        H, E, t = self._case(70, M=8, h=5, v=32)
+        u = np.random.default_rng(71).standard_normal(5)
+        a = oracle.vocab_ce_sharded(H, E, t, 4)
+        b = oracle.vocab_ce_sharded(H, E + u, t, 4)
+        np.testing.assert_allclose(a["loss_rows"], b["loss_rows"], rtol=1e-10, atol=1e-10)
+
+    def test_exactly_one_rank_holds_each_target(self):
+        H, E, t = self._case(72, M=12, h=4, v=48)
+        N, v = 4, 48
+        parts = [oracle.vocab_ce_partials(H, E[i * v // N:(i + 1) * v // N], t, i * v // N, (i + 1) * v // N)
+                 for i in range(N)]
+        logits = H @ E.T
+        for m in range(12):
+            holders = [i for i in range(N) if i * v // N <= t[m] < (i + 1) * v // N]
+            assert len(holders) == 1
+            for i, p in enumerate(parts):
+                if i in holders:
+                    assert abs(p["tlogit"][m] - logits[m, t[m]]) < 1e-12
+                else:
+                    assert p["tlogit"][m] == 0.0
