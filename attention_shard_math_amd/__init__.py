@@ -20,5 +20,8 @@ from ._lib import (  # noqa: F401
     attn_fwd,
     attn_fwd_workspace,
     vocab_embed,
+    vocab_ce_workspace,
+    vocab_ce_partials,
+    vocab_ce_loss,
     shard_sum,
 )

@@ -30,6 +30,8 @@ _SIGS = {
     "tp_attn_fwd": [_i64, _i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_vocab_embed": [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp],
     "tp_shard_sum": [C.c_int, C.POINTER(_vp), C.c_int, _i64, _vp, _vp],
+    "tp_vocab_ce_partials": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "tp_vocab_ce_loss": [_i64, C.POINTER(_vp), C.POINTER(_vp), C.c_int, _vp, _vp, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(lib, _name)
@@ -39,6 +41,8 @@ lib.tp_mlp_bwd_workspace.argtypes = [_i64, _i64, _i64]
 lib.tp_mlp_bwd_workspace.restype = _sz
 lib.tp_mlp_bwd_recompute_workspace.argtypes = [_i64, _i64, _i64]
 lib.tp_mlp_bwd_recompute_workspace.restype = _sz
+lib.tp_vocab_ce_workspace.argtypes = [_i64, _i64, _i64]
+lib.tp_vocab_ce_workspace.restype = _sz
 lib.tp_attn_fwd_workspace.argtypes = [_i64, _i64, _i64, _i64]
 lib.tp_attn_fwd_workspace.restype = _sz
 lib.tp_status_string.argtypes = [C.c_int]
@@ -165,6 +169,34 @@ def vocab_embed(ids, E_i, lo, hi, out, stream=None):
     h = E_i.shape[1]
     _check(lib.tp_vocab_embed(_ptr(ids, dtype=torch.int32, name="ids"), n, _ptr(E_i, (hi - lo, h), None, "E_i"),
                               lo, hi, h, _ptr(out, (n, h), E_i.dtype, "out"), _stream(stream)), "tp_vocab_embed")
+
+
+def vocab_ce_workspace(M, lo, hi):
+    return int(lib.tp_vocab_ce_workspace(M, lo, hi))
+
+
+def vocab_ce_partials(H, E_i, targets, lo, hi, sumexp_i, tlogit_i, ws, stream=None):
+    M, h = H.shape
+    V = hi - lo
+    _check(lib.tp_vocab_ce_partials(M, h, lo, hi, _ptr(H, (M, h), torch.bfloat16, "H"),
+                                    _ptr(E_i, (V, h), torch.bfloat16, "E_i"),
+                                    _ptr(targets, (M,), torch.int32, "targets"),
+                                    _ptr(sumexp_i, (M,), torch.float32, "sumexp_i"),
+                                    _ptr(tlogit_i, (M,), torch.float32, "tlogit_i"),
+                                    _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(),
+                                    _stream(stream)), "tp_vocab_ce_partials")
+
+
+def vocab_ce_loss(sumexp_parts, tlogit_parts, loss_rows, loss_sum, stream=None):
+    n = len(sumexp_parts)
+    if len(tlogit_parts) != n:
+        raise ValueError("sumexp_parts and tlogit_parts differ in length")
+    M = loss_rows.numel()
+    sa = (_vp * max(n, 1))(*[_ptr(p, (M,), torch.float32, f"sumexp_parts[{i}]") for i, p in enumerate(sumexp_parts)])
+    ta = (_vp * max(n, 1))(*[_ptr(p, (M,), torch.float32, f"tlogit_parts[{i}]") for i, p in enumerate(tlogit_parts)])
+    _check(lib.tp_vocab_ce_loss(M, sa, ta, n, _ptr(loss_rows, (M,), torch.float32, "loss_rows"),
+                                _ptr(loss_sum, (1,), torch.float32, "loss_sum"), _stream(stream)),
+           "tp_vocab_ce_loss")
 
 
 def shard_sum(partials, out, stream=None):

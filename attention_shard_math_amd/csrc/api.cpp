@@ -10,6 +10,7 @@
 #include <string>
 
 #include "attn.hpp"
+#include "vocab_ce.hpp"
 #include "bandwidth.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
@@ -298,6 +299,60 @@ TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
     TRY(hip_status(tps::gemm_bf16(g, true, false, tps::EPI_F32, st), fn));
   }
   return ok();
+}
+
+TP_API size_t tp_vocab_ce_workspace(int64_t M, int64_t lo, int64_t hi) {
+  if (M < 0 || lo < 0 || hi <= lo) return 0;
+  return round256((size_t)M * (size_t)(hi - lo) * 4);
+}
+
+TP_API tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t hi, const void* H, const void* E_i,
+                                      const int32_t* targets, float* sumexp_i, float* tlogit_i, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  const char* fn = "tp_vocab_ce_partials";
+  if (lo < 0 || lo >= hi)
+    return fail(TP_ERR_INVALID_ARG, "%s: need 0 <= lo < hi (got lo=%lld hi=%lld)", fn, (long long)lo, (long long)hi);
+  TRY(check_dims(fn, M, h, hi - lo));
+  if (M == 0) return ok();
+  TRY(check_ptr(fn, "H", H));
+  TRY(check_ptr(fn, "E_i", E_i));
+  if (!targets) return fail(TP_ERR_INVALID_ARG, "%s: targets is NULL", fn);
+  TRY(check_ptr(fn, "sumexp_i", sumexp_i));
+  TRY(check_ptr(fn, "tlogit_i", tlogit_i));
+  const size_t need = tp_vocab_ce_workspace(M, lo, hi);
+  if (!ws || ws_bytes < need)
+    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
+                ws ? "" : " (NULL)");
+  TRY(check_ptr(fn, "ws", ws));
+  hipStream_t st = as_stream(stream);
+  const int64_t V = hi - lo;
+  float* logits = static_cast<float*>(ws);
+  // logits_i = H E_i^T: A = H [M,h] (K-contig), B(k,n) = E_i[n, k] (K-contig).
+  tps::GemmArgs g = make_args(H, h, E_i, h, M, V, h, logits, V);
+  TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_F32, st), fn));
+  return hip_status(tps::ce_rows(logits, M, (int)V, targets, lo, sumexp_i, tlogit_i, st), fn);
+}
+
+TP_API tp_status tp_vocab_ce_loss(int64_t M, const float* const* sumexp_parts, const float* const* tlogit_parts,
+                                  int n_parts, float* loss_rows, float* loss_sum, void* stream) {
+  const char* fn = "tp_vocab_ce_loss";
+  if (M < 0) return fail(TP_ERR_INVALID_ARG, "%s: M < 0", fn);
+  if (M > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "%s: M exceeds 2^31-1", fn);
+  if (n_parts < 1 || n_parts > tps::kCeMaxParts)
+    return fail(TP_ERR_INVALID_ARG, "%s: n_parts must be in [1, %d] (got %d)", fn, tps::kCeMaxParts, n_parts);
+  if (!sumexp_parts || !tlogit_parts) return fail(TP_ERR_INVALID_ARG, "%s: part arrays are NULL", fn);
+  TRY(check_ptr(fn, "loss_sum", loss_sum));
+  tps::CeParts p{};
+  if (M > 0) {
+    TRY(check_ptr(fn, "loss_rows", loss_rows));
+    for (int i = 0; i < n_parts; ++i) {
+      TRY(check_ptr(fn, "sumexp_parts[i]", sumexp_parts[i]));
+      TRY(check_ptr(fn, "tlogit_parts[i]", tlogit_parts[i]));
+      p.s[i] = sumexp_parts[i];
+      p.t[i] = tlogit_parts[i];
+    }
+  }
+  return hip_status(tps::ce_loss(p, n_parts, M, loss_rows, loss_sum, as_stream(stream)), fn);
 }
 
 TP_API tp_status tp_vocab_embed(const int32_t* ids, int64_t n_tokens, const void* E_i, int64_t lo, int64_t hi,

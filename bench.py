@@ -49,6 +49,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
+    p.add_argument("--no-next", action="store_true",
+                   help="skip the extra rows timed after the step (PaLM-shaped MLP with recompute)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed steps, run a plain 256 MiB device-to-device copy three times, "
                         "the calibration kernel for HBM byte counters")
@@ -103,6 +105,83 @@ def traffic_from_profiles(key: str):
         return round(rec["kernels"][key]["hbm_bytes_per_launch"])
     except Exception:
         return None
+
+
+def next_rows(tp, torch, dev, randn, reps=5):
+    """Rows beyond the step, timed on their own after it: the PaLM-shaped MLP shard
+    (M=2048, h=18432, f=9216), forward with saved U, backward with activation
+    recompute (U, Y formed again from X and A_i inside mlp_bwd); and the
+    vocabulary-parallel output layer + cross-entropy of one rank."""
+    Mp, Hp, Fp = 2048, 18432, 9216
+    X = randn((Mp, Hp), 1.0, 40)
+    A = randn((Hp, Fp), 0.005, 41)
+    B = randn((Fp, Hp), 0.005, 42)
+    dZ = randn((Mp, Hp), 1.0, 43)
+    U = torch.empty(Mp, Fp, dtype=torch.bfloat16, device=dev)
+    Y = torch.empty_like(U)
+    Z = torch.empty(Mp, Hp, dtype=torch.float32, device=dev)
+    dX = torch.empty(Mp, Hp, dtype=torch.float32, device=dev)
+    dA = torch.empty(Hp, Fp, dtype=torch.float32, device=dev)
+    dB = torch.empty(Fp, Hp, dtype=torch.float32, device=dev)
+    ws = torch.empty(tp.mlp_bwd_recompute_workspace(Mp, Hp, Fp), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    fwd = lambda: tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
+    bwd = lambda: tp.mlp_bwd(X, A, B, None, None, dZ, dX, dA, dB, ws)
+    out = {}
+    for name, fn, n_gemm in (("palm_mlp_fwd", fwd, 2), ("palm_mlp_bwd_recompute", bwd, 5)):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = n_gemm * gemm_flops(Mp, Fp, Hp) / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "gemms": n_gemm, "tflops": round(tf, 1),
+                     "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del X, A, B, dZ, U, Y, Z, dX, dA, dB, ws
+    torch.cuda.empty_cache()
+
+    # Vocabulary-parallel output layer + cross-entropy: one rank's slice of the
+    # 50304-entry vocabulary (6288 rows of E), 2048 tokens, h = 12288; then the
+    # rank-sum/loss step over 8 slices' partial sums.
+    Mv, Hv, Vs, Nv = 2048, 12288, 50304 // 8, 8
+    Hh = randn((Mv, Hv), 1.0, 50)
+    E = randn((Vs, Hv), 0.02, 51)
+    tg = torch.randint(0, 50304, (Mv,), dtype=torch.int32, generator=torch.Generator().manual_seed(52)).to(dev)
+    sums = [torch.empty(Mv, dtype=torch.float32, device=dev) for _ in range(Nv)]
+    tls = [torch.empty(Mv, dtype=torch.float32, device=dev) for _ in range(Nv)]
+    ws = torch.empty(tp.vocab_ce_workspace(Mv, 0, Vs), dtype=torch.uint8, device=dev)
+    rows = torch.empty(Mv, dtype=torch.float32, device=dev)
+    tot = torch.empty(1, dtype=torch.float32, device=dev)
+    part = lambda: tp.vocab_ce_partials(Hh, E, tg, 0, Vs, sums[0], tls[0], ws)
+    part()
+    for i in range(1, Nv):
+        sums[i].copy_(sums[0])
+        tls[i].zero_()
+    loss = lambda: tp.vocab_ce_loss(sums, tls, rows, tot)
+    for name, fn in (("vocab_ce_partials", part), ("vocab_ce_loss", loss)):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        rec = {"ms": round(ms, 4)}
+        if name == "vocab_ce_partials":
+            tf = gemm_flops(Mv, Vs, Hv) / (ms * 1e-3) / 1e12
+            rec.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
+        out[name] = rec
+    del Hh, E, tg, sums, tls, ws, rows, tot
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -244,6 +323,8 @@ def main():
                      "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
         "breakdown": breakdown,
     }
+    if not args.no_next:
+        rec["next_rows"] = next_rows(tp, torch, dev, randn)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
     if args.copy_probe:

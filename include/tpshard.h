@@ -157,6 +157,33 @@ size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_
 tp_status tp_vocab_embed(const int32_t* ids, int64_t n_tokens, const void* E_i,
                          int64_t lo, int64_t hi, int64_t h, void* out, void* stream);
 
+/* Vocabulary-parallel output layer + cross-entropy, one rank's part
+ * [m.youleyou.com/wenzhang/3143730, 四、Embedding层 §4.2 (the output layer maps
+ *  back to the vocabulary with the row-split word embedding) and 五、Cross-Entropy层
+ *  (per-rank row sums of e = exp(logit), all-reduced into the softmax
+ *  denominator, then each row's cross-entropy and the scalar sum)]:
+ *   logits_i = H E_i^T                       -> float32 [M, hi-lo] in the workspace
+ *   sumexp_i[m] = sum_n exp(logits_i[m, n])   -> float32 [M]
+ *   tlogit_i[m] = logits_i[m, t[m] - lo] if lo <= t[m] < hi, else 0 -> float32 [M]
+ *   H [M,h] and E_i [hi-lo, h]: bf16; targets [M] int32 (device).
+ *   Requires 0 <= lo < hi, h and hi-lo multiples of 8. e is exp(logit) as the
+ *   page states it (no maximum subtracted): logits above ~88 overflow float32.
+ *   ws: at least tp_vocab_ce_workspace(M, lo, hi) bytes. */
+tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t hi, const void* H,
+                               const void* E_i, const int32_t* targets, float* sumexp_i,
+                               float* tlogit_i, void* ws, size_t ws_bytes, void* stream);
+size_t tp_vocab_ce_workspace(int64_t M, int64_t lo, int64_t hi);
+
+/* The two all-reduce stand-ins of the vocabulary-parallel loss on one GPU, and
+ * the loss itself [same page, 五、Cross-Entropy层]:
+ *   S[m] = sum_i sumexp_parts[i][m] (rank order), T[m] = sum_i tlogit_parts[i][m],
+ *   loss_rows[m] = log S[m] - T[m], *loss_sum = sum_m loss_rows[m] (fixed order).
+ *   sumexp_parts, tlogit_parts: HOST arrays of n_parts device pointers,
+ *   1 <= n_parts <= 16. loss_rows [M] and loss_sum [1]: float32 (device). */
+tp_status tp_vocab_ce_loss(int64_t M, const float* const* sumexp_parts,
+                           const float* const* tlogit_parts, int n_parts, float* loss_rows,
+                           float* loss_sum, void* stream);
+
 /* Shard-sum standing in for the all-reduce of N partials on one GPU:
  *   out = ((P_0 + P_1) + P_2) + ... + P_{N-1}, elementwise, in float32, in this
  *   fixed order (so the result is reproducible bit for bit).

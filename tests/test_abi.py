@@ -98,6 +98,37 @@ class TestValidation:
         assert e(None, 4, P, 0, 10, 8, P, None) == INVALID
         assert e(P, 4, P, 0, 10, 8, MIS, None) == UNSUPPORTED
 
+    def test_vocab_ce(self):
+        M, h, lo, hi = 16, 64, 40, 104
+        need = lib.tp_vocab_ce_workspace(M, lo, hi)
+        assert need == M * (hi - lo) * 4 and need % 256 == 0
+        assert lib.tp_vocab_ce_workspace(3, 0, 8) == 256
+        assert lib.tp_vocab_ce_workspace(3, 8, 8) == 0
+        c = lib.tp_vocab_ce_partials
+        assert c(M, h, 10, 10, P, P, P, P, P, P, need, None) == INVALID          # lo == hi
+        assert c(M, h, -8, 8, P, P, P, P, P, P, need, None) == INVALID          # lo < 0
+        assert c(-1, h, lo, hi, P, P, P, P, P, P, need, None) == INVALID
+        assert c(M, h, 0, 12, P, P, P, P, P, P, need, None) == UNSUPPORTED      # slice % 8
+        assert c(M, 20, lo, hi, P, P, P, P, P, P, need, None) == UNSUPPORTED    # h % 8
+        assert c(M, h, lo, hi, P, P, None, P, P, P, need, None) == INVALID      # targets NULL
+        assert c(M, h, lo, hi, None, P, P, P, P, P, need, None) == INVALID
+        assert c(M, h, lo, hi, P, MIS, P, P, P, P, need, None) == UNSUPPORTED
+        assert c(M, h, lo, hi, P, P, P, P, P, P, need - 1, None) == WORKSPACE
+        assert c(M, h, lo, hi, P, P, P, P, P, None, need, None) == WORKSPACE
+        assert "workspace" in _err()
+        assert c(0, h, lo, hi, None, None, None, None, None, None, 0, None) == OK  # empty
+        arr = (C.c_void_p * 17)(*([P] * 17))
+        loss = lib.tp_vocab_ce_loss
+        assert loss(M, arr, arr, 0, P, P, None) == INVALID
+        assert loss(M, arr, arr, 17, P, P, None) == INVALID
+        assert loss(-1, arr, arr, 2, P, P, None) == INVALID
+        assert loss(M, None, arr, 2, P, P, None) == INVALID
+        assert loss(M, arr, arr, 2, P, None, None) == INVALID                 # loss_sum NULL
+        assert loss(M, arr, arr, 2, None, P, None) == INVALID                 # loss_rows NULL
+        bad = (C.c_void_p * 2)(P, None)
+        assert loss(M, arr, bad, 2, P, P, None) == INVALID
+        assert "tlogit_parts" in _err()
+
     def test_shard_sum(self):
         arr = (C.c_void_p * 17)(*([P] * 17))
         s = lib.tp_shard_sum

@@ -15,6 +15,7 @@ from .gen import (  # noqa: F401
     mlp_inputs,
     attn_inputs,
     embed_inputs,
+    ce_inputs,
     shard_sum_inputs,
     shard_cols,
     shard_rows,

@@ -34,6 +34,10 @@ CONFIGS = {
     # PaLM-shaped rank shard (h = 18432, TP = 8, f = 4h/8), a second MLP shape.
     6: dict(name="palm_mlp_rank_shard", b=1, s=2048, h=18432, f=9216, N=8, dtype="bf16",
             sigma_x=1.0, sigma_w=0.005, sigma_dz=1.0, seed=1006),
+    # Vocabulary-parallel output layer + cross-entropy over the GPT-3 vocabulary
+    # (padded to 50304 = 8 * 6288), one sequence of 2048 tokens.
+    7: dict(name="vocab_parallel_ce", v=50304, N=8, h=12288, b=1, s=2048, dtype="bf16",
+            sigma_h=1.0, sigma_w=0.02, seed=1007),
 }
 
 
@@ -134,6 +138,21 @@ def embed_inputs(v: int, h: int, n_tokens: int, seed: int, sigma_w: float = 0.02
     E[E == 0x8000] = 0
     ids = rng.integers(0, v, size=n_tokens, dtype=np.int32)
     return dict(E=E, ids=ids)
+
+
+def ce_inputs(M: int, h: int, v: int, seed: int, sigma_h: float = 1.0, sigma_w: float = 0.02,
+              chunk_rows: int = 4096):
+    """Output-layer + cross-entropy workload: final hidden rows H [M, h] (bf16
+    bits), then the full word-embedding table E [v, h] (bf16 bits, drawn in row
+    chunks like ``embed_inputs``), then target ids int32 uniform in [0, v)."""
+    rng = np.random.default_rng(seed)
+    H = bf16_bits(draw_normal_f32(rng, (M, h), sigma_h))
+    E = np.empty((v, h), np.uint16)
+    for r0 in range(0, v, chunk_rows):
+        r1 = min(v, r0 + chunk_rows)
+        E[r0:r1] = bf16_bits(draw_normal_f32(rng, (r1 - r0, h), sigma_w))
+    targets = rng.integers(0, v, size=M, dtype=np.int32)
+    return dict(H=H, E=E, targets=targets)
 
 
 def shard_sum_inputs(n_partials: int, numel: int, seed: int, sigma: float = 1.0,
