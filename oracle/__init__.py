@@ -18,12 +18,17 @@ Pages cited (by title and section as printed):
     (row and column splits with the conjugate f/g operators, forward and
     backward), 二、MLP层 §2.1, 三、Self-Attention层 §3.1, 四、Embedding层 §4.1
     (vocabulary-parallel input embedding with zeroed misses), §4.2 and
-    五、Cross-Entropy层 (vocabulary-parallel output layer and loss).
+    五、Cross-Entropy层 (vocabulary-parallel output layer and loss), 二、§2.2
+    (an all-reduce is a reduce-scatter plus an all-gather).
+  * www.discosf.com/news/5875844 — 2.3 序列并行与激活重计算 (sequence-parallel
+    LayerNorm and Dropout; activation recompute).
   * "Megatron-LM 介绍" (apxml.com) — 核心贡献 item 1 (ColumnParallelLinear).
 
 Parity status per function (what pins it, see tests/test_oracle_pins.py):
   bf16 rounding, GeLU/GeLU', MLP forward/backward, shard-sum, attention, the
-  embedding gather and the vocabulary-parallel cross-entropy are each pinned by closed forms, brute force on tiny inputs,
+  embedding gather, the vocabulary-parallel cross-entropy and the
+  sequence-parallel LayerNorm / reduce-scatter / all-gather / dropout are each
+  pinned by closed forms, brute force on tiny inputs,
   finite differences, sharding invariants or the pages' worked example. No
   function is "parity unpinned".
 """
@@ -36,3 +41,4 @@ from .shard_sum import shard_sum_f64, shard_sum_f32_ordered, shard_sum_bf16_orde
 from .attention import attn_shard, attn_core, mha_full, attn_shard_rows  # noqa: F401
 from .embedding import vocab_embed_shard  # noqa: F401
 from .vocab_ce import vocab_ce_partials, vocab_ce_combine, vocab_ce_sharded  # noqa: F401
+from .seqpar import layernorm, all_gather, reduce_scatter, dropout_residual, sp_mlp_block, tp_mlp_block  # noqa: F401,E501

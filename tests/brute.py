@@ -32,3 +32,15 @@ def attention_head(q, k, v, causal):
         z = sum(e)
         out.append([sum(e[u] * v[u][c] for u in range(last)) / z for c in range(d)])
     return out
+
+
+def layernorm(X, gamma, beta, eps):
+    """Row by row: mean, biased variance, normalise, scale and shift."""
+    out = []
+    for row in X:
+        n = len(row)
+        mu = sum(row) / n
+        var = sum((x - mu) * (x - mu) for x in row) / n
+        inv = 1.0 / math.sqrt(var + eps)
+        out.append([(x - mu) * inv * g + b for x, g, b in zip(row, gamma, beta)])
+    return out

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 from oracle import bf16 as ob
+from oracle import seqpar
 from tests import brute
 from workloads import CONFIGS, mlp_inputs, shard_cols, shard_rows
 
@@ -481,3 +482,78 @@ class TestVocabCrossEntropy:
                     assert abs(p["tlogit"][m] - logits[m, t[m]]) < 1e-12
                 else:
                     assert p["tlogit"][m] == 0.0
+
+
+class TestSequenceParallel:
+    """Sequence-parallel MLP block [www.discosf.com/news/5875844, 2.3] with the
+    all-reduce split into reduce-scatter + all-gather [m.youleyou.com/wenzhang/
+    3143730, 二、§2.2]."""
+
+    def _ln_inputs(self, s, h, seed):
+        rng = np.random.default_rng(seed)
+        R = rng.standard_normal((s, h)) * 3.0 + 0.5
+        gamma = 1.0 + 0.1 * rng.standard_normal(h)
+        beta = 0.1 * rng.standard_normal(h)
+        return R, gamma, beta
+
+    def test_layernorm_brute_force(self):
+        R, g, b = self._ln_inputs(5, 7, 11)
+        got = seqpar.layernorm(R, g, b, 1e-5)
+        want = np.array(brute.layernorm(R.tolist(), g.tolist(), b.tolist(), 1e-5))
+        np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+    def test_layernorm_torch(self):
+        R, g, b = self._ln_inputs(16, 96, 12)
+        want = torch.nn.functional.layer_norm(torch.from_numpy(R), (96,), torch.from_numpy(g),
+                                              torch.from_numpy(b), eps=1e-5).numpy()
+        np.testing.assert_allclose(seqpar.layernorm(R, g, b), want, rtol=1e-12, atol=1e-12)
+
+    def test_layernorm_moments_and_affine_invariance(self):
+        R, _, _ = self._ln_inputs(8, 64, 13)
+        ones, zeros = np.ones(64), np.zeros(64)
+        y = seqpar.layernorm(R, ones, zeros, eps=0.0)
+        np.testing.assert_allclose(y.mean(axis=1), 0.0, atol=1e-13)
+        np.testing.assert_allclose((y ** 2).mean(axis=1), 1.0, rtol=1e-12)
+        # LN(a x + c) with eps a^2 equals LN(x) with eps
+        a, c = 7.5, -3.25
+        np.testing.assert_allclose(seqpar.layernorm(a * R + c, ones, zeros, eps=1e-5 * a * a),
+                                   seqpar.layernorm(R, ones, zeros, eps=1e-5), rtol=1e-11, atol=1e-12)
+
+    def test_gather_and_scatter_are_the_halves_of_an_all_reduce(self):
+        rng = np.random.default_rng(14)
+        N, s, h = 4, 12, 5
+        parts = [rng.standard_normal((s, h)) for _ in range(N)]
+        full = oracle.shard_sum_f64(parts)
+        scattered = [seqpar.reduce_scatter(parts, N, i) for i in range(N)]
+        np.testing.assert_array_equal(seqpar.all_gather(scattered), full)
+        for i in range(N):
+            np.testing.assert_array_equal(scattered[i], full[3 * i:3 * (i + 1)])
+
+    def test_dropout_residual(self):
+        rng = np.random.default_rng(15)
+        R, O = rng.standard_normal((4, 6)), rng.standard_normal((4, 6))
+        np.testing.assert_array_equal(seqpar.dropout_residual(R, O), R + O)
+        np.testing.assert_array_equal(seqpar.dropout_residual(R, O, np.zeros((4, 6), np.uint8), 0.9), R)
+        np.testing.assert_allclose(seqpar.dropout_residual(R, O, np.ones((4, 6), np.uint8), 0.5), R + 2 * O)
+        keep = (rng.random((4, 6)) < 0.5).astype(np.uint8)
+        want = [[R[r][c] + (O[r][c] / 0.8 if keep[r][c] else 0.0) for c in range(6)] for r in range(4)]
+        np.testing.assert_allclose(seqpar.dropout_residual(R, O, keep, 0.8), want, rtol=1e-15)
+
+    @pytest.mark.parametrize("N", [1, 2, 4])
+    def test_sequence_parallel_equals_tensor_parallel(self, N):
+        s, h, f_full = 16, 32, 128
+        R, g, b = self._ln_inputs(s, h, 16 + N)
+        inp = mlp_inputs(s, h, f_full, N, "f32", 17, 1.0, 0.05, None)
+        shards = [(A.astype(np.float64), B.astype(np.float64)) for A, B in inp["shards"]]
+        keep = (np.random.default_rng(18).random((s, h)) < 0.9).astype(np.uint8)
+        for matched in (False, True):
+            sp = seqpar.sp_mlp_block(R, g, b, shards, keep, 0.9, matched=matched)
+            tp_ = seqpar.tp_mlp_block(R, g, b, shards, keep, 0.9, matched=matched)
+            np.testing.assert_array_equal(sp["X"], tp_["X"])
+            np.testing.assert_allclose(sp["R_out"], tp_["R_out"], rtol=1e-13, atol=1e-13)
+        # unsharded: LayerNorm, GeLU(XA)B, dropout, residual written out directly
+        X = seqpar.layernorm(R, g, b)
+        Z = np.array(brute.mlp(X.tolist(), inp["A"].astype(np.float64).tolist(), inp["B"].astype(np.float64).tolist()))
+        want = R + np.where(keep != 0, Z / 0.9, 0.0)
+        np.testing.assert_allclose(seqpar.sp_mlp_block(R, g, b, shards, keep, 0.9, matched=False)["R_out"], want,
+                                   rtol=1e-11, atol=1e-11)
