@@ -24,4 +24,7 @@ from ._lib import (  # noqa: F401
     vocab_ce_partials,
     vocab_ce_loss,
     shard_sum,
+    layernorm,
+    sp_all_gather,
+    sp_reduce_scatter,
 )

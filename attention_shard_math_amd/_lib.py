@@ -32,6 +32,9 @@ _SIGS = {
     "tp_shard_sum": [C.c_int, C.POINTER(_vp), C.c_int, _i64, _vp, _vp],
     "tp_vocab_ce_partials": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_vocab_ce_loss": [_i64, C.POINTER(_vp), C.POINTER(_vp), C.c_int, _vp, _vp, _vp],
+    "tp_layernorm": [_i64, _i64, _vp, _vp, _vp, C.c_float, _vp, _vp],
+    "tp_sp_all_gather": [C.c_int, C.POINTER(_vp), _i64, _i64, _vp, _vp],
+    "tp_sp_reduce_scatter": [C.c_int, C.POINTER(_vp), _i64, _i64, C.c_int, _vp, _vp, C.c_float, _vp, _vp],
 }
 for _name, _args in _SIGS.items():
     _f = getattr(lib, _name)
@@ -197,6 +200,34 @@ def vocab_ce_loss(sumexp_parts, tlogit_parts, loss_rows, loss_sum, stream=None):
     _check(lib.tp_vocab_ce_loss(M, sa, ta, n, _ptr(loss_rows, (M,), torch.float32, "loss_rows"),
                                 _ptr(loss_sum, (1,), torch.float32, "loss_sum"), _stream(stream)),
            "tp_vocab_ce_loss")
+
+
+def layernorm(X, gamma, beta, Y, eps=1e-5, stream=None):
+    """Y (bf16) = LayerNorm(X) row by row; X float32 [rows, h]."""
+    rows, h = X.shape
+    f32 = torch.float32
+    _check(lib.tp_layernorm(rows, h, _ptr(X, (rows, h), f32, "X"), _ptr(gamma, (h,), f32, "gamma"),
+                            _ptr(beta, (h,), f32, "beta"), eps, _ptr(Y, (rows, h), torch.bfloat16, "Y"),
+                            _stream(stream)), "tp_layernorm")
+
+
+def sp_all_gather(slices, out, stream=None):
+    n = len(slices)
+    rows, h = slices[0].shape
+    arr = (_vp * max(n, 1))(*[_ptr(x, (rows, h), torch.bfloat16, f"slices[{i}]") for i, x in enumerate(slices)])
+    _check(lib.tp_sp_all_gather(n, arr, rows, h, _ptr(out, (n * rows, h), torch.bfloat16, "out"), _stream(stream)),
+           "tp_sp_all_gather")
+
+
+def sp_reduce_scatter(partials, rank, residual, out, keep=None, keep_prob=1.0, stream=None):
+    n = len(partials)
+    s, h = partials[0].shape
+    f32 = torch.float32
+    arr = (_vp * max(n, 1))(*[_ptr(p, (s, h), f32, f"partials[{i}]") for i, p in enumerate(partials)])
+    rows = s // n
+    _check(lib.tp_sp_reduce_scatter(n, arr, s, h, rank, _ptr(residual, (rows, h), f32, "residual"),
+                                    _ptr(keep, (rows, h), torch.uint8, "keep"), keep_prob,
+                                    _ptr(out, (rows, h), f32, "out"), _stream(stream)), "tp_sp_reduce_scatter")
 
 
 def shard_sum(partials, out, stream=None):

@@ -11,6 +11,7 @@
 
 #include "attn.hpp"
 #include "vocab_ce.hpp"
+#include "seqpar.hpp"
 #include "bandwidth.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
@@ -371,6 +372,83 @@ TP_API tp_status tp_vocab_embed(const int32_t* ids, int64_t n_tokens, const void
   return hip_status(tps::vocab_gather(ids, n_tokens, static_cast<const uint16_t*>(E_i), lo, hi, h,
                                       static_cast<uint16_t*>(out), as_stream(stream)),
                     fn);
+}
+
+// ---- sequence parallelism
+
+static tp_status check_sp_h(const char* fn, int64_t h) {
+  if (h <= 0) return fail(TP_ERR_INVALID_ARG, "%s: h must be > 0 (got %lld)", fn, (long long)h);
+  if (h % 8) return fail(TP_ERR_UNSUPPORTED, "%s: h must be a multiple of 8 (got %lld)", fn, (long long)h);
+  return TP_OK;
+}
+
+TP_API tp_status tp_layernorm(int64_t rows, int64_t h, const float* X, const float* gamma, const float* beta,
+                              float eps, void* Y, void* stream) {
+  const char* fn = "tp_layernorm";
+  if (rows < 0) return fail(TP_ERR_INVALID_ARG, "%s: rows < 0", fn);
+  TRY(check_sp_h(fn, h));
+  if (h > tps::kLnMaxH)
+    return fail(TP_ERR_UNSUPPORTED, "%s: h above %lld is not supported", fn, (long long)tps::kLnMaxH);
+  if (!(eps >= 0.f)) return fail(TP_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+  if (rows > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "%s: rows exceeds 2^31-1", fn);
+  if (rows == 0) return ok();
+  TRY(check_ptr(fn, "X", X));
+  TRY(check_ptr(fn, "gamma", gamma));
+  TRY(check_ptr(fn, "beta", beta));
+  TRY(check_ptr(fn, "Y", Y));
+  return hip_status(tps::layernorm_rows(X, rows, h, gamma, beta, eps, static_cast<uint16_t*>(Y), as_stream(stream)),
+                    fn);
+}
+
+TP_API tp_status tp_sp_reduce_scatter(int n_parts, const float* const* partials, int64_t s, int64_t h, int rank,
+                                      const float* residual, const uint8_t* keep, float keep_prob, float* out,
+                                      void* stream) {
+  const char* fn = "tp_sp_reduce_scatter";
+  if (n_parts < 1 || n_parts > tps::kSpMaxParts)
+    return fail(TP_ERR_INVALID_ARG, "%s: n_parts must be in [1, %d] (got %d)", fn, tps::kSpMaxParts, n_parts);
+  if (s < 0 || s % n_parts)
+    return fail(TP_ERR_INVALID_ARG, "%s: s must be >= 0 and a multiple of n_parts (got s=%lld)", fn, (long long)s);
+  TRY(check_sp_h(fn, h));
+  if (rank < 0 || rank >= n_parts) return fail(TP_ERR_INVALID_ARG, "%s: rank %d outside [0, %d)", fn, rank, n_parts);
+  if (keep && !(keep_prob > 0.f && keep_prob <= 1.f))
+    return fail(TP_ERR_INVALID_ARG, "%s: keep_prob must be in (0, 1]", fn);
+  if (keep && (reinterpret_cast<uintptr_t>(keep) & 3u))
+    return fail(TP_ERR_UNSUPPORTED, "%s: keep is not 4-byte aligned", fn);
+  const int64_t rows = s / n_parts;
+  if (rows * h == 0) return ok();
+  if (!partials) return fail(TP_ERR_INVALID_ARG, "%s: partials is NULL", fn);
+  tps::SpParts p{};
+  for (int i = 0; i < n_parts; ++i) {
+    char name[32];
+    snprintf(name, sizeof name, "partials[%d]", i);
+    TRY(check_ptr(fn, name, partials[i]));
+    p.p[i] = partials[i];
+  }
+  TRY(check_ptr(fn, "residual", residual));
+  TRY(check_ptr(fn, "out", out));
+  return hip_status(tps::sp_reduce_scatter(p, n_parts, (int64_t)rank * rows, rows, h, residual, keep, keep_prob, out,
+                                           as_stream(stream)),
+                    fn);
+}
+
+TP_API tp_status tp_sp_all_gather(int n_parts, const void* const* slices, int64_t rows, int64_t h, void* out,
+                                  void* stream) {
+  const char* fn = "tp_sp_all_gather";
+  if (n_parts < 1 || n_parts > tps::kSpMaxParts)
+    return fail(TP_ERR_INVALID_ARG, "%s: n_parts must be in [1, %d] (got %d)", fn, tps::kSpMaxParts, n_parts);
+  if (rows < 0) return fail(TP_ERR_INVALID_ARG, "%s: rows < 0", fn);
+  TRY(check_sp_h(fn, h));
+  if (rows == 0) return ok();
+  if (!slices) return fail(TP_ERR_INVALID_ARG, "%s: slices is NULL", fn);
+  tps::SpParts p{};
+  for (int i = 0; i < n_parts; ++i) {
+    char name[32];
+    snprintf(name, sizeof name, "slices[%d]", i);
+    TRY(check_ptr(fn, name, slices[i]));
+    p.p[i] = slices[i];
+  }
+  TRY(check_ptr(fn, "out", out));
+  return hip_status(tps::sp_all_gather(p, n_parts, rows, h, static_cast<uint16_t*>(out), as_stream(stream)), fn);
 }
 
 TP_API tp_status tp_shard_sum(tp_dtype dt, const void* const* partials, int n_partials, int64_t numel, void* out,

@@ -1,0 +1,184 @@
+// Sequence-parallel kernels around the tensor-parallel MLP (gfx950).
+//
+// With sequence parallelism the light row-wise operators run on one rank's
+// contiguous slice of the sequence, and the MLP's all-reduce is split into its
+// two halves: an all-gather of the LayerNorm output before the column GEMM and
+// a reduce-scatter of the fp32 partials after the row GEMM. On one GPU the two
+// collectives are stand-ins that move the same bytes:
+//  * layernorm_rows — one 256-thread workgroup per row. The row stays in
+//    registers (up to 32 float4 per thread), so HBM sees one read of X and one
+//    bf16 write of Y; mean, then the biased variance from the held values
+//    (two-pass, no cancellation), each reduced with a fixed butterfly per wave
+//    and a fixed order over the four waves.
+//  * sp_reduce_scatter — rank-ordered float32 sum of the N partials over the
+//    rank's rows, dropout with an input keep mask, residual add; 16-byte
+//    non-temporal accesses. HBM-bound: (4N + 4 + 1 + 4) bytes per element.
+//  * sp_all_gather — N slice copies into the gathered buffer in one launch.
+#include "common.hpp"
+#include "seqpar.hpp"
+
+namespace tps {
+namespace {
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// Sum over the 256 threads of the workgroup: butterfly per wave, then the four
+// wave sums added in wave order by every thread.
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();  // red may still be read from the previous call
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+template <int VPT>
+__global__ __launch_bounds__(256) void layernorm_kernel(const f32x4* __restrict__ X, int64_t h4,
+                                                        const f32x4* __restrict__ gamma,
+                                                        const f32x4* __restrict__ beta, float eps, float inv_h,
+                                                        uint2* __restrict__ Y) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const f32x4* x = X + row * h4;
+  f32x4 v[VPT];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j = threadIdx.x + k * 256;
+    v[k] = j < h4 ? __builtin_nontemporal_load(x + j) : f32x4{0.f, 0.f, 0.f, 0.f};
+    s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
+  }
+  const float mean = block_sum(s, red) * inv_h;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j = threadIdx.x + k * 256;
+    if (j < h4) {
+      const float d0 = v[k][0] - mean, d1 = v[k][1] - mean, d2 = v[k][2] - mean, d3 = v[k][3] - mean;
+      q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+    }
+  }
+  const float var = block_sum(q, red) * inv_h;
+  const float rstd = 1.0f / sqrtf(var + eps);
+  uint2* y = Y + row * h4;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j = threadIdx.x + k * 256;
+    if (j < h4) {
+      const f32x4 g = gamma[j], b = beta[j];
+      const float y0 = (v[k][0] - mean) * rstd * g[0] + b[0];
+      const float y1 = (v[k][1] - mean) * rstd * g[1] + b[1];
+      const float y2 = (v[k][2] - mean) * rstd * g[2] + b[2];
+      const float y3 = (v[k][3] - mean) * rstd * g[3] + b[3];
+      y[j] = uint2{pack_bf16x2(y0, y1), pack_bf16x2(y2, y3)};
+    }
+  }
+}
+
+template <int N>
+__global__ __launch_bounds__(256) void reduce_scatter_kernel(SpParts p, int64_t off4, int64_t nvec,
+                                                             const f32x4* R, const uint32_t* __restrict__ keep,
+                                                             float keep_prob, f32x4* out) {
+  // out may be the residual itself (in-place update): each element is read and
+  // then written by the same thread.
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) {
+    f32x4 x[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = __builtin_nontemporal_load(static_cast<const f32x4*>(p.p[i]) + off4 + v);
+    f32x4 s = x[0];
+#pragma unroll
+    for (int i = 1; i < N; ++i) s = s + x[i];
+    if (keep) {
+      const uint32_t k = keep[v];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] = ((k >> (8 * c)) & 0xffu) ? s[c] / keep_prob : 0.f;
+    }
+    __builtin_nontemporal_store(__builtin_nontemporal_load(R + v) + s, out + v);
+  }
+}
+
+__global__ __launch_bounds__(256) void all_gather_kernel(SpParts p, int64_t nvec, u32x4* __restrict__ out) {
+  const int j = blockIdx.y;
+  const u32x4* src = static_cast<const u32x4*>(p.p[j]);
+  u32x4* dst = out + (int64_t)j * nvec;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride)
+    __builtin_nontemporal_store(__builtin_nontemporal_load(src + v), dst + v);
+}
+
+template <int N>
+hipError_t launch_rs(const SpParts& p, int64_t off4, int64_t nvec, const float* R, const uint8_t* keep,
+                     float keep_prob, float* out, hipStream_t st) {
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(reduce_scatter_kernel<N>, dim3((unsigned)blocks), dim3(256), 0, st, p, off4, nvec,
+                     reinterpret_cast<const f32x4*>(R), reinterpret_cast<const uint32_t*>(keep), keep_prob,
+                     reinterpret_cast<f32x4*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t layernorm_rows(const float* X, int64_t rows, int64_t h, const float* gamma, const float* beta, float eps,
+                          uint16_t* Y, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const int64_t h4 = h / 4;
+  const int vpt = (int)((h4 + 255) / 256);
+  const dim3 grid((unsigned)rows), block(256);
+  const float inv_h = 1.0f / (float)h;
+  auto Xv = reinterpret_cast<const f32x4*>(X);
+  auto Gv = reinterpret_cast<const f32x4*>(gamma);
+  auto Bv = reinterpret_cast<const f32x4*>(beta);
+  auto Yv = reinterpret_cast<uint2*>(Y);
+  if (vpt <= 4)
+    hipLaunchKernelGGL(layernorm_kernel<4>, grid, block, 0, st, Xv, h4, Gv, Bv, eps, inv_h, Yv);
+  else if (vpt <= 8)
+    hipLaunchKernelGGL(layernorm_kernel<8>, grid, block, 0, st, Xv, h4, Gv, Bv, eps, inv_h, Yv);
+  else if (vpt <= 12)
+    hipLaunchKernelGGL(layernorm_kernel<12>, grid, block, 0, st, Xv, h4, Gv, Bv, eps, inv_h, Yv);
+  else if (vpt <= 18)
+    hipLaunchKernelGGL(layernorm_kernel<18>, grid, block, 0, st, Xv, h4, Gv, Bv, eps, inv_h, Yv);
+  else if (vpt <= 24)
+    hipLaunchKernelGGL(layernorm_kernel<24>, grid, block, 0, st, Xv, h4, Gv, Bv, eps, inv_h, Yv);
+  else if (vpt <= 32)
+    hipLaunchKernelGGL(layernorm_kernel<32>, grid, block, 0, st, Xv, h4, Gv, Bv, eps, inv_h, Yv);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t sp_reduce_scatter(const SpParts& parts, int n, int64_t row0, int64_t rows, int64_t h,
+                             const float* residual, const uint8_t* keep, float keep_prob, float* out, hipStream_t st) {
+  const int64_t nvec = rows * h / 4;
+  if (nvec == 0) return hipSuccess;
+  const int64_t off4 = row0 * h / 4;
+  switch (n) {
+#define TPS_CASE(k) \
+  case k:           \
+    return launch_rs<k>(parts, off4, nvec, residual, keep, keep_prob, out, st);
+    TPS_CASE(1) TPS_CASE(2) TPS_CASE(3) TPS_CASE(4) TPS_CASE(5) TPS_CASE(6) TPS_CASE(7) TPS_CASE(8)
+    TPS_CASE(9) TPS_CASE(10) TPS_CASE(11) TPS_CASE(12) TPS_CASE(13) TPS_CASE(14) TPS_CASE(15) TPS_CASE(16)
+#undef TPS_CASE
+    default:
+      return hipErrorInvalidValue;
+  }
+}
+
+hipError_t sp_all_gather(const SpParts& parts, int n, int64_t rows, int64_t h, uint16_t* out, hipStream_t st) {
+  const int64_t nvec = rows * h / 8;
+  if (nvec == 0 || n == 0) return hipSuccess;
+  int64_t bx = (nvec + 255) / 256;
+  const int64_t cap = (256 * 8 + n - 1) / n;
+  if (bx > cap) bx = cap;
+  hipLaunchKernelGGL(all_gather_kernel, dim3((unsigned)bx, (unsigned)n), dim3(256), 0, st, parts, nvec,
+                     reinterpret_cast<u32x4*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace tps

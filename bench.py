@@ -50,7 +50,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--no-next", action="store_true",
-                   help="skip the extra rows timed after the step (PaLM-shaped MLP with recompute)")
+                   help="skip the extra rows timed after the step (PaLM-shaped MLP with recompute, "
+                        "cross-entropy, sequence parallelism)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed steps, run a plain 256 MiB device-to-device copy three times, "
                         "the calibration kernel for HBM byte counters")
@@ -110,8 +111,9 @@ def traffic_from_profiles(key: str):
 def next_rows(tp, torch, dev, randn, reps=5):
     """Rows beyond the step, timed on their own after it: the PaLM-shaped MLP shard
     (M=2048, h=18432, f=9216), forward with saved U, backward with activation
-    recompute (U, Y formed again from X and A_i inside mlp_bwd); and the
-    vocabulary-parallel output layer + cross-entropy of one rank."""
+    recompute (U, Y formed again from X and A_i inside mlp_bwd); the
+    vocabulary-parallel output layer + cross-entropy of one rank; and the
+    sequence-parallel LayerNorm, all-gather and reduce-scatter of one rank."""
     Mp, Hp, Fp = 2048, 18432, 9216
     X = randn((Mp, Hp), 1.0, 40)
     A = randn((Hp, Fp), 0.005, 41)
@@ -180,6 +182,42 @@ def next_rows(tp, torch, dev, randn, reps=5):
             rec.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
         out[name] = rec
     del Hh, E, tg, sums, tls, ws, rows, tot
+    torch.cuda.empty_cache()
+
+    # Sequence parallelism at the GPT-3 shard: one rank's LayerNorm over its 256
+    # rows, the all-gather stand-in (8 x 256 rows of bf16), and the reduce-scatter
+    # stand-in over 8 fp32 partials [2048, 12288] with dropout and residual.
+    Ss, Hs, Ns = 2048, 12288, 8
+    rs_rows = Ss // Ns
+    Rr = randn((rs_rows, Hs), 1.0, 60, torch.float32)
+    gam = randn((Hs,), 0.1, 61, torch.float32) + 1.0
+    bet = randn((Hs,), 0.1, 62, torch.float32)
+    Ls = [torch.empty(rs_rows, Hs, dtype=torch.bfloat16, device=dev) for _ in range(Ns)]
+    Xg = torch.empty(Ss, Hs, dtype=torch.bfloat16, device=dev)
+    parts = [randn((Ss, Hs), 1.0, 63 + i, torch.float32) for i in range(Ns)]
+    keep = (torch.rand(rs_rows, Hs, generator=torch.Generator().manual_seed(71)) < 0.9).to(torch.uint8).to(dev)
+    Ro = torch.empty_like(Rr)
+    sp_rows = (
+        ("sp_layernorm", lambda: tp.layernorm(Rr, gam, bet, Ls[0]), rs_rows * Hs * (4 + 2) + 2 * Hs * 4),
+        ("sp_all_gather", lambda: tp.sp_all_gather(Ls, Xg), 2 * Ss * Hs * 2),
+        ("sp_reduce_scatter", lambda: tp.sp_reduce_scatter(parts, 3, Rr, Ro, keep=keep, keep_prob=0.9),
+         rs_rows * Hs * (4 * Ns + 4 + 1 + 4)),
+    )
+    for name, fn, nbytes in sp_rows:
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out[name] = {"ms": round(ms, 4), "bytes": nbytes, "gbs": round(gbs, 1),
+                     "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    del Rr, gam, bet, Ls, Xg, parts, keep, Ro
     torch.cuda.empty_cache()
     return out
 

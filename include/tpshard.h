@@ -184,6 +184,36 @@ tp_status tp_vocab_ce_loss(int64_t M, const float* const* sumexp_parts,
                            const float* const* tlogit_parts, int n_parts, float* loss_rows,
                            float* loss_sum, void* stream);
 
+/* Sequence parallelism around the tensor-parallel MLP [www.discosf.com/news/5875844,
+ * 2.3 序列并行与激活重计算 (LayerNorm and Dropout run on each rank's slice of the
+ * sequence instead of on the whole sequence everywhere); m.youleyou.com/wenzhang/3143730,
+ * 二、§2.2 (the all-reduce is a reduce-scatter followed by an all-gather)].
+ * Rank i owns rows [i*s/N, (i+1)*s/N) of the sequence.
+ *
+ * LayerNorm of one rank's rows (the page does not write LayerNorm out; this is the
+ * standard one): per row, mean and biased variance over h in float32,
+ *   Y = bf16((X - mean) / sqrt(var + eps) * gamma + beta)   (round to nearest even)
+ *   X [rows, h] float32, gamma/beta [h] float32, Y [rows, h] bf16; h % 8 == 0,
+ *   h <= 32768. Y may point into the rows of a gathered [s, h] buffer. */
+tp_status tp_layernorm(int64_t rows, int64_t h, const float* X, const float* gamma,
+                       const float* beta, float eps, void* Y, void* stream);
+
+/* All-gather stand-in on one GPU: out = [slices[0]; ...; slices[n-1]], each slice
+ * bf16 [rows, h], out bf16 [n*rows, h]. slices: HOST array of n device pointers,
+ * 1 <= n <= 16; h % 8 == 0. */
+tp_status tp_sp_all_gather(int n_parts, const void* const* slices, int64_t rows, int64_t h,
+                           void* out, void* stream);
+
+/* Reduce-scatter stand-in for rank `rank`, fused with Dropout and the residual add:
+ *   O = ((P_0 + P_1) + ...) + P_{n-1} over rows [rank*s/n, (rank+1)*s/n) (float32, rank order)
+ *   out = residual + (keep ? O / keep_prob : 0)  (keep NULL: out = residual + O)
+ * partials: HOST array of n device pointers to float32 [s, h]; residual and out float32
+ * [s/n, h] (out may equal residual); keep: uint8 [s/n, h] (nonzero = kept, the drawn
+ * mask is an input), 4-byte aligned, keep_prob in (0, 1]. s % n == 0, h % 8 == 0. */
+tp_status tp_sp_reduce_scatter(int n_parts, const float* const* partials, int64_t s, int64_t h,
+                               int rank, const float* residual, const uint8_t* keep,
+                               float keep_prob, float* out, void* stream);
+
 /* Shard-sum standing in for the all-reduce of N partials on one GPU:
  *   out = ((P_0 + P_1) + P_2) + ... + P_{N-1}, elementwise, in float32, in this
  *   fixed order (so the result is reproducible bit for bit).

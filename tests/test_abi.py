@@ -129,6 +129,38 @@ class TestValidation:
         assert loss(M, arr, bad, 2, P, P, None) == INVALID
         assert "tlogit_parts" in _err()
 
+    def test_sequence_parallel(self):
+        ln = lib.tp_layernorm
+        assert ln(-1, 64, P, P, P, 1e-5, P, None) == INVALID
+        assert ln(4, 0, P, P, P, 1e-5, P, None) == INVALID
+        assert ln(4, 60, P, P, P, 1e-5, P, None) == UNSUPPORTED           # h % 8
+        assert ln(4, 32776, P, P, P, 1e-5, P, None) == UNSUPPORTED        # h too large
+        assert ln(4, 64, P, P, P, -1.0, P, None) == INVALID               # eps < 0
+        assert ln(4, 64, P, None, P, 1e-5, P, None) == INVALID            # gamma NULL
+        assert ln(4, 64, P, P, P, 1e-5, MIS, None) == UNSUPPORTED
+        assert ln(0, 64, None, None, None, 1e-5, None, None) == OK        # empty
+        arr = (C.c_void_p * 17)(*([P] * 17))
+        ag = lib.tp_sp_all_gather
+        assert ag(0, arr, 4, 64, P, None) == INVALID
+        assert ag(17, arr, 4, 64, P, None) == INVALID
+        assert ag(2, arr, 4, 12, P, None) == UNSUPPORTED
+        assert ag(2, arr, -1, 64, P, None) == INVALID
+        assert ag(2, (C.c_void_p * 2)(P, MIS), 4, 64, P, None) == UNSUPPORTED
+        assert "slices[1]" in _err()
+        assert ag(2, None, 0, 64, None, None) == OK
+        rs = lib.tp_sp_reduce_scatter
+        assert rs(4, arr, 18, 64, 0, P, None, 1.0, P, None) == INVALID     # s % n
+        assert rs(4, arr, 16, 64, 4, P, None, 1.0, P, None) == INVALID     # rank
+        assert rs(4, arr, 16, 64, -1, P, None, 1.0, P, None) == INVALID
+        assert rs(4, arr, 16, 64, 0, P, P, 0.0, P, None) == INVALID        # keep_prob
+        assert rs(4, arr, 16, 64, 0, P, P, 1.5, P, None) == INVALID
+        assert rs(4, arr, 16, 64, 0, P, P + 2, 0.5, P, None) == UNSUPPORTED  # keep alignment
+        assert rs(4, arr, 16, 64, 0, None, None, 1.0, P, None) == INVALID  # residual NULL
+        assert rs(4, arr, 16, 20, 0, P, None, 1.0, P, None) == UNSUPPORTED
+        assert rs(2, (C.c_void_p * 2)(P, None), 16, 64, 0, P, None, 1.0, P, None) == INVALID
+        assert rs(17, arr, 17, 64, 0, P, None, 1.0, P, None) == INVALID
+        assert rs(4, None, 0, 64, 0, None, None, 1.0, None, None) == OK
+
     def test_shard_sum(self):
         arr = (C.c_void_p * 17)(*([P] * 17))
         s = lib.tp_shard_sum

@@ -1,0 +1,182 @@
+"""GPU parity of the sequence-parallel kernels (LayerNorm on a rank's rows, the
+all-gather and reduce-scatter stand-ins, dropout + residual) and of the whole
+sequence-parallel MLP block against the float64 oracle, through the C ABI.
+
+Tolerances: LayerNorm runs in float32 and rounds once to bf16, so each output is
+within one bf16 spacing of the float64 value (plus 4e-6 for the float32
+arithmetic near zero, whose terms are O(1)); the all-gather is a copy
+(bit-exact); the reduce-scatter adds N float32 values in rank order, so it is
+within 1e-5 absolute + 1e-6 relative of the float64 sum, and dropped entries
+equal the residual exactly. The block's MLP uses the bf16 GEMM tolerance.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import seqpar
+from tests.gpu_util import DEV, assert_bf16_close, bits_host, f32_dev, f64_host, note
+from workloads import CONFIGS, mlp_inputs, shard_sum_inputs, sp_inputs
+
+pytestmark = pytest.mark.gpu
+
+tp = pytest.importorskip("attention_shard_math_amd")
+
+
+def _bf16_spacing(r):
+    a = np.maximum(np.abs(r), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def assert_ln_close(g, r, what):
+    d = np.abs(g - r)
+    bad = d > _bf16_spacing(r) + 4e-6
+    assert not bad.any(), f"{what}: {bad.sum()} outputs beyond one bf16 spacing (max diff {d.max():.3e})"
+    same = np.mean(g == oracle.round_to_bf16(r))
+    assert same >= 0.99, f"{what}: only {same:.4f} equal the rounded float64 value"
+
+
+def _ln_gpu(R, gamma, beta):
+    rows, h = R.shape
+    Y = torch.empty(rows, h, dtype=torch.bfloat16, device=DEV)
+    tp.layernorm(f32_dev(R), f32_dev(gamma), f32_dev(beta), Y)
+    return Y
+
+
+@pytest.mark.parametrize("rows,h", [(37, 8), (5, 328), (64, 1032), (3, 12288), (2, 18432), (1, 32768)])
+def test_layernorm(rows, h):
+    inp = sp_inputs(rows, h, seed=500 + h, sigma_r=2.0)
+    R = inp["R"] + np.float32(0.75)  # a row mean away from zero
+    note(f"layernorm rows={rows} h={h}")
+    Y = _ln_gpu(R, inp["gamma"], inp["beta"])
+    torch.cuda.synchronize()
+    r = seqpar.layernorm(R.astype(np.float64), inp["gamma"], inp["beta"])
+    assert_ln_close(f64_host(Y), r, f"LN rows={rows} h={h}")
+
+
+def test_layernorm_constant_row_gives_beta():
+    h = 256
+    R = np.full((3, h), 2.5, np.float32)
+    gamma = np.linspace(0.5, 1.5, h, dtype=np.float32)
+    beta = np.linspace(-1, 1, h, dtype=np.float32)
+    note("layernorm constant rows")
+    Y = _ln_gpu(R, gamma, beta)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64_host(Y), np.broadcast_to(oracle.round_to_bf16(beta.astype(np.float64)), (3, h)))
+
+
+def test_all_gather_bit_exact():
+    for n, rows, h in [(1, 3, 8), (4, 17, 64), (16, 2, 1024)]:
+        note(f"sp_all_gather n={n} rows={rows} h={h}")
+        sl = [torch.randn(rows, h, device=DEV).to(torch.bfloat16) for _ in range(n)]
+        out = torch.empty(n * rows, h, dtype=torch.bfloat16, device=DEV)
+        tp.sp_all_gather(sl, out)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits_host(out), np.concatenate([bits_host(x) for x in sl]))
+
+
+@pytest.mark.parametrize("n,s,h,drop", [(1, 4, 8, False), (3, 30, 72, True), (8, 64, 520, True), (16, 32, 64, False)])
+def test_reduce_scatter(n, s, h, drop):
+    parts = [p.reshape(s, h) for p in shard_sum_inputs(n, s * h, seed=600 + n)]
+    inp = sp_inputs(s, h, seed=700 + n, keep_prob=0.8)
+    rows = s // n
+    pd = [f32_dev(p) for p in parts]
+    for rank in sorted({0, n // 2, n - 1}):
+        rs = slice(rank * rows, (rank + 1) * rows)
+        keep = inp["keep"][rs] if drop else None
+        note(f"sp_reduce_scatter n={n} s={s} h={h} rank={rank} dropout={drop}")
+        out = torch.full((rows, h), float("nan"), dtype=torch.float32, device=DEV)
+        tp.sp_reduce_scatter(pd, rank, f32_dev(inp["R"][rs]), out,
+                             keep=None if keep is None else torch.from_numpy(keep).to(DEV), keep_prob=0.8)
+        torch.cuda.synchronize()
+        O = seqpar.reduce_scatter(parts, n, rank)
+        want = seqpar.dropout_residual(inp["R"][rs], O, keep, 0.8)
+        g = f64_host(out)
+        np.testing.assert_allclose(g, want, rtol=1e-6, atol=1e-5)
+        if drop:
+            np.testing.assert_array_equal(g[keep == 0], inp["R"][rs][keep == 0])
+
+
+def test_reduce_scatter_in_place():
+    n, s, h = 4, 16, 64
+    parts = [p.reshape(s, h) for p in shard_sum_inputs(n, s * h, seed=611)]
+    R = sp_inputs(s, h, seed=612)["R"]
+    note("sp_reduce_scatter in place")
+    res = f32_dev(R[4:8])
+    tp.sp_reduce_scatter([f32_dev(p) for p in parts], 1, res, res)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(f64_host(res), R[4:8] + seqpar.reduce_scatter(parts, n, 1), rtol=1e-6, atol=1e-5)
+
+
+def _sp_block_gpu(R, gamma, beta, shards_dev, keep, p, N):
+    s, h = R.shape
+    rows = s // N
+    Rd, g, b = f32_dev(R), f32_dev(gamma), f32_dev(beta)
+    L = [torch.empty(rows, h, dtype=torch.bfloat16, device=DEV) for _ in range(N)]
+    for i in range(N):
+        tp.layernorm(Rd[i * rows:(i + 1) * rows], g, b, L[i])
+    X = torch.empty(s, h, dtype=torch.bfloat16, device=DEV)
+    tp.sp_all_gather(L, X)
+    Z = []
+    for A, B in shards_dev:
+        f = A.shape[1]
+        Y = torch.empty(s, f, dtype=torch.bfloat16, device=DEV)
+        z = torch.empty(s, h, dtype=torch.float32, device=DEV)
+        tp.mlp_fwd(X, A, B, Y, z)
+        Z.append(z)
+    out = torch.empty(s, h, dtype=torch.float32, device=DEV)
+    kd = torch.from_numpy(keep).to(DEV)
+    for i in range(N):
+        rs = slice(i * rows, (i + 1) * rows)
+        tp.sp_reduce_scatter(Z, i, Rd[rs], out[rs], keep=kd[rs], keep_prob=p)
+    return X, out
+
+
+@pytest.mark.parametrize("N", [2, 4])
+def test_sp_mlp_block(N):
+    s, h, f_full = 256, 1024, 4096
+    sp = sp_inputs(s, h, seed=800 + N, keep_prob=0.9)
+    mi = mlp_inputs(s, h, f_full, N, "bf16", 810 + N, 1.0, 0.02, None)
+    from tests.gpu_util import bf16_dev
+    from oracle.bf16 import bf16_bits_to_f64
+    shards_dev = [(bf16_dev(A), bf16_dev(B)) for A, B in mi["shards"]]
+    note(f"sequence-parallel MLP block s={s} h={h} N={N}")
+    X, out = _sp_block_gpu(sp["R"], sp["gamma"], sp["beta"], shards_dev, sp["keep"], 0.9, N)
+    torch.cuda.synchronize()
+    shards = [(bf16_bits_to_f64(A), bf16_bits_to_f64(B)) for A, B in mi["shards"]]
+    R64 = sp["R"].astype(np.float64)
+    want = seqpar.sp_mlp_block(R64, sp["gamma"], sp["beta"], shards, sp["keep"], 0.9, matched=True)
+    assert_ln_close(f64_host(X), seqpar.layernorm(R64, sp["gamma"], sp["beta"]), "gathered LN")
+    assert_bf16_close(f64_host(out) - R64, want["R_out"] - R64, "dropout(reduce-scatter)")
+
+
+def test_full_size_layernorm_gather_reduce_scatter():
+    """GPT-3 shard: 8 ranks of 256 rows x 12288; the reduce-scatter of 8 fp32
+    partials [2048, 12288] with dropout 0.9 and the residual, for every rank."""
+    c = CONFIGS[8]
+    s, h, N = c["s"], c["h"], c["N"]
+    rows = s // N
+    sp = sp_inputs(s, h, c["seed"], c["sigma_r"], c["sigma_g"], c["sigma_b"], c["keep_prob"])
+    parts = [p.reshape(s, h) for p in shard_sum_inputs(N, s * h, c["seed"] + 1, c["sigma_p"])]
+    Rd, g, b = f32_dev(sp["R"]), f32_dev(sp["gamma"]), f32_dev(sp["beta"])
+    L = [torch.empty(rows, h, dtype=torch.bfloat16, device=DEV) for _ in range(N)]
+    note("full-size layernorm x8 + all-gather")
+    for i in range(N):
+        tp.layernorm(Rd[i * rows:(i + 1) * rows], g, b, L[i])
+    X = torch.empty(s, h, dtype=torch.bfloat16, device=DEV)
+    tp.sp_all_gather(L, X)
+    torch.cuda.synchronize()
+    assert_ln_close(f64_host(X), seqpar.layernorm(sp["R"].astype(np.float64), sp["gamma"], sp["beta"]), "LN 2048x12288")
+    pd = [f32_dev(p) for p in parts]
+    kd = torch.from_numpy(sp["keep"]).to(DEV)
+    out = torch.empty(s, h, dtype=torch.float32, device=DEV)
+    note("full-size reduce-scatter x8")
+    for i in range(N):
+        rs = slice(i * rows, (i + 1) * rows)
+        tp.sp_reduce_scatter(pd, i, Rd[rs], out[rs], keep=kd[rs], keep_prob=c["keep_prob"])
+    torch.cuda.synchronize()
+    g_out = f64_host(out)
+    for i in range(N):
+        rs = slice(i * rows, (i + 1) * rows)
+        want = seqpar.dropout_residual(sp["R"][rs], seqpar.reduce_scatter(parts, N, i), sp["keep"][rs], c["keep_prob"])
+        np.testing.assert_allclose(g_out[rs], want, rtol=1e-6, atol=1e-5)

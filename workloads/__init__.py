@@ -16,6 +16,7 @@ from .gen import (  # noqa: F401
     attn_inputs,
     embed_inputs,
     ce_inputs,
+    sp_inputs,
     shard_sum_inputs,
     shard_cols,
     shard_rows,

@@ -38,6 +38,10 @@ CONFIGS = {
     # (padded to 50304 = 8 * 6288), one sequence of 2048 tokens.
     7: dict(name="vocab_parallel_ce", v=50304, N=8, h=12288, b=1, s=2048, dtype="bf16",
             sigma_h=1.0, sigma_w=0.02, seed=1007),
+    # Sequence-parallel MLP block at the GPT-3 shard: LayerNorm on s/N rows per rank,
+    # all-gather, reduce-scatter of 8 fp32 partials fused with dropout and residual.
+    8: dict(name="gpt3_sp_mlp_block", s=2048, h=12288, f=6144, N=8, sigma_r=1.0, sigma_g=0.1,
+            sigma_b=0.1, keep_prob=0.9, sigma_p=1.0, seed=1008),
 }
 
 
@@ -153,6 +157,19 @@ def ce_inputs(M: int, h: int, v: int, seed: int, sigma_h: float = 1.0, sigma_w: 
         E[r0:r1] = bf16_bits(draw_normal_f32(rng, (r1 - r0, h), sigma_w))
     targets = rng.integers(0, v, size=M, dtype=np.int32)
     return dict(H=H, E=E, targets=targets)
+
+
+def sp_inputs(s: int, h: int, seed: int, sigma_r: float = 1.0, sigma_g: float = 0.1,
+              sigma_b: float = 0.1, keep_prob: float = 0.9):
+    """Sequence-parallel block inputs: residual rows R [s, h] float32 N(0, sigma_r),
+    LayerNorm gamma = 1 + N(0, sigma_g) and beta = N(0, sigma_b) [h] float32, then a
+    dropout keep mask [s, h] uint8 (1 where a uniform draw in [0, 1) is below keep_prob)."""
+    rng = np.random.default_rng(seed)
+    R = draw_normal_f32(rng, (s, h), sigma_r)
+    gamma = (np.float32(1.0) + draw_normal_f32(rng, (h,), sigma_g)).astype(np.float32)
+    beta = draw_normal_f32(rng, (h,), sigma_b)
+    keep = (rng.random((s, h), dtype=np.float32) < np.float32(keep_prob)).astype(np.uint8)
+    return dict(R=R, gamma=gamma, beta=beta, keep=keep)
 
 
 def shard_sum_inputs(n_partials: int, numel: int, seed: int, sigma: float = 1.0,
