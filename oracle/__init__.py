@@ -38,7 +38,9 @@ from .mlp import (  # noqa: F401
     mlp_fwd_rows, mlp_bwd_cols,
 )
 from .shard_sum import shard_sum_f64, shard_sum_f32_ordered, shard_sum_bf16_ordered  # noqa: F401
-from .attention import attn_shard, attn_core, mha_full, attn_shard_rows  # noqa: F401
+from .attention import (  # noqa: F401
+    attn_shard, attn_core, mha_full, attn_shard_rows, attn_core_bwd, attn_lse, attn_shard_bwd,
+)
 from .embedding import vocab_embed_shard  # noqa: F401
 from .vocab_ce import vocab_ce_partials, vocab_ce_combine, vocab_ce_sharded  # noqa: F401
 from .seqpar import layernorm, all_gather, reduce_scatter, dropout_residual, sp_mlp_block, tp_mlp_block  # noqa: F401,E501

@@ -16,7 +16,13 @@ Readings where the pages are silent or garbled (listed in the design doc):
     Wo_i rows follow the same head order;
   * "matched" mode rounds Q, K, V and the concatenated head outputs O to
     bfloat16, where the GPU stores them. The softmax probabilities are not
-    rounded here.
+    rounded here;
+  * backward: the chain rule through the same formula, written out per head
+    (dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(P * dP)), dQ = dS K / sqrt(d),
+    dK = dS^T Q / sqrt(d)); the layer's two all-reduces (forward after Wo,
+    backward of the input gradient) make the rank's dX_i a partial
+    [m.youleyou.com/wenzhang/3143730, 三、Self-Attention层 §3.2]. Matched mode
+    rounds dO = dOut Wo_i^T and dQKV to bfloat16, where the GPU stores them.
 """
 import numpy as np
 
@@ -92,3 +98,57 @@ def attn_shard_rows(X, Wqkv_i, Wo_i, b, s, n_heads_local, d, rows, causal=True,
             O[n, c] = (e / e.sum()) @ V[kr, c]
     O = _r(O, matched)
     return dict(O=O, out=O @ Wo_i)
+
+
+def _head_attention_bwd(q, k, v, do, causal):
+    """Gradients of <do, softmax(q k^T / sqrt(d)) v> with respect to q, k, v."""
+    d = q.shape[1]
+    S = (q @ k.T) / np.sqrt(d)
+    if causal:
+        t = np.arange(q.shape[0])[:, None]
+        u = np.arange(k.shape[0])[None, :]
+        S = np.where(u <= t, S, -np.inf)
+    S = S - S.max(axis=1, keepdims=True)
+    P = np.exp(S)
+    P /= P.sum(axis=1, keepdims=True)
+    dV = P.T @ do
+    dP = do @ v.T
+    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    return dS @ k / np.sqrt(d), dS.T @ q / np.sqrt(d), dV
+
+
+def attn_core_bwd(Q, K, V, dO, b, s, n_heads, d, causal=True):
+    """Per-sequence, per-head attention backward. All [b*s, n_heads*d]."""
+    dQ, dK, dV = (np.empty_like(Q, dtype=np.float64) for _ in range(3))
+    for bi in range(b):
+        r = slice(bi * s, (bi + 1) * s)
+        for j in range(n_heads):
+            c = slice(j * d, (j + 1) * d)
+            dQ[r, c], dK[r, c], dV[r, c] = _head_attention_bwd(Q[r, c], K[r, c], V[r, c], dO[r, c], causal)
+    return dQ, dK, dV
+
+
+def attn_lse(Q, K, b, s, n_heads, d, causal=True):
+    """log-sum-exp of each query's scaled scores, [b, n_heads, s] (natural log)."""
+    out = np.empty((b, n_heads, s), np.float64)
+    for bi in range(b):
+        r = slice(bi * s, (bi + 1) * s)
+        for j in range(n_heads):
+            c = slice(j * d, (j + 1) * d)
+            S = (Q[r, c] @ K[r, c].T) / np.sqrt(d)
+            if causal:
+                S = np.where(np.arange(s)[None, :] <= np.arange(s)[:, None], S, -np.inf)
+            m = S.max(axis=1)
+            out[bi, j] = m + np.log(np.exp(S - m[:, None]).sum(axis=1))
+    return out
+
+
+def attn_shard_bwd(X, Wqkv_i, Wo_i, dOut, b, s, n_heads_local, d, causal=True, matched=True):
+    """One rank's attention backward: dWo_i = O^T dOut, dO = dOut Wo_i^T, the core
+    backward, dWqkv_i = X^T dQKV and the input-gradient partial dX_i = dQKV Wqkv_i^T."""
+    f = attn_shard(X, Wqkv_i, Wo_i, b, s, n_heads_local, d, causal, matched)
+    dWo = f["O"].T @ dOut
+    dO = _r(dOut @ Wo_i.T, matched)
+    dQ, dK, dV = attn_core_bwd(f["Q"], f["K"], f["V"], dO, b, s, n_heads_local, d, causal)
+    dQKV = _r(np.concatenate([dQ, dK, dV], axis=1), matched)
+    return dict(fwd=f, dO=dO, dQKV=dQKV, dWo=dWo, dWqkv=X.T @ dQKV, dX=dQKV @ Wqkv_i.T)

@@ -557,3 +557,90 @@ class TestSequenceParallel:
         want = R + np.where(keep != 0, Z / 0.9, 0.0)
         np.testing.assert_allclose(seqpar.sp_mlp_block(R, g, b, shards, keep, 0.9, matched=False)["R_out"], want,
                                    rtol=1e-11, atol=1e-11)
+
+
+class TestAttentionBackward:
+    """Attention backward [m.youleyou.com/wenzhang/3143730, 三、§3.2]: the chain rule
+    through per-head causal softmax attention, pinned against torch's float64
+    autograd, central finite differences, and the head-sharding identities."""
+
+    def _qkv(self, seed, b, s, H, d, scale=0.7):
+        rng = np.random.default_rng(seed)
+        return [rng.standard_normal((b * s, H * d)) * scale for _ in range(4)]
+
+    @pytest.mark.parametrize("causal", [True, False])
+    def test_torch_autograd(self, causal):
+        b, s, H, d = 2, 9, 3, 8
+        Q, K, V, dO = self._qkv(61, b, s, H, d)
+        dQ, dK, dV = oracle.attn_core_bwd(Q, K, V, dO, b, s, H, d, causal)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (Q, K, V))
+        outs = []
+        for bi in range(b):
+            r = slice(bi * s, (bi + 1) * s)
+            for j in range(H):
+                c = slice(j * d, (j + 1) * d)
+                outs.append((torch.nn.functional.scaled_dot_product_attention(
+                    tq[r, c][None], tk[r, c][None], tv[r, c][None], is_causal=causal)[0] *
+                    torch.from_numpy(dO[r, c])).sum())
+        torch.stack(outs).sum().backward()
+        for g, t in ((dQ, tq), (dK, tk), (dV, tv)):
+            np.testing.assert_allclose(g, t.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+    def test_finite_differences(self):
+        b, s, H, d = 1, 5, 1, 4
+        Q, K, V, dO = self._qkv(62, b, s, H, d)
+        grads = oracle.attn_core_bwd(Q, K, V, dO, b, s, H, d, True)
+        eps = 1e-6
+        for which in range(3):
+            for (i, j) in [(0, 0), (2, 3), (4, 1)]:
+                args = [Q.copy(), K.copy(), V.copy()]
+                args[which][i, j] += eps
+                fp = (oracle.attn_core(*args, b, s, H, d, True) * dO).sum()
+                args[which][i, j] -= 2 * eps
+                fm = (oracle.attn_core(*args, b, s, H, d, True) * dO).sum()
+                assert abs((fp - fm) / (2 * eps) - grads[which][i, j]) < 1e-7
+
+    def test_last_key_and_first_query(self):
+        """Causal: the last key is seen only by the last query, so dV of the last
+        key is P[s-1, s-1] dO[s-1]; the first query attends only to the first key,
+        so its dQ is zero (softmax of one entry is constant)."""
+        b, s, H, d = 1, 6, 1, 4
+        Q, K, V, dO = self._qkv(63, b, s, H, d)
+        dQ, dK, dV = oracle.attn_core_bwd(Q, K, V, dO, b, s, H, d, True)
+        lse = oracle.attn_lse(Q, K, b, s, H, d, True)[0, 0]
+        p_last = np.exp(Q[-1] @ K[-1] / np.sqrt(d) - lse[-1])
+        np.testing.assert_allclose(dV[-1], p_last * dO[-1], rtol=1e-12)
+        np.testing.assert_allclose(dQ[0], 0.0, atol=1e-15)
+        # lse of the first query is its own scaled score
+        np.testing.assert_allclose(lse[0], Q[0] @ K[0] / np.sqrt(d), rtol=1e-12)
+
+    def test_shards_sum_to_full_mha_backward(self):
+        rng = np.random.default_rng(64)
+        b, s, Hh, d, N = 1, 6, 4, 4, 2
+        h = Hh * d
+        X = rng.standard_normal((b * s, h))
+        Wq, Wk, Wv = (rng.standard_normal((h, h)) * 0.3 for _ in range(3))
+        Wo = rng.standard_normal((h, h)) * 0.3
+        dOut = rng.standard_normal((b * s, h))
+        tX = torch.tensor(X, requires_grad=True)
+        tW = [torch.tensor(w, requires_grad=True) for w in (Wq, Wk, Wv, Wo)]
+        Qf, Kf, Vf = (tX @ w for w in tW[:3])
+        heads = []
+        for j in range(Hh):
+            c = slice(j * d, (j + 1) * d)
+            heads.append(torch.nn.functional.scaled_dot_product_attention(Qf[:, c][None], Kf[:, c][None],
+                                                                          Vf[:, c][None], is_causal=True)[0])
+        ((torch.cat(heads, 1) @ tW[3]) * torch.from_numpy(dOut)).sum().backward()
+        Hl = Hh // N
+        dX = np.zeros_like(X)
+        for i in range(N):
+            cols = slice(i * Hl * d, (i + 1) * Hl * d)
+            Wqkv_i = np.concatenate([Wq[:, cols], Wk[:, cols], Wv[:, cols]], axis=1)
+            r = oracle.attn_shard_bwd(X, Wqkv_i, Wo[cols], dOut, b, s, Hl, d, True, matched=False)
+            dX += r["dX"]
+            np.testing.assert_allclose(r["dWo"], tW[3].grad.numpy()[cols], rtol=1e-10, atol=1e-12)
+            w = Hl * d
+            for k, tw in enumerate(tW[:3]):
+                np.testing.assert_allclose(r["dWqkv"][:, k * w:(k + 1) * w], tw.grad.numpy()[:, cols],
+                                           rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(dX, tX.grad.numpy(), rtol=1e-10, atol=1e-12)
