@@ -19,6 +19,12 @@ from ._lib import (  # noqa: F401
     attn_core,
     attn_fwd,
     attn_fwd_workspace,
+    attn_fwd_train,
+    attn_core_train,
+    attn_core_bwd,
+    attn_core_bwd_workspace,
+    attn_bwd,
+    attn_bwd_workspace,
     vocab_embed,
     vocab_ce_workspace,
     vocab_ce_partials,

@@ -32,6 +32,11 @@ _SIGS = {
     "tp_shard_sum": [C.c_int, C.POINTER(_vp), C.c_int, _i64, _vp, _vp],
     "tp_vocab_ce_partials": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_vocab_ce_loss": [_i64, C.POINTER(_vp), C.POINTER(_vp), C.c_int, _vp, _vp, _vp],
+    "tp_attn_core_train": [_i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp],
+    "tp_attn_fwd_train": [_i64, _i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_attn_core_bwd": [_i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "tp_attn_bwd": [_i64, _i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                    _sz, _vp],
     "tp_layernorm": [_i64, _i64, _vp, _vp, _vp, C.c_float, _vp, _vp],
     "tp_sp_all_gather": [C.c_int, C.POINTER(_vp), _i64, _i64, _vp, _vp],
     "tp_sp_reduce_scatter": [C.c_int, C.POINTER(_vp), _i64, _i64, C.c_int, _vp, _vp, C.c_float, _vp, _vp],
@@ -45,6 +50,10 @@ lib.tp_mlp_bwd_workspace.restype = _sz
 lib.tp_mlp_bwd_recompute_workspace.argtypes = [_i64, _i64, _i64]
 lib.tp_mlp_bwd_recompute_workspace.restype = _sz
 lib.tp_vocab_ce_workspace.argtypes = [_i64, _i64, _i64]
+lib.tp_attn_core_bwd_workspace.argtypes = [_i64, _i64, _i64]
+lib.tp_attn_core_bwd_workspace.restype = _sz
+lib.tp_attn_bwd_workspace.argtypes = [_i64, _i64, _i64, _i64, _i64]
+lib.tp_attn_bwd_workspace.restype = _sz
 lib.tp_vocab_ce_workspace.restype = _sz
 lib.tp_attn_fwd_workspace.argtypes = [_i64, _i64, _i64, _i64]
 lib.tp_attn_fwd_workspace.restype = _sz
@@ -172,6 +181,63 @@ def vocab_embed(ids, E_i, lo, hi, out, stream=None):
     h = E_i.shape[1]
     _check(lib.tp_vocab_embed(_ptr(ids, dtype=torch.int32, name="ids"), n, _ptr(E_i, (hi - lo, h), None, "E_i"),
                               lo, hi, h, _ptr(out, (n, h), E_i.dtype, "out"), _stream(stream)), "tp_vocab_embed")
+
+
+def _wsargs(ws):
+    return (None, 0) if ws is None else (_ptr(ws, name="ws"), ws.numel() * ws.element_size())
+
+
+def attn_core_train(QKV, O, lse, b, s, n_heads_local, d_head, causal=True, stream=None):
+    w = n_heads_local * d_head
+    bf = torch.bfloat16
+    _check(lib.tp_attn_core_train(b, s, n_heads_local, d_head, int(causal), _ptr(QKV, (b * s, 3 * w), bf, "QKV"),
+                                  _ptr(O, (b * s, w), bf, "O"), _ptr(lse, (b, n_heads_local, s), torch.float32, "lse"),
+                                  _stream(stream)), "tp_attn_core_train")
+
+
+def attn_fwd_train(X, Wqkv_i, Wo_i, out_partial, QKV, O, lse, b, s, n_heads_local, d_head, causal=True,
+                   stream=None):
+    h = X.shape[1]
+    w = n_heads_local * d_head
+    bf = torch.bfloat16
+    _check(lib.tp_attn_fwd_train(b, s, h, n_heads_local, d_head, int(causal), _ptr(X, (b * s, h), bf, "X"),
+                                 _ptr(Wqkv_i, (h, 3 * w), bf, "Wqkv_i"), _ptr(Wo_i, (w, h), bf, "Wo_i"),
+                                 _ptr(out_partial, (b * s, h), torch.float32, "out_partial"),
+                                 _ptr(QKV, (b * s, 3 * w), bf, "QKV"), _ptr(O, (b * s, w), bf, "O"),
+                                 _ptr(lse, (b, n_heads_local, s), torch.float32, "lse"), _stream(stream)),
+           "tp_attn_fwd_train")
+
+
+def attn_core_bwd_workspace(b, s, n_heads_local):
+    return int(lib.tp_attn_core_bwd_workspace(b, s, n_heads_local))
+
+
+def attn_core_bwd(QKV, O, dO, lse, dQKV, ws, b, s, n_heads_local, d_head, causal=True, stream=None):
+    w = n_heads_local * d_head
+    bf = torch.bfloat16
+    wp, wb = _wsargs(ws)
+    _check(lib.tp_attn_core_bwd(b, s, n_heads_local, d_head, int(causal), _ptr(QKV, (b * s, 3 * w), bf, "QKV"),
+                                _ptr(O, (b * s, w), bf, "O"), _ptr(dO, (b * s, w), bf, "dO"),
+                                _ptr(lse, (b, n_heads_local, s), torch.float32, "lse"),
+                                _ptr(dQKV, (b * s, 3 * w), bf, "dQKV"), wp, wb, _stream(stream)), "tp_attn_core_bwd")
+
+
+def attn_bwd_workspace(b, s, h, n_heads_local, d_head):
+    return int(lib.tp_attn_bwd_workspace(b, s, h, n_heads_local, d_head))
+
+
+def attn_bwd(X, Wqkv_i, Wo_i, QKV, O, lse, dOut, dX_i, dWqkv_i, dWo_i, ws, b, s, n_heads_local, d_head,
+             causal=True, stream=None):
+    h = X.shape[1]
+    w = n_heads_local * d_head
+    bf, f32 = torch.bfloat16, torch.float32
+    wp, wb = _wsargs(ws)
+    _check(lib.tp_attn_bwd(b, s, h, n_heads_local, d_head, int(causal), _ptr(X, (b * s, h), bf, "X"),
+                           _ptr(Wqkv_i, (h, 3 * w), bf, "Wqkv_i"), _ptr(Wo_i, (w, h), bf, "Wo_i"),
+                           _ptr(QKV, (b * s, 3 * w), bf, "QKV"), _ptr(O, (b * s, w), bf, "O"),
+                           _ptr(lse, (b, n_heads_local, s), f32, "lse"), _ptr(dOut, (b * s, h), bf, "dOut"),
+                           _ptr(dX_i, (b * s, h), f32, "dX_i"), _ptr(dWqkv_i, (h, 3 * w), f32, "dWqkv_i"),
+                           _ptr(dWo_i, (w, h), f32, "dWo_i"), wp, wb, _stream(stream)), "tp_attn_bwd")
 
 
 def vocab_ce_workspace(M, lo, hi):

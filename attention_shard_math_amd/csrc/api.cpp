@@ -264,6 +264,19 @@ TP_API tp_status tp_attn_core(int64_t b, int64_t s, int64_t n_heads_local, int64
                     fn);
 }
 
+TP_API tp_status tp_attn_core_train(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
+                                    const void* QKV, void* O, float* lse, void* stream) {
+  const char* fn = "tp_attn_core_train";
+  TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  if (b * s == 0) return ok();
+  TRY(check_ptr(fn, "QKV", QKV));
+  TRY(check_ptr(fn, "O", O));
+  TRY(check_ptr(fn, "lse", lse));
+  return hip_status(tps::attn_fwd(static_cast<const uint16_t*>(QKV), static_cast<uint16_t*>(O), (int)b, (int)s,
+                                  (int)n_heads_local, (int)d_head, causal != 0, as_stream(stream), lse),
+                    fn);
+}
+
 TP_API size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head) {
   if (b < 0 || s < 0 || n_heads_local < 0 || d_head < 0) return 0;
   const size_t t = (size_t)b * (size_t)s, w = (size_t)n_heads_local * (size_t)d_head;
@@ -298,6 +311,125 @@ TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   {
     tps::GemmArgs g = make_args(O, w, Wo_i, h, M, h, w, out_partial, h);
     TRY(hip_status(tps::gemm_bf16(g, true, false, tps::EPI_F32, st), fn));
+  }
+  return ok();
+}
+
+TP_API tp_status tp_attn_fwd_train(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head,
+                                   int causal, const void* X, const void* Wqkv_i, const void* Wo_i,
+                                   float* out_partial, void* QKV, void* O, float* lse, void* stream) {
+  const char* fn = "tp_attn_fwd_train";
+  TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  TRY(check_dims(fn, b * s, h, 3 * n_heads_local * d_head));
+  if (b * s == 0) return ok();
+  TRY(check_ptr(fn, "X", X));
+  TRY(check_ptr(fn, "Wqkv_i", Wqkv_i));
+  TRY(check_ptr(fn, "Wo_i", Wo_i));
+  TRY(check_ptr(fn, "out_partial", out_partial));
+  TRY(check_ptr(fn, "QKV", QKV));
+  TRY(check_ptr(fn, "O", O));
+  TRY(check_ptr(fn, "lse", lse));
+  const int64_t M = b * s, w = n_heads_local * d_head;
+  hipStream_t st = as_stream(stream);
+  {
+    tps::GemmArgs g = make_args(X, h, Wqkv_i, 3 * w, M, 3 * w, h, QKV, 3 * w);
+    TRY(hip_status(tps::gemm_bf16(g, true, false, tps::EPI_BF16, st), fn));
+  }
+  TRY(hip_status(tps::attn_fwd(static_cast<const uint16_t*>(QKV), static_cast<uint16_t*>(O), (int)b, (int)s,
+                               (int)n_heads_local, (int)d_head, causal != 0, st, lse),
+                 fn));
+  {
+    tps::GemmArgs g = make_args(O, w, Wo_i, h, M, h, w, out_partial, h);
+    TRY(hip_status(tps::gemm_bf16(g, true, false, tps::EPI_F32, st), fn));
+  }
+  return ok();
+}
+
+TP_API size_t tp_attn_core_bwd_workspace(int64_t b, int64_t s, int64_t n_heads_local) {
+  if (b < 0 || s < 0 || n_heads_local < 0) return 0;
+  return round256((size_t)b * (size_t)s * (size_t)n_heads_local * 4);
+}
+
+TP_API tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
+                                  const void* QKV, const void* O, const void* dO, const float* lse, void* dQKV,
+                                  void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "tp_attn_core_bwd";
+  TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  if (b * s == 0) return ok();
+  TRY(check_ptr(fn, "QKV", QKV));
+  TRY(check_ptr(fn, "O", O));
+  TRY(check_ptr(fn, "dO", dO));
+  TRY(check_ptr(fn, "lse", lse));
+  TRY(check_ptr(fn, "dQKV", dQKV));
+  const size_t need = tp_attn_core_bwd_workspace(b, s, n_heads_local);
+  if (!ws || ws_bytes < need)
+    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
+                ws ? "" : " (NULL)");
+  TRY(check_ptr(fn, "ws", ws));
+  return hip_status(tps::attn_bwd(static_cast<const uint16_t*>(QKV), static_cast<const uint16_t*>(O),
+                                  static_cast<const uint16_t*>(dO), lse, static_cast<uint16_t*>(dQKV),
+                                  static_cast<float*>(ws), (int)b, (int)s, (int)n_heads_local, (int)d_head,
+                                  causal != 0, as_stream(stream)),
+                    fn);
+}
+
+TP_API size_t tp_attn_bwd_workspace(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head) {
+  (void)h;
+  if (b < 0 || s < 0 || n_heads_local < 0 || d_head < 0) return 0;
+  const size_t t = (size_t)b * (size_t)s, w = (size_t)n_heads_local * (size_t)d_head;
+  return round256(t * w * 2) + round256(t * 3 * w * 2) + tp_attn_core_bwd_workspace(b, s, n_heads_local);
+}
+
+TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head, int causal,
+                             const void* X, const void* Wqkv_i, const void* Wo_i, const void* QKV, const void* O,
+                             const float* lse, const void* dOut, float* dX_i, float* dWqkv_i, float* dWo_i, void* ws,
+                             size_t ws_bytes, void* stream) {
+  const char* fn = "tp_attn_bwd";
+  TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  TRY(check_dims(fn, b * s, h, 3 * n_heads_local * d_head));
+  TRY(check_ptr(fn, "dWqkv_i", dWqkv_i));
+  TRY(check_ptr(fn, "dWo_i", dWo_i));
+  const int64_t M = b * s, w = n_heads_local * d_head;
+  if (M > 0) {
+    TRY(check_ptr(fn, "X", X));
+    TRY(check_ptr(fn, "Wqkv_i", Wqkv_i));
+    TRY(check_ptr(fn, "Wo_i", Wo_i));
+    TRY(check_ptr(fn, "QKV", QKV));
+    TRY(check_ptr(fn, "O", O));
+    TRY(check_ptr(fn, "lse", lse));
+    TRY(check_ptr(fn, "dOut", dOut));
+    TRY(check_ptr(fn, "dX_i", dX_i));
+  }
+  const size_t need = tp_attn_bwd_workspace(b, s, h, n_heads_local, d_head);
+  if (need && (!ws || ws_bytes < need))
+    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
+                ws ? "" : " (NULL)");
+  TRY(check_opt_ptr(fn, "ws", ws));
+  hipStream_t st = as_stream(stream);
+  char* wsb = static_cast<char*>(ws);
+  uint16_t* dO = reinterpret_cast<uint16_t*>(wsb);
+  uint16_t* dqkv = reinterpret_cast<uint16_t*>(wsb + round256((size_t)M * w * 2));
+  float* Dws = reinterpret_cast<float*>(wsb + round256((size_t)M * w * 2) + round256((size_t)M * 3 * w * 2));
+  {  // dWo_i = O^T dOut: A(m,k) = O[k, m], B(k,n) = dOut[k, n]
+    tps::GemmArgs g = make_args(O, w, dOut, h, w, h, M, dWo_i, h);
+    TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, st), fn));
+  }
+  if (M > 0) {
+    {  // dO = dOut Wo_i^T: A = dOut [M,h] (K-contig), B(k,n) = Wo_i[n, k] (K-contig)
+      tps::GemmArgs g = make_args(dOut, h, Wo_i, h, M, w, h, dO, w);
+      TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_BF16, st), fn));
+    }
+    TRY(hip_status(tps::attn_bwd(static_cast<const uint16_t*>(QKV), static_cast<const uint16_t*>(O), dO, lse, dqkv,
+                                 Dws, (int)b, (int)s, (int)n_heads_local, (int)d_head, causal != 0, st),
+                   fn));
+  }
+  {  // dWqkv_i = X^T dQKV: A(m,k) = X[k, m], B(k,n) = dQKV[k, n]
+    tps::GemmArgs g = make_args(X, h, dqkv, 3 * w, h, 3 * w, M, dWqkv_i, 3 * w);
+    TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, st), fn));
+  }
+  if (M > 0) {  // dX_i = dQKV Wqkv_i^T: A = dQKV [M,3w] (K-contig), B(k,n) = Wqkv_i[n, k] (K-contig)
+    tps::GemmArgs g = make_args(dqkv, 3 * w, Wqkv_i, 3 * w, M, h, 3 * w, dX_i, h);
+    TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_F32, st), fn));
   }
   return ok();
 }

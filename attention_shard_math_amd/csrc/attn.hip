@@ -74,7 +74,8 @@ __device__ __forceinline__ int swz_v(int d) { return (d ^ (d >> 3)) & 7; }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ O, int s,
-                                                      int Hl, int nqb, int per_xcd, int n_items, float scale_log2) {
+                                                      int Hl, int nqb, int per_xcd, int n_items, float scale_log2,
+                                                      float* __restrict__ lse) {
   constexpr int DCH = D / 8;                // 16-byte chunks per K row
   constexpr int KS = D / 16;                // k-steps of S^T over d
   constexpr int DT = D / 32;                // O^T tiles along d
@@ -290,7 +291,13 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
 
   if (qrow < s) {
     const int ln = opaque(lane), lr2 = ln & 31, hh2 = ln >> 5;
-    const float inv = 1.f / xhalf_sum(l_i);
+    const float lsum = xhalf_sum(l_i);
+    const float inv = 1.f / lsum;
+    if (lse && hh2 == 0) {
+      // natural-log log-sum-exp of the row's scaled scores: (m + log2 l) * ln 2
+      const float mref = m_i == kNegInf ? 0.f : m_i;
+      lse[((int64_t)bi * Hl + head) * s + qw + lr2] = (mref + __log2f(lsum)) * 0.69314718055994531f;
+    }
     uint16_t* orow = O + ((int64_t)bi * s + qw + lr2) * ((int64_t)Hl * D) + (int64_t)head * D;
     // O^T accumulator lane (lr, hh), reg e of tile i: d = 32i + 8(e/4) + 4hh + e%4.
 #pragma unroll
@@ -306,7 +313,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
 }
 
 template <int D, bool C>
-hipError_t launch_attn(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, hipStream_t st) {
+hipError_t launch_attn(const uint16_t* qkv, uint16_t* O, float* lse, int b, int s, int Hl, hipStream_t st) {
   const int nqb = (s + AQ - 1) / AQ;
   const int64_t items = (int64_t)b * Hl * nqb;
   if (items == 0) return hipSuccess;
@@ -315,15 +322,18 @@ hipError_t launch_attn(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, h
   const int per_xcd = (int)((items + 7) / 8);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
   hipLaunchKernelGGL((attn_fwd_kernel<D, C>), dim3(8u * per_xcd), dim3(NT), 0, st, qkv, O, s, Hl, nqb, per_xcd,
-                     (int)items, scale_log2);
+                     (int)items, scale_log2, lse);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t attn_fwd(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, int d, bool causal, hipStream_t st) {
-  if (d == 128) return causal ? launch_attn<128, true>(qkv, O, b, s, Hl, st) : launch_attn<128, false>(qkv, O, b, s, Hl, st);
-  if (d == 64) return causal ? launch_attn<64, true>(qkv, O, b, s, Hl, st) : launch_attn<64, false>(qkv, O, b, s, Hl, st);
+hipError_t attn_fwd(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, int d, bool causal, hipStream_t st,
+                    float* lse) {
+  if (d == 128)
+    return causal ? launch_attn<128, true>(qkv, O, lse, b, s, Hl, st) : launch_attn<128, false>(qkv, O, lse, b, s, Hl, st);
+  if (d == 64)
+    return causal ? launch_attn<64, true>(qkv, O, lse, b, s, Hl, st) : launch_attn<64, false>(qkv, O, lse, b, s, Hl, st);
   return hipErrorInvalidValue;
 }
 

@@ -157,6 +157,46 @@ size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_
 tp_status tp_vocab_embed(const int32_t* ids, int64_t n_tokens, const void* E_i,
                          int64_t lo, int64_t hi, int64_t h, void* out, void* stream);
 
+/* tp_attn_core that also writes the per-query log-sum-exp the backward needs:
+ *   lse float32 [b, Hl, s] = log sum_u exp(q.k_u / sqrt(d)) over the visible keys. */
+tp_status tp_attn_core_train(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
+                             const void* QKV, void* O, float* lse, void* stream);
+
+/* Training forward of the attention shard: as tp_attn_fwd, but Q|K|V, the head
+ * outputs O and the per-query log-sum-exp go to caller buffers, kept for the backward.
+ *   QKV bf16 [b*s, 3*Hl*d], O bf16 [b*s, Hl*d], lse float32 [b, Hl, s]:
+ *   lse = log sum_u exp(q.k_u / sqrt(d)) over the visible keys (natural log). */
+tp_status tp_attn_fwd_train(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head,
+                            int causal, const void* X, const void* Wqkv_i, const void* Wo_i,
+                            float* out_partial, void* QKV, void* O, float* lse, void* stream);
+
+/* Attention core backward over the local heads [m.youleyou.com/wenzhang/3143730,
+ * 三、Self-Attention层 §3.2 (the layer's backward, per head, then the input
+ * gradient's all-reduce); the head formula as in tp_attn_core]:
+ *   P = exp(q.k / sqrt(d) - lse), dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO*O)),
+ *   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d); written as bf16 dQKV [b*s, 3*Hl*d] in the
+ *   [Q | K | V] layout of QKV. dO bf16 [b*s, Hl*d]; lse from tp_attn_fwd_train.
+ *   Deterministic (no atomics). ws: tp_attn_core_bwd_workspace(b, s, Hl) bytes. */
+tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
+                           const void* QKV, const void* O, const void* dO, const float* lse,
+                           void* dQKV, void* ws, size_t ws_bytes, void* stream);
+size_t tp_attn_core_bwd_workspace(int64_t b, int64_t s, int64_t n_heads_local);
+
+/* Backward of one rank's attention shard [same page, 三、§3.2; "Megatron-LM：张量并行与
+ * 大规模训练" §2.2]: with dOut bf16 [b*s, h] (replicated, the output all-reduce's
+ * backward is the identity):
+ *   dWo_i = O^T dOut (float32 [Hl*d, h]), dO = dOut Wo_i^T (bf16, workspace),
+ *   dQKV = core backward (bf16, workspace), dWqkv_i = X^T dQKV (float32 [h, 3*Hl*d]),
+ *   dX_i = dQKV Wqkv_i^T (float32 [b*s, h], the partial the input all-reduce adds).
+ *   QKV, O, lse: saved by tp_attn_fwd_train. ws: tp_attn_bwd_workspace(...) bytes. */
+tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head,
+                      int causal, const void* X, const void* Wqkv_i, const void* Wo_i,
+                      const void* QKV, const void* O, const float* lse, const void* dOut,
+                      float* dX_i, float* dWqkv_i, float* dWo_i, void* ws, size_t ws_bytes,
+                      void* stream);
+size_t tp_attn_bwd_workspace(int64_t b, int64_t s, int64_t h, int64_t n_heads_local,
+                             int64_t d_head);
+
 /* Vocabulary-parallel output layer + cross-entropy, one rank's part
  * [m.youleyou.com/wenzhang/3143730, 四、Embedding层 §4.2 (the output layer maps
  *  back to the vocabulary with the row-split word embedding) and 五、Cross-Entropy层

@@ -89,6 +89,30 @@ class TestValidation:
         assert lib.tp_attn_fwd(2, 100, 256, 3, 64, 1, P, P, P, P, P, ws - 16, None) == WORKSPACE
         assert lib.tp_attn_fwd(2, 100, 260, 3, 64, 1, P, P, P, P, P, ws, None) == UNSUPPORTED  # h % 8
 
+    def test_attention_backward(self):
+        ws = lib.tp_attn_core_bwd_workspace(2, 100, 3)
+        assert ws == 2 * 100 * 3 * 4 + (-(2 * 100 * 3 * 4) % 256)
+        cb = lib.tp_attn_core_bwd
+        assert cb(1, 16, 2, 96, 1, P, P, P, P, P, P, ws, None) == UNSUPPORTED       # d_head
+        assert cb(1, 16, 2, 128, 1, P, P, None, P, P, P, ws, None) == INVALID      # dO NULL
+        assert cb(1, 16, 2, 128, 1, P, P, P, None, P, P, ws, None) == INVALID      # lse NULL
+        assert cb(1, 16, 2, 128, 1, P, P, P, P, P, P, 16 * 2 * 4 - 4, None) == WORKSPACE
+        assert cb(1, 16, 2, 128, 1, P, MIS, P, P, P, P, 256, None) == UNSUPPORTED
+        assert cb(0, 16, 2, 128, 1, None, None, None, None, None, None, 0, None) == OK
+        need = lib.tp_attn_bwd_workspace(1, 64, 256, 2, 64)
+        t, w = 64, 128
+        assert need == -(-t * w * 2 // 256) * 256 + -(-t * 3 * w * 2 // 256) * 256 + lib.tp_attn_core_bwd_workspace(1, 64, 2)
+        b = lib.tp_attn_bwd
+        args = [P] * 10  # X, Wqkv_i, Wo_i, QKV, O, lse, dOut, dX_i, dWqkv_i, dWo_i
+        assert b(1, 64, 256, 2, 64, 1, *args, P, need - 1, None) == WORKSPACE
+        assert b(1, 64, 260, 2, 64, 1, *args, P, need, None) == UNSUPPORTED           # h % 8
+        assert b(1, 64, 256, 2, 64, 1, *args[:9], None, P, need, None) == INVALID  # dWo NULL
+        assert b(1, 64, 256, 2, 64, 1, *args[:6], None, *args[7:], P, need, None) == INVALID  # dOut NULL
+        f = lib.tp_attn_fwd_train
+        assert f(1, 64, 256, 2, 64, 1, P, P, P, P, P, P, None, None) == INVALID     # lse NULL
+        assert f(1, 64, 256, 2, 96, 1, P, P, P, P, P, P, P, None) == UNSUPPORTED
+        assert f(0, 64, 256, 2, 64, 1, None, None, None, None, None, None, None, None) == OK
+
     def test_vocab_embed(self):
         e = lib.tp_vocab_embed
         assert e(P, 4, P, 10, 10, 8, P, None) == INVALID   # lo == hi
