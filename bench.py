@@ -51,7 +51,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing leg")
     p.add_argument("--no-next", action="store_true",
                    help="skip the extra rows timed after the step (PaLM-shaped MLP with recompute, "
-                        "cross-entropy, sequence parallelism)")
+                        "cross-entropy, attention backward, sequence parallelism)")
     p.add_argument("--copy-probe", action="store_true",
                    help="after the timed steps, run a plain 256 MiB device-to-device copy three times, "
                         "the calibration kernel for HBM byte counters")
@@ -112,8 +112,9 @@ def next_rows(tp, torch, dev, randn, reps=5):
     """Rows beyond the step, timed on their own after it: the PaLM-shaped MLP shard
     (M=2048, h=18432, f=9216), forward with saved U, backward with activation
     recompute (U, Y formed again from X and A_i inside mlp_bwd); the
-    vocabulary-parallel output layer + cross-entropy of one rank; and the
-    sequence-parallel LayerNorm, all-gather and reduce-scatter of one rank."""
+    vocabulary-parallel output layer + cross-entropy of one rank; the attention
+    backward (core, and the whole shard); and the sequence-parallel LayerNorm,
+    all-gather and reduce-scatter of one rank."""
     Mp, Hp, Fp = 2048, 18432, 9216
     X = randn((Mp, Hp), 1.0, 40)
     A = randn((Hp, Fp), 0.005, 41)
@@ -182,6 +183,48 @@ def next_rows(tp, torch, dev, randn, reps=5):
             rec.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
         out[name] = rec
     del Hh, E, tg, sums, tls, ws, rows, tot
+    torch.cuda.empty_cache()
+
+    # Attention backward at the GPT-3 shard (12 heads x 128, s = 2048, h = 12288):
+    # the core alone and the whole shard (Wo, Wqkv and input-gradient GEMMs).
+    Ha, Hla, Da, Sa = 12288, 12, 128, 2048
+    wa = Hla * Da
+    Xa = randn((Sa, Ha), 1.0, 80)
+    Wqkv = randn((Ha, 3 * wa), 0.006, 81)
+    Wo = randn((wa, Ha), 0.006, 82)
+    dOut = randn((Sa, Ha), 1.0, 83)
+    outp = torch.empty(Sa, Ha, dtype=torch.float32, device=dev)
+    QKV = torch.empty(Sa, 3 * wa, dtype=torch.bfloat16, device=dev)
+    Oa = torch.empty(Sa, wa, dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(1, Hla, Sa, dtype=torch.float32, device=dev)
+    tp.attn_fwd_train(Xa, Wqkv, Wo, outp, QKV, Oa, lse, 1, Sa, Hla, Da, True)
+    dOa = randn((Sa, wa), 1.0, 84)
+    dQKV = torch.empty_like(QKV)
+    wsc = torch.empty(tp.attn_core_bwd_workspace(1, Sa, Hla), dtype=torch.uint8, device=dev)
+    dXa = torch.empty(Sa, Ha, dtype=torch.float32, device=dev)
+    dWqkv = torch.empty(Ha, 3 * wa, dtype=torch.float32, device=dev)
+    dWo = torch.empty(wa, Ha, dtype=torch.float32, device=dev)
+    wsb = torch.empty(tp.attn_bwd_workspace(1, Sa, Ha, Hla, Da), dtype=torch.uint8, device=dev)
+    core_gflop = 5 * 2 * Da * Hla * Sa * (Sa + 1) / 2 / 1e9  # dV, dP, dQ, dK + the S recompute, causal pairs
+    shard_gflop = core_gflop + (2 * gemm_flops(Sa, wa, Ha) + 2 * gemm_flops(Sa, 3 * wa, Ha)) / 1e9
+    for name, fn, gf in (
+            ("attn_core_bwd", lambda: tp.attn_core_bwd(QKV, Oa, dOa, lse, dQKV, wsc, 1, Sa, Hla, Da, True), core_gflop),
+            ("attn_shard_bwd", lambda: tp.attn_bwd(Xa, Wqkv, Wo, QKV, Oa, lse, dOut, dXa, dWqkv, dWo, wsb, 1, Sa,
+                                                   Hla, Da, True), shard_gflop)):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = gf * 1e9 / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "gflop": round(gf, 2), "tflops": round(tf, 1),
+                     "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del Xa, Wqkv, Wo, dOut, outp, QKV, Oa, lse, dOa, dQKV, wsc, dXa, dWqkv, dWo, wsb
     torch.cuda.empty_cache()
 
     # Sequence parallelism at the GPT-3 shard: one rank's LayerNorm over its 256
