@@ -6,13 +6,16 @@
 // Three launches:
 //   * attn_bwd_rowdot — D per (query, head), 16 lanes per row of 128;
 //   * attn_bwd_dkdv   — one workgroup per (sequence, head, block of 32*NW keys),
-//     wave w owning 32 keys; it walks the query blocks of 32 that can see its
-//     keys, with the block's Q and dO staged in LDS (double-buffered) and shared
-//     by the waves; dK and dV stay in registers;
+//     wave w owning 32 keys (their K and V fragments, dK and dV in registers);
+//     it walks the query blocks of 32 that can see its keys, with each block's Q
+//     and dO staged in LDS (double-buffered) and shared by the waves;
 //   * attn_bwd_dq     — one workgroup per (sequence, head, block of 32*NW
 //     queries), wave w owning 32 queries whose Q and dO fragments sit in
 //     registers; it walks the key blocks of 32 up to the diagonal, K and V
 //     staged in LDS.
+// The staged tiles are loaded into registers two steps ahead of their use (two
+// register sets, the loop unrolled by two), so a step's compute covers the
+// global-load latency of the tile after next.
 // Both big kernels run their products on v_mfma_f32_32x32x16_bf16. The score
 // tile comes out of the MFMA with a lane owning one column and 16 rows
 // {8(e/4) + 4(l/32) + e%4}; those 16 values (8 per 16-row k-slice, packed to
@@ -26,6 +29,7 @@
 // 16-row ds_read_b128 fragment reads and for the 4-row x 2-chunk transposing reads.
 #include "attn.hpp"
 #include "common.hpp"
+
 
 namespace tps {
 namespace {
@@ -167,24 +171,26 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
   }
   const int qstart = CAUSAL ? k0 : 0;  // query blocks of 32 from the diagonal
   const int nq = (s - qstart + 31) / 32;
-  u32x4 rq[QP], rdo[QP];
-  float rl = 0.f, rd = 0.f;
-  auto fetch = [&](int q0) __attribute__((always_inline)) {
-    load_rows<D, 32, NTH>(rq, Qg, ld, q0, s, tid);
-    load_rows<D, 32, NTH>(rdo, dOg, ldo, q0, s, tid);
-    if (tid < 32) rl = (q0 + tid < s) ? lseg[q0 + tid] * kLog2e : __builtin_inff();
-    else if (tid < 64) rd = (q0 + tid - 32 < s) ? Dg[q0 + tid - 32] : 0.f;
+  struct Tile {
+    u32x4 q[QP], o[QP];
+    float l, d;
   };
-  auto put = [&](int buf) __attribute__((always_inline)) {
-    store_rows<D, 32, NTH>(rq, sQ[buf], tid);
-    store_rows<D, 32, NTH>(rdo, sdO[buf], tid);
-    if (tid < 32) sL[buf][tid] = rl;
-    else if (tid < 64) sDv[buf][tid - 32] = rd;
+  Tile t0, t1;
+  auto fetch = [&](Tile& t, int q0) __attribute__((always_inline)) {
+    load_rows<D, 32, NTH>(t.q, Qg, ld, q0, s, tid);
+    load_rows<D, 32, NTH>(t.o, dOg, ldo, q0, s, tid);
+    if (tid < 32) t.l = (q0 + tid < s) ? lseg[q0 + tid] * kLog2e : __builtin_inff();
+    else if (tid < 64) t.d = (q0 + tid - 32 < s) ? Dg[q0 + tid - 32] : 0.f;
   };
-  if (nq > 0) {
-    fetch(qstart);
-    put(0);
-  }
+  auto put = [&](const Tile& t, int buf) __attribute__((always_inline)) {
+    store_rows<D, 32, NTH>(t.q, sQ[buf], tid);
+    store_rows<D, 32, NTH>(t.o, sdO[buf], tid);
+    if (tid < 32) sL[buf][tid] = t.l;
+    else if (tid < 64) sDv[buf][tid - 32] = t.d;
+  };
+  if (nq > 0) fetch(t0, qstart);
+  if (nq > 1) fetch(t1, qstart + 32);
+  if (nq > 0) put(t0, 0);
   __syncthreads();
 
   f32x16 dk[DT], dv[DT];
@@ -192,11 +198,19 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
   for (int i = 0; i < DT; ++i)
 #pragma unroll
     for (int e = 0; e < 16; ++e) dk[i][e] = dv[i][e] = 0.f;
+  // This wave's 32 keys as the other operand of S and dP, for the whole walk.
+  bf16x8 kfr[KS], vfr[KS];
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    kfr[kk] = frag_rows<D>(sK, 32 * wave, kk, lane);
+    vfr[kk] = frag_rows<D>(sV, 32 * wave, kk, lane);
+  }
 
-  for (int j = 0; j < nq; ++j) {
+  // cur holds query block j+1 (stored to LDS at the end of the step); nxt is
+  // free and receives block j+2.
+  auto step = [&](int j, Tile& cur, Tile& nxt) __attribute__((always_inline)) {
     const int q0 = qstart + 32 * j, buf = j & 1;
-    if (j + 1 < nq) fetch(q0 + 32);
-    // A wave whose keys all lie past the block's last query sees nothing (causal).
+    if (j + 2 < nq) fetch(nxt, q0 + 64);
     if (!(CAUSAL && kw > q0 + 31)) {
       const uint16_t* tq = sQ[buf];
       const uint16_t* td = sdO[buf];
@@ -205,13 +219,9 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
       for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        // S[q][key] = Q K^T, dP[q][key] = dO V^T over d
-        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(tq, 0, kk, lane), frag_rows<D>(sK, 32 * wave, kk, lane),
-                                                    S, 0, 0, 0);
-        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(td, 0, kk, lane),
-                                                     frag_rows<D>(sV, 32 * wave, kk, lane), dP, 0, 0, 0);
+        S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(tq, 0, kk, lane), kfr[kk], S, 0, 0, 0);
+        dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(td, 0, kk, lane), vfr[kk], dP, 0, 0, 0);
       }
-      // lane: key kw + lr; register e: query q0 + 8(e/4) + 4hh + e%4
       const int key = kw + lr;
       float p[16], ds[16];
 #pragma unroll
@@ -238,8 +248,12 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
           dk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], frag_tr<D>(tq, 16 * t, 32 * i, lane), dk[i], 0, 0, 0);
         }
     }
-    if (j + 1 < nq) put(buf ^ 1);
+    if (j + 1 < nq) put(cur, buf ^ 1);
     __syncthreads();
+  };
+  for (int j = 0; j < nq; j += 2) {
+    step(j, t1, t0);
+    if (j + 1 < nq) step(j + 1, t0, t1);
   }
 
   // accumulator lane: d column 32i + lr; register e: key kw + 8(e/4) + 4hh + e%4
@@ -294,12 +308,18 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
 
   const int kend = CAUSAL ? min(s, q0 + QB) : s;
   const int nk = (kend + 31) / 32;
-  u32x4 rk[KP], rv[KP];
+  u32x4 rk0[KP], rv0[KP], rk1[KP], rv1[KP];
   if (nk > 0) {
-    load_rows<D, 32, NTH>(rk, Kg, ld, 0, s, tid);
-    load_rows<D, 32, NTH>(rv, Vg, ld, 0, s, tid);
-    store_rows<D, 32, NTH>(rk, sK[0], tid);
-    store_rows<D, 32, NTH>(rv, sV[0], tid);
+    load_rows<D, 32, NTH>(rk0, Kg, ld, 0, s, tid);
+    load_rows<D, 32, NTH>(rv0, Vg, ld, 0, s, tid);
+  }
+  if (nk > 1) {
+    load_rows<D, 32, NTH>(rk1, Kg, ld, 32, s, tid);
+    load_rows<D, 32, NTH>(rv1, Vg, ld, 32, s, tid);
+  }
+  if (nk > 0) {
+    store_rows<D, 32, NTH>(rk0, sK[0], tid);
+    store_rows<D, 32, NTH>(rv0, sV[0], tid);
   }
   __syncthreads();
 
@@ -309,11 +329,14 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
 #pragma unroll
     for (int e = 0; e < 16; ++e) dq[i][e] = 0.f;
 
-  for (int j = 0; j < nk; ++j) {
+  // ck/cv hold key block j+1 (stored to LDS at the end of the step); fk/fv are
+  // free and receive block j+2, two steps ahead of its use.
+  auto step = [&](int j, u32x4 (&ck)[KP], u32x4 (&cv)[KP], u32x4 (&fk)[KP], u32x4 (&fv)[KP])
+      __attribute__((always_inline)) {
     const int k0 = 32 * j, buf = j & 1;
-    if (j + 1 < nk) {
-      load_rows<D, 32, NTH>(rk, Kg, ld, k0 + 32, s, tid);
-      load_rows<D, 32, NTH>(rv, Vg, ld, k0 + 32, s, tid);
+    if (j + 2 < nk) {
+      load_rows<D, 32, NTH>(fk, Kg, ld, k0 + 64, s, tid);
+      load_rows<D, 32, NTH>(fv, Vg, ld, k0 + 64, s, tid);
     }
     if (!(CAUSAL && k0 > qw + 31)) {
       const uint16_t* tk = sK[buf];
@@ -323,11 +346,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
       for (int e = 0; e < 16; ++e) S[e] = dP[e] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk) {
-        // S^T[key][q] = K Q^T, dP^T[key][q] = V dO^T over d
         S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(tk, 0, kk, lane), qf[kk], S, 0, 0, 0);
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(tv, 0, kk, lane), of[kk], dP, 0, 0, 0);
       }
-      // lane: query qrow; register e: key k0 + 8(e/4) + 4hh + e%4
       float ds[16];
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -337,8 +358,6 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
         ds[e] = pv * (dP[e] - Dq);
       }
       const bf16x8 sa[2] = {pack8(ds), pack8(ds + 8)};
-      // dQ^T[d][q] = K^T dS^T: the k-operand is dS^T from registers (lane = query
-      // column, keys in the score order), the other K^T read transposed.
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -346,10 +365,14 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
           dq[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(tk, 16 * t, 32 * i, lane), sa[t], dq[i], 0, 0, 0);
     }
     if (j + 1 < nk) {
-      store_rows<D, 32, NTH>(rk, sK[buf ^ 1], tid);
-      store_rows<D, 32, NTH>(rv, sV[buf ^ 1], tid);
+      store_rows<D, 32, NTH>(ck, sK[buf ^ 1], tid);
+      store_rows<D, 32, NTH>(cv, sV[buf ^ 1], tid);
     }
     __syncthreads();
+  };
+  for (int j = 0; j < nk; j += 2) {
+    step(j, rk1, rv1, rk0, rv0);
+    if (j + 1 < nk) step(j + 1, rk0, rv0, rk1, rv1);
   }
 
   // dQ^T accumulator lane: query column qrow; register e of tile i: d = 32i + 8(e/4) + 4hh + e%4
