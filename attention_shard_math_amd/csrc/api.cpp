@@ -346,8 +346,10 @@ TP_API tp_status tp_attn_fwd_train(int64_t b, int64_t s, int64_t h, int64_t n_he
 }
 
 TP_API size_t tp_attn_core_bwd_workspace(int64_t b, int64_t s, int64_t n_heads_local) {
-  if (b < 0 || s < 0 || n_heads_local < 0) return 0;
-  return round256((size_t)b * (size_t)s * (size_t)n_heads_local * 4);
+  if (b <= 0 || s <= 0 || n_heads_local <= 0) return 0;
+  if (b * s > kMaxDim || n_heads_local > kMaxDim) return 0;
+  // sized for the largest head dimension (128), so one figure serves both
+  return tps::attn_bwd_workspace((int)b, (int)s, (int)n_heads_local, 128);
 }
 
 TP_API tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
@@ -367,8 +369,8 @@ TP_API tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, i
                 ws ? "" : " (NULL)");
   TRY(check_ptr(fn, "ws", ws));
   return hip_status(tps::attn_bwd(static_cast<const uint16_t*>(QKV), static_cast<const uint16_t*>(O),
-                                  static_cast<const uint16_t*>(dO), lse, static_cast<uint16_t*>(dQKV),
-                                  static_cast<float*>(ws), (int)b, (int)s, (int)n_heads_local, (int)d_head,
+                                  static_cast<const uint16_t*>(dO), lse, static_cast<uint16_t*>(dQKV), ws, (int)b,
+                                  (int)s, (int)n_heads_local, (int)d_head,
                                   causal != 0, as_stream(stream)),
                     fn);
 }
@@ -409,7 +411,7 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   char* wsb = static_cast<char*>(ws);
   uint16_t* dO = reinterpret_cast<uint16_t*>(wsb);
   uint16_t* dqkv = reinterpret_cast<uint16_t*>(wsb + round256((size_t)M * w * 2));
-  float* Dws = reinterpret_cast<float*>(wsb + round256((size_t)M * w * 2) + round256((size_t)M * 3 * w * 2));
+  void* core_ws = wsb + round256((size_t)M * w * 2) + round256((size_t)M * 3 * w * 2);
   {  // dWo_i = O^T dOut: A(m,k) = O[k, m], B(k,n) = dOut[k, n]
     tps::GemmArgs g = make_args(O, w, dOut, h, w, h, M, dWo_i, h);
     TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, st), fn));
@@ -420,7 +422,7 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
       TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_BF16, st), fn));
     }
     TRY(hip_status(tps::attn_bwd(static_cast<const uint16_t*>(QKV), static_cast<const uint16_t*>(O), dO, lse, dqkv,
-                                 Dws, (int)b, (int)s, (int)n_heads_local, (int)d_head, causal != 0, st),
+                                 core_ws, (int)b, (int)s, (int)n_heads_local, (int)d_head, causal != 0, st),
                    fn));
   }
   {  // dWqkv_i = X^T dQKV: A(m,k) = X[k, m], B(k,n) = dQKV[k, n]

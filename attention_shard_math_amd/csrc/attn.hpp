@@ -11,7 +11,9 @@ hipError_t attn_fwd(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, int 
                     float* lse = nullptr);
 
 // Backward of attn_fwd over the same layout: dQKV bf16 [b*s, 3*Hl*d] from qkv, O,
-// dO bf16 [b*s, Hl*d] and lse. Dws: float32 [b*Hl*s] scratch for rowsum(dO*O).
+// dO bf16 [b*s, Hl*d] and lse. ws: attn_bwd_workspace(b, s, Hl, d) bytes of
+// scratch (rowsum(dO*O) and the fp32 partials of split walks).
+size_t attn_bwd_workspace(int b, int s, int Hl, int d);
 hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO, const float* lse, uint16_t* dqkv,
-                    float* Dws, int b, int s, int Hl, int d, bool causal, hipStream_t st);
+                    void* ws, int b, int s, int Hl, int d, bool causal, hipStream_t st);
 }  // namespace tps

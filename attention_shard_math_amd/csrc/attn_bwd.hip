@@ -16,6 +16,7 @@
 // The staged tiles are loaded into registers two steps ahead of their use (two
 // register sets, the loop unrolled by two), so a step's compute covers the
 // global-load latency of the tile after next.
+// The two walks are cut into chunks for causal balance (see combine_kernel).
 // Both big kernels run their products on v_mfma_f32_32x32x16_bf16. The score
 // tile comes out of the MFMA with a lane owning one column and 16 rows
 // {8(e/4) + 4(l/32) + e%4}; those 16 values (8 per 16-row k-slice, packed to
@@ -132,13 +133,78 @@ __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict_
   }
 }
 
+// ------------------------------------------------------------------ causal balance
+// A block's walk of n steps (32 rows each) is cut into ceil(n / C) chunks of at
+// most C steps, each run by its own workgroup, so the diagonal blocks' long walks
+// no longer set the kernel's length. A chunk of a block that has several writes
+// its fp32 partial to a workspace slot; combine_kernel adds a block's partials in
+// chunk order afterwards (deterministic). C is chosen so that no block has more
+// than kMaxChunks chunks.
+constexpr int kMaxChunks = 4;
+
+// Steps of key block kb's walk over query blocks (dK, dV).
+template <bool CAUSAL>
+__device__ __host__ __forceinline__ int kv_steps(int kb, int KB, int s) {
+  return (s - (CAUSAL ? kb * KB : 0) + 31) / 32;
+}
+// Steps of query block qb's walk over key blocks (dQ).
+template <bool CAUSAL>
+__device__ __host__ __forceinline__ int q_steps(int qb, int QB, int s) {
+  return ((CAUSAL ? min(s, (qb + 1) * QB) : s) + 31) / 32;
+}
+
+// Rank r of a head's chunks (0 = the heaviest block's first chunk) -> (block, chunk).
+template <bool CAUSAL, bool QSIDE>
+__device__ __forceinline__ void chunk_of(int r, int nblk, int R, int s, int C, int& blk, int& c) {
+  for (int i = 0; i < nblk; ++i) {
+    const int b = QSIDE ? nblk - 1 - i : i;  // causal: the last query block / first key block is heaviest
+    const int n = (QSIDE ? q_steps<CAUSAL>(b, R, s) : kv_steps<CAUSAL>(b, R, s));
+    const int nc = (n + C - 1) / C;
+    if (r < nc) {
+      blk = b;
+      c = r;
+      return;
+    }
+    r -= nc;
+  }
+  blk = -1;
+  c = 0;
+}
+
+// out[row, col0 + d] = bf16(scale * sum_c part[c][row][d]) for every block with
+// more than one chunk. part slots: [bh][blk][kMaxChunks][R][D] float32.
+template <int D, bool CAUSAL, bool QSIDE>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
+                                                      int s, int Hl, int nblk, int R, int C, int col_block,
+                                                      float scale) {
+  const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
+  const int n = QSIDE ? q_steps<CAUSAL>(blk, R, s) : kv_steps<CAUSAL>(blk, R, s);
+  const int nc = (n + C - 1) / C;
+  if (nc <= 1) return;
+  const int bi = bh / Hl, head = bh % Hl;
+  const int64_t ld = 3LL * Hl * D;
+  const float* pb = part + ((int64_t)bh * nblk + blk) * kMaxChunks * R * D;
+  for (int v = blockIdx.y * 256 + threadIdx.x; v < R * D / 4; v += gridDim.y * 256) {
+    const int row = blk * R + (v * 4) / D, d = (v * 4) % D;
+    if (row >= s) continue;
+    f32x4 a = *reinterpret_cast<const f32x4*>(pb + (int64_t)v * 4);
+    for (int c = 1; c < nc; ++c) a = a + *reinterpret_cast<const f32x4*>(pb + (int64_t)c * R * D + v * 4);
+    uint2 u;
+    u.x = cvt2(a[0] * scale, a[1] * scale);
+    u.y = cvt2(a[2] * scale, a[3] * scale);
+    *reinterpret_cast<uint2*>(out + ((int64_t)bi * s + row) * ld + (int64_t)(col_block * Hl + head) * D + d) = u;
+  }
+}
+
 // ------------------------------------------------------------------ dK, dV
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restrict__ qkv,
                                                        const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ lse,
                                                        const float* __restrict__ Dv, uint16_t* __restrict__ dqkv,
-                                                       int s, int Hl, int nkb, float scale_log2, float scale) {
+                                                       float* __restrict__ partK, float* __restrict__ partV, int s,
+                                                       int Hl, int BH, int nkb, int C, float scale_log2,
+                                                       float scale) {
   constexpr int NTH = NW * 64, KB = 32 * NW, KS = D / 16, DT = D / 32;
   constexpr int QP = 32 * D / 8 / NTH;  // 16-byte chunks per thread per 32-row tile
   __shared__ __attribute__((aligned(16))) uint16_t sK[KB * D];
@@ -148,8 +214,11 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
   __shared__ __attribute__((aligned(16))) float sL[2][32];
   __shared__ __attribute__((aligned(16))) float sDv[2][32];
 
-  const int item = blockIdx.x;
-  const int bh = item / nkb, kb = item % nkb;  // key block 0 (the heaviest) first
+  // Chunks of every head, heaviest first: rank r of all heads before rank r + 1.
+  const int bh = blockIdx.x % BH;
+  int kb, chunk;
+  chunk_of<CAUSAL, false>(blockIdx.x / BH, nkb, KB, s, C, kb, chunk);
+  if (kb < 0) return;
   const int bi = bh / Hl, head = bh % Hl;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int64_t ld = 3LL * Hl * D, ldo = (int64_t)Hl * D;
@@ -169,8 +238,10 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
     load_rows<D, KB, NTH>(r, Vg, ld, k0, s, tid);
     store_rows<D, KB, NTH>(r, sV, tid);
   }
-  const int qstart = CAUSAL ? k0 : 0;  // query blocks of 32 from the diagonal
-  const int nq = (s - qstart + 31) / 32;
+  const int nsteps = kv_steps<CAUSAL>(kb, KB, s), nch = (nsteps + C - 1) / C;
+  // this chunk's query blocks of 32 (the walk starts at the diagonal)
+  const int qstart = (CAUSAL ? k0 : 0) + 32 * C * chunk;
+  const int nq = min(C, nsteps - C * chunk);
   struct Tile {
     u32x4 q[QP], o[QP];
     float l, d;
@@ -257,6 +328,21 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
   }
 
   // accumulator lane: d column 32i + lr; register e: key kw + 8(e/4) + 4hh + e%4
+  if (nch > 1) {
+    const int64_t slot = ((int64_t)bh * nkb + kb) * kMaxChunks + chunk;
+    float* pk = partK + slot * KB * D;
+    float* pv = partV + slot * KB * D;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int kr = 32 * wave + 8 * (e >> 2) + 4 * hh + (e & 3);
+#pragma unroll
+      for (int i = 0; i < DT; ++i) {
+        pk[kr * D + 32 * i + lr] = dk[i][e];
+        pv[kr * D + 32 * i + lr] = dv[i][e];
+      }
+    }
+    return;
+  }
   uint16_t* dKg = dqkv + (int64_t)bi * s * ld + (int64_t)(Hl + head) * D;
   uint16_t* dVg = dqkv + (int64_t)bi * s * ld + (int64_t)(2 * Hl + head) * D;
 #pragma unroll
@@ -276,15 +362,17 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
 template <int D, bool CAUSAL, int NW>
 __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
                                                      const float* __restrict__ lse, const float* __restrict__ Dv,
-                                                     uint16_t* __restrict__ dqkv, int s, int Hl, int nqb,
-                                                     float scale_log2, float scale) {
+                                                     uint16_t* __restrict__ dqkv, float* __restrict__ partQ, int s,
+                                                     int Hl, int BH, int nqb, int C, float scale_log2, float scale) {
   constexpr int NTH = NW * 64, QB = 32 * NW, KS = D / 16, DT = D / 32;
   constexpr int KP = 32 * D / 8 / NTH;
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][32 * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][32 * D];
 
-  const int item = blockIdx.x;
-  const int bh = item / nqb, qb = nqb - 1 - item % nqb;  // the heaviest (last) query block first
+  const int bh = blockIdx.x % BH;
+  int qb, chunk;
+  chunk_of<CAUSAL, true>(blockIdx.x / BH, nqb, QB, s, C, qb, chunk);
+  if (qb < 0) return;
   const int bi = bh / Hl, head = bh % Hl;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
   const int64_t ld = 3LL * Hl * D, ldo = (int64_t)Hl * D;
@@ -306,16 +394,17 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
   const float Lq = qrow < s ? lse[(int64_t)bh * s + qrow] * kLog2e : __builtin_inff();
   const float Dq = qrow < s ? Dv[(int64_t)bh * s + qrow] : 0.f;
 
-  const int kend = CAUSAL ? min(s, q0 + QB) : s;
-  const int nk = (kend + 31) / 32;
+  const int nsteps = q_steps<CAUSAL>(qb, QB, s), nch = (nsteps + C - 1) / C;
+  const int kbase = 32 * C * chunk;          // this chunk's first key
+  const int nk = min(C, nsteps - C * chunk);  // its key blocks of 32
   u32x4 rk0[KP], rv0[KP], rk1[KP], rv1[KP];
   if (nk > 0) {
-    load_rows<D, 32, NTH>(rk0, Kg, ld, 0, s, tid);
-    load_rows<D, 32, NTH>(rv0, Vg, ld, 0, s, tid);
+    load_rows<D, 32, NTH>(rk0, Kg, ld, kbase, s, tid);
+    load_rows<D, 32, NTH>(rv0, Vg, ld, kbase, s, tid);
   }
   if (nk > 1) {
-    load_rows<D, 32, NTH>(rk1, Kg, ld, 32, s, tid);
-    load_rows<D, 32, NTH>(rv1, Vg, ld, 32, s, tid);
+    load_rows<D, 32, NTH>(rk1, Kg, ld, kbase + 32, s, tid);
+    load_rows<D, 32, NTH>(rv1, Vg, ld, kbase + 32, s, tid);
   }
   if (nk > 0) {
     store_rows<D, 32, NTH>(rk0, sK[0], tid);
@@ -333,7 +422,7 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
   // free and receive block j+2, two steps ahead of its use.
   auto step = [&](int j, u32x4 (&ck)[KP], u32x4 (&cv)[KP], u32x4 (&fk)[KP], u32x4 (&fv)[KP])
       __attribute__((always_inline)) {
-    const int k0 = 32 * j, buf = j & 1;
+    const int k0 = kbase + 32 * j, buf = j & 1;
     if (j + 2 < nk) {
       load_rows<D, 32, NTH>(fk, Kg, ld, k0 + 64, s, tid);
       load_rows<D, 32, NTH>(fv, Vg, ld, k0 + 64, s, tid);
@@ -376,6 +465,18 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
   }
 
   // dQ^T accumulator lane: query column qrow; register e of tile i: d = 32i + 8(e/4) + 4hh + e%4
+  if (nch > 1) {
+    if (qrow < s) {
+      float* pq = partQ + ((((int64_t)bh * nqb + qb) * kMaxChunks + chunk) * QB + (qrow - q0)) * D;
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(pq + 32 * i + 8 * g + 4 * hh) =
+              f32x4{dq[i][4 * g], dq[i][4 * g + 1], dq[i][4 * g + 2], dq[i][4 * g + 3]};
+    }
+    return;
+  }
   if (qrow < s) {
     uint16_t* dQg = dqkv + ((int64_t)bi * s + qrow) * ld + (int64_t)head * D;
 #pragma unroll
@@ -390,32 +491,83 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
   }
 }
 
-template <int D, bool C>
+// Workspace: D = rowsum(dO * O) [b*Hl*s], then the partial slots of dQ, dK, dV.
+struct BwdLayout {
+  int64_t d_bytes, q_bytes, kv_bytes;
+  int nqb, nkb, C;
+};
+constexpr int kNW = 4;  // waves per workgroup (32 rows each) in both walks
+
+inline int64_t r256(int64_t x) { return (x + 255) & ~int64_t(255); }
+
+inline BwdLayout bwd_layout(int b, int s, int Hl, int d) {
+  BwdLayout L;
+  const int64_t BH = (int64_t)b * Hl;
+  L.nqb = (s + 32 * kNW - 1) / (32 * kNW);
+  L.nkb = L.nqb;
+  const int max_steps = (s + 31) / 32;
+  L.C = max(16, (max_steps + kMaxChunks - 1) / kMaxChunks);
+  L.d_bytes = r256(BH * s * 4);
+  const int64_t slots = L.C >= max_steps ? 0 : BH * L.nqb * kMaxChunks;  // no block splits when C covers every walk
+  L.q_bytes = r256(slots * 32 * kNW * d * 4);
+  L.kv_bytes = r256(slots * 32 * kNW * d * 4);
+  return L;
+}
+
+template <int D, bool CAUSAL>
 hipError_t launch_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO, const float* lse, uint16_t* dqkv,
-                      float* Dws, int b, int s, int Hl, hipStream_t st) {
-  constexpr int NWK = 4, NWQ = 4;
+                      void* ws, int b, int s, int Hl, hipStream_t st) {
   const int64_t rows = (int64_t)b * s * Hl;
   if (rows == 0) return hipSuccess;
+  const BwdLayout L = bwd_layout(b, s, Hl, D);
+  char* w = static_cast<char*>(ws);
+  float* Dws = reinterpret_cast<float*>(w);
+  float* partQ = reinterpret_cast<float*>(w + L.d_bytes);
+  float* partK = reinterpret_cast<float*>(w + L.d_bytes + L.q_bytes);
+  float* partV = reinterpret_cast<float*>(w + L.d_bytes + L.q_bytes + L.kv_bytes);
+  const int BH = b * Hl, R = 32 * kNW;
+  int items_q = 0, items_k = 0, max_nc = 1;
+  for (int i = 0; i < L.nqb; ++i) {
+    const int nq = (q_steps<CAUSAL>(i, R, s) + L.C - 1) / L.C, nk = (kv_steps<CAUSAL>(i, R, s) + L.C - 1) / L.C;
+    items_q += nq;
+    items_k += nk;
+    max_nc = max(max_nc, max(nq, nk));
+  }
+  if (max_nc > 1 && L.q_bytes == 0) return hipErrorInvalidValue;
   const float scale = 1.f / sqrtf((float)D), scale_log2 = kLog2e * scale;
   hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, dO, O, Dws, s, Hl, D, rows);
-  const int nkb = (s + 32 * NWK - 1) / (32 * NWK), nqb = (s + 32 * NWQ - 1) / (32 * NWQ);
-  hipLaunchKernelGGL((dkdv_kernel<D, C, NWK>), dim3((unsigned)((int64_t)b * Hl * nkb)), dim3(NWK * 64), 0, st, qkv,
-                     dO, lse, Dws, dqkv, s, Hl, nkb, scale_log2, scale);
-  hipLaunchKernelGGL((dq_kernel<D, C, NWQ>), dim3((unsigned)((int64_t)b * Hl * nqb)), dim3(NWQ * 64), 0, st, qkv, dO,
-                     lse, Dws, dqkv, s, Hl, nqb, scale_log2, scale);
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, kNW>), dim3((unsigned)((int64_t)BH * items_k)), dim3(kNW * 64), 0, st,
+                     qkv, dO, lse, Dws, dqkv, partK, partV, s, Hl, BH, L.nkb, L.C, scale_log2, scale);
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, kNW>), dim3((unsigned)((int64_t)BH * items_q)), dim3(kNW * 64), 0, st, qkv,
+                     dO, lse, Dws, dqkv, partQ, s, Hl, BH, L.nqb, L.C, scale_log2, scale);
+  if (max_nc > 1) {
+    const dim3 grid((unsigned)((int64_t)BH * L.nqb), (unsigned)((R * D / 4 + 255) / 256));
+    hipLaunchKernelGGL((combine_kernel<D, CAUSAL, true>), grid, dim3(256), 0, st, partQ, dqkv, s, Hl, L.nqb, R, L.C, 0,
+                       scale);
+    hipLaunchKernelGGL((combine_kernel<D, CAUSAL, false>), grid, dim3(256), 0, st, partK, dqkv, s, Hl, L.nkb, R, L.C,
+                       1, scale);
+    hipLaunchKernelGGL((combine_kernel<D, CAUSAL, false>), grid, dim3(256), 0, st, partV, dqkv, s, Hl, L.nkb, R, L.C,
+                       2, 1.f);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t attn_bwd_workspace(int b, int s, int Hl, int d) {
+  if (b <= 0 || s <= 0 || Hl <= 0) return 0;
+  const BwdLayout L = bwd_layout(b, s, Hl, d);
+  return (size_t)(L.d_bytes + L.q_bytes + 2 * L.kv_bytes);
+}
+
 hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO, const float* lse, uint16_t* dqkv,
-                    float* Dws, int b, int s, int Hl, int d, bool causal, hipStream_t st) {
+                    void* ws, int b, int s, int Hl, int d, bool causal, hipStream_t st) {
   if (d == 128)
-    return causal ? launch_bwd<128, true>(qkv, O, dO, lse, dqkv, Dws, b, s, Hl, st)
-                  : launch_bwd<128, false>(qkv, O, dO, lse, dqkv, Dws, b, s, Hl, st);
+    return causal ? launch_bwd<128, true>(qkv, O, dO, lse, dqkv, ws, b, s, Hl, st)
+                  : launch_bwd<128, false>(qkv, O, dO, lse, dqkv, ws, b, s, Hl, st);
   if (d == 64)
-    return causal ? launch_bwd<64, true>(qkv, O, dO, lse, dqkv, Dws, b, s, Hl, st)
-                  : launch_bwd<64, false>(qkv, O, dO, lse, dqkv, Dws, b, s, Hl, st);
+    return causal ? launch_bwd<64, true>(qkv, O, dO, lse, dqkv, ws, b, s, Hl, st)
+                  : launch_bwd<64, false>(qkv, O, dO, lse, dqkv, ws, b, s, Hl, st);
   return hipErrorInvalidValue;
 }
 
