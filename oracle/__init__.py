@@ -43,4 +43,7 @@ from .attention import (  # noqa: F401
 )
 from .embedding import vocab_embed_shard  # noqa: F401
 from .vocab_ce import vocab_ce_partials, vocab_ce_combine, vocab_ce_sharded  # noqa: F401
-from .seqpar import layernorm, all_gather, reduce_scatter, dropout_residual, sp_mlp_block, tp_mlp_block  # noqa: F401,E501
+from .seqpar import (  # noqa: F401
+    layernorm, all_gather, reduce_scatter, dropout_residual, sp_mlp_block, tp_mlp_block, layernorm_bwd,
+    dropout_bwd, sp_mlp_block_bwd,
+)

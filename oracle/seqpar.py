@@ -25,13 +25,21 @@ Readings (listed in DESIGN.md):
     GEMM's input dtype); the reduce-scatter adds the partials in rank order 0..N-1;
   * rank i owns rows [i*s/N, (i+1)*s/N).
 
-float64 throughout; ``matched=True`` rounds the LayerNorm output to bf16 as the
-GPU stores it.
+Backward (the chain rule through the same block; the page states only the
+forward split): Dropout's backward scales the kept gradient by 1/p; the
+reduce-scatter's backward is an all-gather of the ranks' gradient rows (the
+MLP's replicated upstream gradient); the all-gather's backward is a
+reduce-scatter of the MLP's input-gradient partials; LayerNorm's backward runs
+on the rank's rows, and its gamma, beta gradients are per-rank partials that an
+all-reduce adds. The residual path passes the gradient through.
+
+float64 throughout; ``matched=True`` rounds the LayerNorm output, and in the
+backward the gathered upstream gradient, to bf16 as the GPU stores them.
 """
 import numpy as np
 
 from .bf16 import round_to_bf16
-from .mlp import mlp_fwd_shard
+from .mlp import mlp_bwd_shard, mlp_fwd_shard
 
 LN_EPS = 1e-5
 
@@ -106,3 +114,55 @@ def tp_mlp_block(R, gamma, beta, shards, keep=None, p=1.0, matched=True, eps=LN_
         z = mlp_fwd_shard(X, A_j, B_j, matched=matched)["Z"]
         Z = z if Z is None else Z + z
     return dict(X=X, R_out=dropout_residual(R, Z, keep, p))
+
+
+def layernorm_bwd(X, gamma, dY, eps=LN_EPS):
+    """Gradients of sum(dY * LayerNorm(X)) with respect to X, gamma and beta.
+
+    With xh = (x - mean) * rstd and g = dY * gamma, per row:
+    dX = rstd * (g - mean(g) - xh * mean(g * xh)); dgamma = sum_rows dY * xh;
+    dbeta = sum_rows dY."""
+    X = np.asarray(X, np.float64)
+    dY = np.asarray(dY, np.float64)
+    mu = X.mean(axis=1, keepdims=True)
+    rstd = 1.0 / np.sqrt(((X - mu) ** 2).mean(axis=1, keepdims=True) + eps)
+    xh = (X - mu) * rstd
+    g = dY * np.asarray(gamma, np.float64)
+    dX = rstd * (g - g.mean(axis=1, keepdims=True) - xh * (g * xh).mean(axis=1, keepdims=True))
+    return dict(dX=dX, dgamma=(dY * xh).sum(axis=0), dbeta=dY.sum(axis=0))
+
+
+def dropout_bwd(dY, keep=None, p=1.0):
+    """Gradient through Dropout: kept entries scaled by 1/p, dropped ones zero."""
+    dY = np.asarray(dY, np.float64)
+    if keep is None:
+        return dY
+    return np.where(np.asarray(keep) != 0, dY / p, 0.0)
+
+
+def sp_mlp_block_bwd(R, gamma, beta, shards, dR_out, keep=None, p=1.0, matched=True, eps=LN_EPS):
+    """Backward of sp_mlp_block for the upstream gradient dR_out [s, h] of the new
+    residual rows. Returns dR (all ranks' rows), dgamma and dbeta (summed over the
+    ranks' partials), the per-rank partials, and each rank's dA_j, dB_j."""
+    N = len(shards)
+    s = R.shape[0]
+    f = sp_mlp_block(R, gamma, beta, shards, keep, p, matched, eps)
+    fw = [mlp_fwd_shard(f["X"], A_j, B_j, matched=matched) for A_j, B_j in shards]
+    dO = [dropout_bwd(dR_out[row_slice(s, N, i)], None if keep is None else keep[row_slice(s, N, i)], p)
+          for i in range(N)]
+    dZ = all_gather(dO)
+    if matched:
+        dZ = round_to_bf16(dZ)
+    g = [mlp_bwd_shard(f["X"], A_j, B_j, fw[j]["U"], fw[j]["Y"], dZ, matched=matched)
+         for j, (A_j, B_j) in enumerate(shards)]
+    dX_parts = [gj["dX"] for gj in g]
+    dR, dgam, dbet = [], [], []
+    for i in range(N):
+        rs = row_slice(s, N, i)
+        dL_i = reduce_scatter(dX_parts, N, i)
+        lb = layernorm_bwd(R[rs], gamma, dL_i, eps)
+        dR.append(np.asarray(dR_out[rs], np.float64) + lb["dX"])
+        dgam.append(lb["dgamma"])
+        dbet.append(lb["dbeta"])
+    return dict(dR=np.concatenate(dR, axis=0), dgamma=sum(dgam), dbeta=sum(dbet), dgamma_parts=dgam,
+                dbeta_parts=dbet, dZ=dZ, dX_parts=dX_parts, dA=[gj["dA"] for gj in g], dB=[gj["dB"] for gj in g])

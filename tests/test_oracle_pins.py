@@ -644,3 +644,60 @@ class TestAttentionBackward:
                 np.testing.assert_allclose(r["dWqkv"][:, k * w:(k + 1) * w], tw.grad.numpy()[:, cols],
                                            rtol=1e-10, atol=1e-12)
         np.testing.assert_allclose(dX, tX.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+class TestSequenceParallelBackward:
+    """Backward of the sequence-parallel block: LayerNorm's backward against torch
+    float64 autograd and finite differences; the whole block's gradients against
+    autograd of the unsharded block."""
+
+    def test_layernorm_bwd_torch(self):
+        rng = np.random.default_rng(71)
+        X = rng.standard_normal((6, 40)) * 2 + 0.3
+        g, b = 1 + 0.1 * rng.standard_normal(40), 0.1 * rng.standard_normal(40)
+        dY = rng.standard_normal((6, 40))
+        r = seqpar.layernorm_bwd(X, g, dY)
+        tX, tg, tb = (torch.tensor(a, requires_grad=True) for a in (X, g, b))
+        (torch.nn.functional.layer_norm(tX, (40,), tg, tb, eps=1e-5) * torch.from_numpy(dY)).sum().backward()
+        np.testing.assert_allclose(r["dX"], tX.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["dgamma"], tg.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(r["dbeta"], tb.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+    def test_layernorm_bwd_finite_differences(self):
+        rng = np.random.default_rng(72)
+        X = rng.standard_normal((3, 8))
+        g, b = 1 + 0.2 * rng.standard_normal(8), rng.standard_normal(8)
+        dY = rng.standard_normal((3, 8))
+        r = seqpar.layernorm_bwd(X, g, dY)
+        eps = 1e-6
+        for (i, j) in [(0, 0), (1, 5), (2, 7)]:
+            Xp, Xm = X.copy(), X.copy()
+            Xp[i, j] += eps
+            Xm[i, j] -= eps
+            num = ((seqpar.layernorm(Xp, g, b) - seqpar.layernorm(Xm, g, b)) * dY).sum() / (2 * eps)
+            assert abs(num - r["dX"][i, j]) < 1e-7
+        # each row's dX sums to zero (LayerNorm is shift invariant)
+        np.testing.assert_allclose(r["dX"].sum(axis=1), 0.0, atol=1e-12)
+
+    @pytest.mark.parametrize("N", [1, 2, 4])
+    def test_sp_block_bwd_equals_autograd_of_unsharded_block(self, N):
+        s, h, f_full, p = 8, 16, 64, 0.8
+        rng = np.random.default_rng(73 + N)
+        R = rng.standard_normal((s, h)) + 0.2
+        g, b = 1 + 0.1 * rng.standard_normal(h), 0.1 * rng.standard_normal(h)
+        A, B = rng.standard_normal((h, f_full)) * 0.2, rng.standard_normal((f_full, h)) * 0.2
+        keep = (rng.random((s, h)) < p).astype(np.uint8)
+        dRo = rng.standard_normal((s, h))
+        shards = [(A[:, j * f_full // N:(j + 1) * f_full // N], B[j * f_full // N:(j + 1) * f_full // N])
+                  for j in range(N)]
+        got = seqpar.sp_mlp_block_bwd(R, g, b, shards, dRo, keep, p, matched=False)
+        tR, tg, tb, tA, tB = (torch.tensor(a, requires_grad=True) for a in (R, g, b, A, B))
+        X = torch.nn.functional.layer_norm(tR, (h,), tg, tb, eps=1e-5)
+        Z = torch.nn.functional.gelu(X @ tA) @ tB
+        out = tR + torch.where(torch.from_numpy(keep) != 0, Z / p, torch.zeros_like(Z))
+        (out * torch.from_numpy(dRo)).sum().backward()
+        np.testing.assert_allclose(got["dR"], tR.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(got["dgamma"], tg.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(got["dbeta"], tb.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(np.concatenate(got["dA"], axis=1), tA.grad.numpy(), rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(np.concatenate(got["dB"], axis=0), tB.grad.numpy(), rtol=1e-10, atol=1e-12)
