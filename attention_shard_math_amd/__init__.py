@@ -31,6 +31,9 @@ from ._lib import (  # noqa: F401
     vocab_ce_loss,
     shard_sum,
     layernorm,
+    layernorm_bwd,
+    layernorm_bwd_workspace,
+    sp_dropout_bwd,
     sp_all_gather,
     sp_reduce_scatter,
 )

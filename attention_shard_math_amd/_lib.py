@@ -39,6 +39,8 @@ _SIGS = {
                     _sz, _vp],
     "tp_layernorm": [_i64, _i64, _vp, _vp, _vp, C.c_float, _vp, _vp],
     "tp_sp_all_gather": [C.c_int, C.POINTER(_vp), _i64, _i64, _vp, _vp],
+    "tp_layernorm_bwd": [_i64, _i64, _vp, _vp, _vp, _vp, C.c_float, _vp, _vp, _vp, _vp, _sz, _vp],
+    "tp_sp_dropout_bwd": [_i64, _i64, _vp, _vp, C.c_float, _vp, _vp],
     "tp_sp_reduce_scatter": [C.c_int, C.POINTER(_vp), _i64, _i64, C.c_int, _vp, _vp, C.c_float, _vp, _vp],
 }
 for _name, _args in _SIGS.items():
@@ -50,6 +52,8 @@ lib.tp_mlp_bwd_workspace.restype = _sz
 lib.tp_mlp_bwd_recompute_workspace.argtypes = [_i64, _i64, _i64]
 lib.tp_mlp_bwd_recompute_workspace.restype = _sz
 lib.tp_vocab_ce_workspace.argtypes = [_i64, _i64, _i64]
+lib.tp_layernorm_bwd_workspace.argtypes = [_i64, _i64]
+lib.tp_layernorm_bwd_workspace.restype = _sz
 lib.tp_attn_core_bwd_workspace.argtypes = [_i64, _i64, _i64]
 lib.tp_attn_core_bwd_workspace.restype = _sz
 lib.tp_attn_bwd_workspace.argtypes = [_i64, _i64, _i64, _i64, _i64]
@@ -275,6 +279,27 @@ def layernorm(X, gamma, beta, Y, eps=1e-5, stream=None):
     _check(lib.tp_layernorm(rows, h, _ptr(X, (rows, h), f32, "X"), _ptr(gamma, (h,), f32, "gamma"),
                             _ptr(beta, (h,), f32, "beta"), eps, _ptr(Y, (rows, h), torch.bfloat16, "Y"),
                             _stream(stream)), "tp_layernorm")
+
+
+def layernorm_bwd_workspace(rows, h):
+    return int(lib.tp_layernorm_bwd_workspace(rows, h))
+
+
+def layernorm_bwd(X, gamma, dY, dX, dgamma, dbeta, ws, dRes=None, eps=1e-5, stream=None):
+    rows, h = X.shape
+    f32 = torch.float32
+    wp, wb = _wsargs(ws)
+    _check(lib.tp_layernorm_bwd(rows, h, _ptr(X, (rows, h), f32, "X"), _ptr(gamma, (h,), f32, "gamma"),
+                                _ptr(dY, (rows, h), f32, "dY"), _ptr(dRes, (rows, h), f32, "dRes"), eps,
+                                _ptr(dX, (rows, h), f32, "dX"), _ptr(dgamma, (h,), f32, "dgamma"),
+                                _ptr(dbeta, (h,), f32, "dbeta"), wp, wb, _stream(stream)), "tp_layernorm_bwd")
+
+
+def sp_dropout_bwd(dY, out, keep=None, keep_prob=1.0, stream=None):
+    rows, h = dY.shape
+    _check(lib.tp_sp_dropout_bwd(rows, h, _ptr(dY, (rows, h), torch.float32, "dY"),
+                                 _ptr(keep, (rows, h), torch.uint8, "keep"), keep_prob,
+                                 _ptr(out, (rows, h), torch.bfloat16, "out"), _stream(stream)), "tp_sp_dropout_bwd")
 
 
 def sp_all_gather(slices, out, stream=None):

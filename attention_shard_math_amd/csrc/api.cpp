@@ -534,6 +534,55 @@ TP_API tp_status tp_layernorm(int64_t rows, int64_t h, const float* X, const flo
                     fn);
 }
 
+TP_API size_t tp_layernorm_bwd_workspace(int64_t rows, int64_t h) {
+  if (rows < 0 || h <= 0) return 0;
+  return tps::layernorm_bwd_workspace(rows, h);
+}
+
+TP_API tp_status tp_layernorm_bwd(int64_t rows, int64_t h, const float* X, const float* gamma, const float* dY,
+                                  const float* dRes, float eps, float* dX, float* dgamma, float* dbeta, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  const char* fn = "tp_layernorm_bwd";
+  if (rows < 0) return fail(TP_ERR_INVALID_ARG, "%s: rows < 0", fn);
+  TRY(check_sp_h(fn, h));
+  if (h > tps::kLnBwdMaxH)
+    return fail(TP_ERR_UNSUPPORTED, "%s: h above %lld is not supported", fn, (long long)tps::kLnBwdMaxH);
+  if (!(eps >= 0.f)) return fail(TP_ERR_INVALID_ARG, "%s: eps must be >= 0", fn);
+  if (rows > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "%s: rows exceeds 2^31-1", fn);
+  TRY(check_ptr(fn, "gamma", gamma));
+  TRY(check_ptr(fn, "dgamma", dgamma));
+  TRY(check_ptr(fn, "dbeta", dbeta));
+  if (rows > 0) {
+    TRY(check_ptr(fn, "X", X));
+    TRY(check_ptr(fn, "dY", dY));
+    TRY(check_opt_ptr(fn, "dRes", dRes));
+    TRY(check_ptr(fn, "dX", dX));
+  }
+  const size_t need = tp_layernorm_bwd_workspace(rows, h);
+  if (!ws || ws_bytes < need)
+    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
+                ws ? "" : " (NULL)");
+  TRY(check_ptr(fn, "ws", ws));
+  return hip_status(tps::layernorm_bwd(X, rows, h, gamma, dY, dRes, eps, dX, dgamma, dbeta, ws, as_stream(stream)),
+                    fn);
+}
+
+TP_API tp_status tp_sp_dropout_bwd(int64_t rows, int64_t h, const float* dY, const uint8_t* keep, float keep_prob,
+                                   void* out, void* stream) {
+  const char* fn = "tp_sp_dropout_bwd";
+  if (rows < 0) return fail(TP_ERR_INVALID_ARG, "%s: rows < 0", fn);
+  TRY(check_sp_h(fn, h));
+  if (keep && !(keep_prob > 0.f && keep_prob <= 1.f))
+    return fail(TP_ERR_INVALID_ARG, "%s: keep_prob must be in (0, 1]", fn);
+  if (keep && (reinterpret_cast<uintptr_t>(keep) & 3u))
+    return fail(TP_ERR_UNSUPPORTED, "%s: keep is not 4-byte aligned", fn);
+  if (rows == 0) return ok();
+  TRY(check_ptr(fn, "dY", dY));
+  TRY(check_ptr(fn, "out", out));
+  return hip_status(tps::sp_dropout_bwd(dY, rows, h, keep, keep_prob, static_cast<uint16_t*>(out), as_stream(stream)),
+                    fn);
+}
+
 TP_API tp_status tp_sp_reduce_scatter(int n_parts, const float* const* partials, int64_t s, int64_t h, int rank,
                                       const float* residual, const uint8_t* keep, float keep_prob, float* out,
                                       void* stream) {
@@ -558,7 +607,7 @@ TP_API tp_status tp_sp_reduce_scatter(int n_parts, const float* const* partials,
     TRY(check_ptr(fn, name, partials[i]));
     p.p[i] = partials[i];
   }
-  TRY(check_ptr(fn, "residual", residual));
+  TRY(check_opt_ptr(fn, "residual", residual));
   TRY(check_ptr(fn, "out", out));
   return hip_status(tps::sp_reduce_scatter(p, n_parts, (int64_t)rank * rows, rows, h, residual, keep, keep_prob, out,
                                            as_stream(stream)),

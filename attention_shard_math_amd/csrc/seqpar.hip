@@ -14,6 +14,16 @@
 //    rank's rows, dropout with an input keep mask, residual add; 16-byte
 //    non-temporal accesses. HBM-bound: (4N + 4 + 1 + 4) bytes per element.
 //  * sp_all_gather — N slice copies into the gathered buffer in one launch.
+// Backward:
+//  * layernorm_bwd_rows — one workgroup per row, X and dY rows in registers:
+//    dX = rstd (g - mean(g) - xh mean(g xh)) (+ the residual path's gradient),
+//    g = dY gamma, xh = (x - mean) rstd; the row's mean and rstd are kept for
+//    the column sums;
+//  * layernorm_bwd_cols — dgamma = sum_rows dY xh, dbeta = sum_rows dY, as
+//    partial sums over 64 row blocks (fixed order) and a final ordered sum;
+//  * dropout_bwd — dY / p where kept, else 0, rounded to bf16 (the MLP
+//    backward's input); the all-gather and reduce-scatter above serve the
+//    backward unchanged (each is the other's backward).
 #include "common.hpp"
 #include "seqpar.hpp"
 
@@ -80,6 +90,116 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const f32x4* __restrict_
   }
 }
 
+template <int VPT>
+__global__ __launch_bounds__(256) void layernorm_bwd_rows_kernel(const f32x4* __restrict__ X, int64_t h4,
+                                                                 const f32x4* __restrict__ gamma,
+                                                                 const f32x4* __restrict__ dY,
+                                                                 const f32x4* __restrict__ dRes, float eps,
+                                                                 float inv_h, f32x4* __restrict__ dX,
+                                                                 float2* __restrict__ stats) {
+  __shared__ float red[4];
+  const int64_t row = blockIdx.x;
+  const f32x4* x = X + row * h4;
+  const f32x4* dy = dY + row * h4;
+  f32x4 v[VPT], gv[VPT];
+  float sx = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j = threadIdx.x + k * 256;
+    v[k] = j < h4 ? x[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+    gv[k] = j < h4 ? dy[j] * gamma[j] : f32x4{0.f, 0.f, 0.f, 0.f};
+    sx += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
+  }
+  const float mean = block_sum(sx, red) * inv_h;
+  float q = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j = threadIdx.x + k * 256;
+    if (j < h4) {
+      const float d0 = v[k][0] - mean, d1 = v[k][1] - mean, d2 = v[k][2] - mean, d3 = v[k][3] - mean;
+      q += (d0 * d0 + d1 * d1) + (d2 * d2 + d3 * d3);
+    }
+  }
+  const float rstd = 1.0f / sqrtf(block_sum(q, red) * inv_h + eps);
+  float sg = 0.f, sgx = 0.f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j = threadIdx.x + k * 256;
+    if (j < h4) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        v[k][c] = (v[k][c] - mean) * rstd;  // xh
+        sg += gv[k][c];
+        sgx += gv[k][c] * v[k][c];
+      }
+    }
+  }
+  const float mg = block_sum(sg, red) * inv_h;
+  const float mgx = block_sum(sgx, red) * inv_h;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int64_t j = threadIdx.x + k * 256;
+    if (j < h4) {
+      f32x4 o;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) o[c] = rstd * (gv[k][c] - mg - v[k][c] * mgx);
+      if (dRes) o = o + dRes[row * h4 + j];
+      dX[row * h4 + j] = o;
+    }
+  }
+  if (threadIdx.x == 0) stats[row] = float2{mean, rstd};
+}
+
+// Partial column sums over row block blockIdx.y (rows rb*rpb .. +rpb), in row order.
+__global__ __launch_bounds__(256) void layernorm_bwd_cols_kernel(const f32x4* __restrict__ X,
+                                                                 const f32x4* __restrict__ dY,
+                                                                 const float2* __restrict__ stats, int64_t rows,
+                                                                 int64_t h4, int64_t rpb, f32x4* __restrict__ pg,
+                                                                 f32x4* __restrict__ pb) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= h4) return;
+  const int64_t r0 = (int64_t)blockIdx.y * rpb, r1 = min(rows, r0 + rpb);
+  f32x4 ag = {0.f, 0.f, 0.f, 0.f}, ab = {0.f, 0.f, 0.f, 0.f};
+  for (int64_t r = r0; r < r1; ++r) {
+    const float2 st = stats[r];
+    const f32x4 dy = dY[r * h4 + j], x = X[r * h4 + j];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) ag[c] += dy[c] * ((x[c] - st.x) * st.y);
+    ab = ab + dy;
+  }
+  pg[(int64_t)blockIdx.y * h4 + j] = ag;
+  pb[(int64_t)blockIdx.y * h4 + j] = ab;
+}
+
+__global__ __launch_bounds__(256) void colsum_kernel(const f32x4* __restrict__ pg, const f32x4* __restrict__ pb,
+                                                     int nb, int64_t h4, f32x4* __restrict__ dgamma,
+                                                     f32x4* __restrict__ dbeta) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= h4) return;
+  f32x4 g = pg[j], b = pb[j];
+  for (int i = 1; i < nb; ++i) {
+    g = g + pg[(int64_t)i * h4 + j];
+    b = b + pb[(int64_t)i * h4 + j];
+  }
+  dgamma[j] = g;
+  dbeta[j] = b;
+}
+
+__global__ __launch_bounds__(256) void dropout_bwd_kernel(const f32x4* __restrict__ dY,
+                                                          const uint32_t* __restrict__ keep, float keep_prob,
+                                                          int64_t nvec, uint2* __restrict__ out) {
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x; v < nvec; v += stride) {
+    f32x4 g = dY[v];
+    if (keep) {
+      const uint32_t k = keep[v];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) g[c] = ((k >> (8 * c)) & 0xffu) ? g[c] / keep_prob : 0.f;
+    }
+    out[v] = uint2{pack_bf16x2(g[0], g[1]), pack_bf16x2(g[2], g[3])};
+  }
+}
+
 template <int N>
 __global__ __launch_bounds__(256) void reduce_scatter_kernel(SpParts p, int64_t off4, int64_t nvec,
                                                              const f32x4* R, const uint32_t* __restrict__ keep,
@@ -99,7 +219,8 @@ __global__ __launch_bounds__(256) void reduce_scatter_kernel(SpParts p, int64_t 
 #pragma unroll
       for (int c = 0; c < 4; ++c) s[c] = ((k >> (8 * c)) & 0xffu) ? s[c] / keep_prob : 0.f;
     }
-    __builtin_nontemporal_store(__builtin_nontemporal_load(R + v) + s, out + v);
+    if (R) s = __builtin_nontemporal_load(R + v) + s;
+    __builtin_nontemporal_store(s, out + v);
   }
 }
 
@@ -150,6 +271,62 @@ hipError_t layernorm_rows(const float* X, int64_t rows, int64_t h, const float* 
     hipLaunchKernelGGL(layernorm_kernel<32>, grid, block, 0, st, Xv, h4, Gv, Bv, eps, inv_h, Yv);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t layernorm_bwd(const float* X, int64_t rows, int64_t h, const float* gamma, const float* dY,
+                         const float* dRes, float eps, float* dX, float* dgamma, float* dbeta, void* ws,
+                         hipStream_t st) {
+  const int64_t h4 = h / 4;
+  const int vpt = (int)((h4 + 255) / 256);
+  float2* stats = static_cast<float2*>(ws);
+  float* pg = reinterpret_cast<float*>(static_cast<char*>(ws) + ((rows * 8 + 255) & ~int64_t(255)));
+  float* pb = pg + kLnBwdRowBlocks * h;
+  if (rows > 0) {
+    const dim3 grid((unsigned)rows), block(256);
+    const float inv_h = 1.0f / (float)h;
+    auto Xv = reinterpret_cast<const f32x4*>(X);
+    auto Gv = reinterpret_cast<const f32x4*>(gamma);
+    auto Dv = reinterpret_cast<const f32x4*>(dY);
+    auto Rv = reinterpret_cast<const f32x4*>(dRes);
+    auto Ov = reinterpret_cast<f32x4*>(dX);
+    if (vpt <= 4)
+      hipLaunchKernelGGL(layernorm_bwd_rows_kernel<4>, grid, block, 0, st, Xv, h4, Gv, Dv, Rv, eps, inv_h, Ov, stats);
+    else if (vpt <= 8)
+      hipLaunchKernelGGL(layernorm_bwd_rows_kernel<8>, grid, block, 0, st, Xv, h4, Gv, Dv, Rv, eps, inv_h, Ov, stats);
+    else if (vpt <= 12)
+      hipLaunchKernelGGL(layernorm_bwd_rows_kernel<12>, grid, block, 0, st, Xv, h4, Gv, Dv, Rv, eps, inv_h, Ov, stats);
+    else if (vpt <= 18)
+      hipLaunchKernelGGL(layernorm_bwd_rows_kernel<18>, grid, block, 0, st, Xv, h4, Gv, Dv, Rv, eps, inv_h, Ov, stats);
+    else if (vpt <= 24)
+      hipLaunchKernelGGL(layernorm_bwd_rows_kernel<24>, grid, block, 0, st, Xv, h4, Gv, Dv, Rv, eps, inv_h, Ov, stats);
+    else
+      return hipErrorInvalidValue;
+  }
+  const int nb = (int)(rows < kLnBwdRowBlocks ? (rows > 0 ? rows : 1) : kLnBwdRowBlocks);
+  const int64_t rpb = rows > 0 ? (rows + nb - 1) / nb : 0;
+  const unsigned gx = (unsigned)((h4 + 255) / 256);
+  hipLaunchKernelGGL(layernorm_bwd_cols_kernel, dim3(gx, (unsigned)nb), dim3(256), 0, st,
+                     reinterpret_cast<const f32x4*>(X), reinterpret_cast<const f32x4*>(dY), stats, rows, h4, rpb,
+                     reinterpret_cast<f32x4*>(pg), reinterpret_cast<f32x4*>(pb));
+  hipLaunchKernelGGL(colsum_kernel, dim3(gx), dim3(256), 0, st, reinterpret_cast<const f32x4*>(pg),
+                     reinterpret_cast<const f32x4*>(pb), nb, h4, reinterpret_cast<f32x4*>(dgamma),
+                     reinterpret_cast<f32x4*>(dbeta));
+  return hipGetLastError();
+}
+
+size_t layernorm_bwd_workspace(int64_t rows, int64_t h) {
+  return (size_t)(((rows * 8 + 255) & ~int64_t(255)) + 2 * kLnBwdRowBlocks * h * 4);
+}
+
+hipError_t sp_dropout_bwd(const float* dY, int64_t rows, int64_t h, const uint8_t* keep, float keep_prob,
+                          uint16_t* out, hipStream_t st) {
+  const int64_t nvec = rows * h / 4;
+  if (nvec == 0) return hipSuccess;
+  int64_t blocks = (nvec + 255) / 256;
+  if (blocks > 256 * 8) blocks = 256 * 8;
+  hipLaunchKernelGGL(dropout_bwd_kernel, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<const f32x4*>(dY),
+                     reinterpret_cast<const uint32_t*>(keep), keep_prob, nvec, reinterpret_cast<uint2*>(out));
   return hipGetLastError();
 }
 

@@ -248,11 +248,32 @@ tp_status tp_sp_all_gather(int n_parts, const void* const* slices, int64_t rows,
  *   O = ((P_0 + P_1) + ...) + P_{n-1} over rows [rank*s/n, (rank+1)*s/n) (float32, rank order)
  *   out = residual + (keep ? O / keep_prob : 0)  (keep NULL: out = residual + O)
  * partials: HOST array of n device pointers to float32 [s, h]; residual and out float32
- * [s/n, h] (out may equal residual); keep: uint8 [s/n, h] (nonzero = kept, the drawn
- * mask is an input), 4-byte aligned, keep_prob in (0, 1]. s % n == 0, h % 8 == 0. */
+ * [s/n, h] (out may equal residual; residual NULL: no residual add, as in the backward,
+ * where this is the all-gather's backward); keep: uint8 [s/n, h] (nonzero = kept, the
+ * drawn mask is an input), 4-byte aligned, keep_prob in (0, 1]. s % n == 0, h % 8 == 0. */
 tp_status tp_sp_reduce_scatter(int n_parts, const float* const* partials, int64_t s, int64_t h,
                                int rank, const float* residual, const uint8_t* keep,
                                float keep_prob, float* out, void* stream);
+
+/* Backward of the sequence-parallel block on one rank's rows (the chain rule through
+ * the operators above; the page gives the forward split only):
+ *
+ * LayerNorm backward: with xh = (X - mean) * rstd and g = dY * gamma per row,
+ *   dX = rstd * (g - mean(g) - xh * mean(g * xh)) (+ dRes, the residual path's gradient,
+ *   if not NULL), dgamma = sum_rows dY * xh, dbeta = sum_rows dY (this rank's partials,
+ *   overwritten; the ranks' partials are then all-reduced). X, dY, dRes, dX float32
+ *   [rows, h]; gamma, dgamma, dbeta float32 [h]; h % 8 == 0, h <= 24576.
+ *   ws: tp_layernorm_bwd_workspace(rows, h) bytes. Deterministic. */
+tp_status tp_layernorm_bwd(int64_t rows, int64_t h, const float* X, const float* gamma,
+                           const float* dY, const float* dRes, float eps, float* dX,
+                           float* dgamma, float* dbeta, void* ws, size_t ws_bytes, void* stream);
+size_t tp_layernorm_bwd_workspace(int64_t rows, int64_t h);
+
+/* Dropout backward into the MLP backward's bf16 input: out = bf16(keep ? dY / keep_prob : 0)
+ * (keep NULL: out = bf16(dY)). dY float32 [rows, h], out bf16 [rows, h] (may point into the
+ * rows of a gathered [s, h] buffer); keep 4-byte aligned. */
+tp_status tp_sp_dropout_bwd(int64_t rows, int64_t h, const float* dY, const uint8_t* keep,
+                            float keep_prob, void* out, void* stream);
 
 /* Shard-sum standing in for the all-reduce of N partials on one GPU:
  *   out = ((P_0 + P_1) + P_2) + ... + P_{N-1}, elementwise, in float32, in this

@@ -179,11 +179,34 @@ class TestValidation:
         assert rs(4, arr, 16, 64, 0, P, P, 0.0, P, None) == INVALID        # keep_prob
         assert rs(4, arr, 16, 64, 0, P, P, 1.5, P, None) == INVALID
         assert rs(4, arr, 16, 64, 0, P, P + 2, 0.5, P, None) == UNSUPPORTED  # keep alignment
-        assert rs(4, arr, 16, 64, 0, None, None, 1.0, P, None) == INVALID  # residual NULL
+        assert rs(4, arr, 16, 64, 0, MIS, None, 1.0, P, None) == UNSUPPORTED  # residual misaligned
+        assert rs(4, arr, 16, 64, 0, None, None, 1.0, None, None) == INVALID  # out NULL
         assert rs(4, arr, 16, 20, 0, P, None, 1.0, P, None) == UNSUPPORTED
         assert rs(2, (C.c_void_p * 2)(P, None), 16, 64, 0, P, None, 1.0, P, None) == INVALID
         assert rs(17, arr, 17, 64, 0, P, None, 1.0, P, None) == INVALID
         assert rs(4, None, 0, 64, 0, None, None, 1.0, None, None) == OK
+
+    def test_sequence_parallel_backward(self):
+        need = lib.tp_layernorm_bwd_workspace(10, 64)
+        assert need >= 10 * 8 and need % 4 == 0
+        lb = lib.tp_layernorm_bwd
+        assert lb(-1, 64, P, P, P, None, 1e-5, P, P, P, P, need, None) == INVALID
+        assert lb(10, 60, P, P, P, None, 1e-5, P, P, P, P, need, None) == UNSUPPORTED      # h % 8
+        assert lb(10, 24584, P, P, P, None, 1e-5, P, P, P, P, need, None) == UNSUPPORTED   # h too large
+        assert lb(10, 64, P, P, P, None, -1.0, P, P, P, P, need, None) == INVALID           # eps
+        assert lb(10, 64, P, P, None, None, 1e-5, P, P, P, P, need, None) == INVALID        # dY NULL
+        assert lb(10, 64, P, P, P, MIS, 1e-5, P, P, P, P, need, None) == UNSUPPORTED        # dRes misaligned
+        assert lb(10, 64, P, P, P, None, 1e-5, P, None, P, P, need, None) == INVALID        # dgamma NULL
+        assert lb(10, 64, P, P, P, None, 1e-5, P, P, P, P, need - 1, None) == WORKSPACE
+        assert lb(10, 64, P, P, P, None, 1e-5, P, P, P, None, need, None) == WORKSPACE
+        db = lib.tp_sp_dropout_bwd
+        assert db(-1, 64, P, None, 1.0, P, None) == INVALID
+        assert db(4, 12, P, None, 1.0, P, None) == UNSUPPORTED
+        assert db(4, 64, P, P, 0.0, P, None) == INVALID
+        assert db(4, 64, P, P + 2, 0.5, P, None) == UNSUPPORTED
+        assert db(4, 64, None, None, 1.0, P, None) == INVALID
+        assert db(4, 64, P, None, 1.0, MIS, None) == UNSUPPORTED
+        assert db(0, 64, None, None, 1.0, None, None) == OK
 
     def test_shard_sum(self):
         arr = (C.c_void_p * 17)(*([P] * 17))

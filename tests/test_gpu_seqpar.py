@@ -180,3 +180,142 @@ def test_full_size_layernorm_gather_reduce_scatter():
         rs = slice(i * rows, (i + 1) * rows)
         want = seqpar.dropout_residual(sp["R"][rs], seqpar.reduce_scatter(parts, N, i), sp["keep"][rs], c["keep_prob"])
         np.testing.assert_allclose(g_out[rs], want, rtol=1e-6, atol=1e-5)
+
+
+# ---------------------------------------------------------------- backward
+# LayerNorm's backward is float32 throughout: dX within 2e-5 of max|dX| plus 1e-4
+# relative per element, dgamma/dbeta (sums over the rows) within 1e-4 relative
+# plus 1e-5 of their maximum. Dropout's backward rounds once to bf16: within one
+# bf16 spacing of the float64 value.
+
+
+def _close_f32(g, r, what, rel=1e-4, nw=2e-5):
+    g, r = np.asarray(g, np.float64), np.asarray(r, np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    tol = rel * np.abs(r) + nw * max(np.abs(r).max(), 1e-30)
+    bad = np.abs(g - r) > tol
+    assert not bad.any(), f"{what}: {bad.sum()} beyond tolerance, max diff {np.abs(g - r).max():.3e}"
+
+
+def _close_rel(g, r, what, normwise=2e-2, mean_rel=5e-3):
+    """bf16-GEMM tolerance in relative terms (gradients of any magnitude):
+    max|g - r| <= 2e-2 max|r| and mean|g - r| <= 5e-3 mean|r|."""
+    g, r = np.asarray(g, np.float64), np.asarray(r, np.float64)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    d = np.abs(g - r)
+    nw, mr = d.max() / max(np.abs(r).max(), 1e-30), d.mean() / max(np.abs(r).mean(), 1e-30)
+    assert nw <= normwise and mr <= mean_rel, f"{what}: normwise {nw:.3e}, mean relative {mr:.3e}"
+
+
+def _ln_bwd_gpu(R, gamma, dY, dRes=None):
+    rows, h = R.shape
+    dX = torch.full((rows, h), float("nan"), dtype=torch.float32, device=DEV)
+    dg = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    db = torch.full((h,), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tp.layernorm_bwd_workspace(rows, h), dtype=torch.uint8, device=DEV)
+    tp.layernorm_bwd(f32_dev(R), f32_dev(gamma), f32_dev(dY), dX, dg, db, ws,
+                     dRes=None if dRes is None else f32_dev(dRes))
+    return dX, dg, db
+
+
+@pytest.mark.parametrize("rows,h,res", [(37, 8, False), (5, 328, True), (64, 1032, False), (3, 12288, True),
+                                        (2, 18432, False), (100, 24576, False), (256, 12288, True)])
+def test_layernorm_bwd(rows, h, res):
+    inp = sp_inputs(rows, h, seed=900 + h + rows, sigma_r=2.0)
+    rng = np.random.default_rng(901 + h)
+    dY = rng.standard_normal((rows, h)).astype(np.float32)
+    dRes = rng.standard_normal((rows, h)).astype(np.float32) if res else None
+    R = inp["R"] + np.float32(0.5)
+    note(f"layernorm_bwd rows={rows} h={h} dRes={res}")
+    dX, dg, db = _ln_bwd_gpu(R, inp["gamma"], dY, dRes)
+    torch.cuda.synchronize()
+    r = seqpar.layernorm_bwd(R.astype(np.float64), inp["gamma"], dY)
+    want = r["dX"] + (dRes if res else 0.0)
+    _close_f32(f64_host(dX), want, "dX")
+    _close_f32(f64_host(dg), r["dgamma"], "dgamma")
+    _close_f32(f64_host(db), r["dbeta"], "dbeta")
+
+
+def test_dropout_bwd():
+    for rows, h, drop in [(3, 8, False), (17, 72, True), (256, 12288, True)]:
+        note(f"sp_dropout_bwd rows={rows} h={h} dropout={drop}")
+        rng = np.random.default_rng(950 + h)
+        dY = rng.standard_normal((rows, h)).astype(np.float32)
+        keep = (rng.random((rows, h)) < 0.9).astype(np.uint8) if drop else None
+        out = torch.empty(rows, h, dtype=torch.bfloat16, device=DEV)
+        tp.sp_dropout_bwd(f32_dev(dY), out, keep=None if keep is None else torch.from_numpy(keep).to(DEV),
+                          keep_prob=0.9)
+        torch.cuda.synchronize()
+        r = seqpar.dropout_bwd(dY, keep, 0.9)
+        g = f64_host(out)
+        assert np.all(np.abs(g - r) <= _bf16_spacing(r)), "dropout_bwd beyond one bf16 spacing"
+        if drop:
+            assert np.all(g[keep == 0] == 0.0)
+
+
+@pytest.mark.parametrize("N", [2, 4])
+def test_sp_mlp_block_backward(N):
+    """The whole sequence-parallel block backward composed from the C ABI:
+    dropout backward -> all-gather -> MLP backward per rank -> reduce-scatter ->
+    LayerNorm backward with the residual path, against the float64 oracle."""
+    s, h, f_full, p = 256, 1024, 4096, 0.9
+    sp = sp_inputs(s, h, seed=960 + N, keep_prob=p)
+    mi = mlp_inputs(s, h, f_full, N, "bf16", 970 + N, 1.0, 0.02, None)
+    dRo = np.random.default_rng(980 + N).standard_normal((s, h)).astype(np.float32)
+    from tests.gpu_util import bf16_dev
+    from oracle.bf16 import bf16_bits_to_f64
+    rows = s // N
+    note(f"sequence-parallel block backward s={s} h={h} N={N}")
+    shards_dev = [(bf16_dev(A), bf16_dev(B)) for A, B in mi["shards"]]
+    X, _ = _sp_block_gpu(sp["R"], sp["gamma"], sp["beta"], shards_dev, sp["keep"], p, N)
+    kd = torch.from_numpy(sp["keep"]).to(DEV)
+    dRd = f32_dev(dRo)
+    sl = [torch.empty(rows, h, dtype=torch.bfloat16, device=DEV) for _ in range(N)]
+    for i in range(N):
+        rs = slice(i * rows, (i + 1) * rows)
+        tp.sp_dropout_bwd(dRd[rs], sl[i], keep=kd[rs], keep_prob=p)
+    dZ = torch.empty(s, h, dtype=torch.bfloat16, device=DEV)
+    tp.sp_all_gather(sl, dZ)
+    dXp, dAs, dBs = [], [], []
+    for A, B in shards_dev:
+        f = A.shape[1]
+        U = torch.empty(s, f, dtype=torch.bfloat16, device=DEV)
+        Y = torch.empty(s, f, dtype=torch.bfloat16, device=DEV)
+        Z = torch.empty(s, h, dtype=torch.float32, device=DEV)
+        tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
+        dX = torch.empty(s, h, dtype=torch.float32, device=DEV)
+        dA = torch.empty(h, f, dtype=torch.float32, device=DEV)
+        dB = torch.empty(f, h, dtype=torch.float32, device=DEV)
+        ws = torch.empty(tp.mlp_bwd_workspace(s, h, f), dtype=torch.uint8, device=DEV)
+        tp.mlp_bwd(X, A, B, U, Y, dZ, dX, dA, dB, ws)
+        dXp.append(dX)
+        dAs.append(dA)
+        dBs.append(dB)
+    Rd, gd = f32_dev(sp["R"]), f32_dev(sp["gamma"])
+    dR = torch.empty(s, h, dtype=torch.float32, device=DEV)
+    dgs, dbs = [], []
+    lws = torch.empty(tp.layernorm_bwd_workspace(rows, h), dtype=torch.uint8, device=DEV)
+    for i in range(N):
+        rs = slice(i * rows, (i + 1) * rows)
+        dL = torch.empty(rows, h, dtype=torch.float32, device=DEV)
+        tp.sp_reduce_scatter(dXp, i, None, dL)
+        dg = torch.empty(h, dtype=torch.float32, device=DEV)
+        db = torch.empty(h, dtype=torch.float32, device=DEV)
+        tp.layernorm_bwd(Rd[rs], gd, dL, dR[rs], dg, db, lws, dRes=dRd[rs])
+        dgs.append(dg)
+        dbs.append(db)
+    dgam = torch.empty(h, dtype=torch.float32, device=DEV)
+    dbet = torch.empty(h, dtype=torch.float32, device=DEV)
+    tp.shard_sum(dgs, dgam)
+    tp.shard_sum(dbs, dbet)
+    torch.cuda.synchronize()
+    shards = [(bf16_bits_to_f64(A), bf16_bits_to_f64(B)) for A, B in mi["shards"]]
+    want = seqpar.sp_mlp_block_bwd(sp["R"].astype(np.float64), sp["gamma"], sp["beta"], shards, dRo, sp["keep"], p,
+                                   matched=True)
+    _close_rel(f64_host(dZ), want["dZ"], "gathered dZ")
+    _close_rel(f64_host(dR) - dRo, want["dR"] - dRo, "dR (through LayerNorm)")
+    _close_rel(f64_host(dgam), want["dgamma"], "dgamma")
+    _close_rel(f64_host(dbet), want["dbeta"], "dbeta")
+    for j in range(N):
+        _close_rel(f64_host(dAs[j]), want["dA"][j], f"dA_{j}")
+        _close_rel(f64_host(dBs[j]), want["dB"][j], f"dB_{j}")
