@@ -240,8 +240,18 @@ def next_rows(tp, torch, dev, randn, reps=5):
     parts = [randn((Ss, Hs), 1.0, 63 + i, torch.float32) for i in range(Ns)]
     keep = (torch.rand(rs_rows, Hs, generator=torch.Generator().manual_seed(71)) < 0.9).to(torch.uint8).to(dev)
     Ro = torch.empty_like(Rr)
+    dYs = randn((rs_rows, Hs), 1.0, 72, torch.float32)
+    dRs = randn((rs_rows, Hs), 1.0, 73, torch.float32)
+    dXs = torch.empty_like(dYs)
+    dgs = torch.empty(Hs, dtype=torch.float32, device=dev)
+    dbs = torch.empty_like(dgs)
+    lws = torch.empty(tp.layernorm_bwd_workspace(rs_rows, Hs), dtype=torch.uint8, device=dev)
+    dZs = torch.empty(rs_rows, Hs, dtype=torch.bfloat16, device=dev)
     sp_rows = (
         ("sp_layernorm", lambda: tp.layernorm(Rr, gam, bet, Ls[0]), rs_rows * Hs * (4 + 2) + 2 * Hs * 4),
+        ("sp_layernorm_bwd", lambda: tp.layernorm_bwd(Rr, gam, dYs, dXs, dgs, dbs, lws, dRes=dRs),
+         rs_rows * Hs * 16 + 3 * Hs * 4),
+        ("sp_dropout_bwd", lambda: tp.sp_dropout_bwd(dYs, dZs, keep=keep, keep_prob=0.9), rs_rows * Hs * 7),
         ("sp_all_gather", lambda: tp.sp_all_gather(Ls, Xg), 2 * Ss * Hs * 2),
         ("sp_reduce_scatter", lambda: tp.sp_reduce_scatter(parts, 3, Rr, Ro, keep=keep, keep_prob=0.9),
          rs_rows * Hs * (4 * Ns + 4 + 1 + 4)),
@@ -260,7 +270,7 @@ def next_rows(tp, torch, dev, randn, reps=5):
         gbs = nbytes / (ms * 1e-3) / 1e9
         out[name] = {"ms": round(ms, 4), "bytes": nbytes, "gbs": round(gbs, 1),
                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
-    del Rr, gam, bet, Ls, Xg, parts, keep, Ro
+    del Rr, gam, bet, Ls, Xg, parts, keep, Ro, dYs, dRs, dXs, dgs, dbs, lws, dZs
     torch.cuda.empty_cache()
     return out
 
