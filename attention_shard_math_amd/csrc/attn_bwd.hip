@@ -534,6 +534,7 @@ hipError_t launch_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO
     max_nc = max(max_nc, max(nq, nk));
   }
   if (max_nc > 1 && L.q_bytes == 0) return hipErrorInvalidValue;
+  if ((int64_t)BH * max(items_q, items_k) > 0x7fffffffLL) return hipErrorInvalidValue;  // grid.x range
   const float scale = 1.f / sqrtf((float)D), scale_log2 = kLog2e * scale;
   hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, dO, O, Dws, s, Hl, D, rows);
   hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, kNW>), dim3((unsigned)((int64_t)BH * items_k)), dim3(kNW * 64), 0, st,
