@@ -126,6 +126,7 @@ def test_full_size_gpt3_shard_backward():
     torch.cuda.synchronize()
     r = oracle.attn_shard_bwd(*(bf16_bits_to_f64(ai[k]) for k in ("X", "Wqkv", "Wo")), bf16_bits_to_f64(dOut),
                               b, s, Hl, d, True, matched=True)
+    assert_grad_close(f64_host(out), r["fwd"]["out"], "out_partial (all elements)")
     assert_grad_close(f64_host(dWo), r["dWo"], "dWo_i")
     assert_grad_close(f64_host(dWqkv), r["dWqkv"], "dWqkv_i")
     assert_grad_close(f64_host(dX), r["dX"], "dX_i")

@@ -175,6 +175,16 @@ class TestConfig3FullSize:
         for k, t in g.items():
             assert torch.isfinite(t.float()).all(), k
 
+    def test_every_element(self, case):
+        """All of U, Y, Z, dX, dA, dB against the float64 oracle over the whole shard."""
+        o, g = case
+        f = oracle.mlp_fwd_shard(o["X"], o["A"], o["B"])
+        for k in ("U", "Y", "Z"):
+            assert_bf16_close(f64_host(g[k]), f[k], f"{k} (all elements)")
+        b = oracle.mlp_bwd_shard(o["X"], o["A"], o["B"], f["U"], f["Y"], o["dZ"])
+        for k in ("dX", "dA", "dB"):
+            assert_bf16_close(f64_host(g[k]), b[k], f"{k} (all elements)")
+
 
 @pytest.mark.parametrize("M,h,f", [(32, 1024, 2048), (300, 512, 768), (1, 64, 128)])
 def test_backward_recompute_matches_saved(M, h, f):
