@@ -248,6 +248,16 @@ class TestPalmShape:
         assert_bf16_close(f64_host(g["dB"][cols, :]), s["dB_rows"], "dB rows")
         assert_bf16_close(f64_host(g["dX"][rows, :]), s["dX_rows"], "dX rows")
 
+    def test_every_element(self, case):
+        """All outputs of the PaLM-shaped shard (backward through recompute)."""
+        o, g = case
+        f = oracle.mlp_fwd_shard(o["X"], o["A"], o["B"])
+        for k in ("U", "Y", "Z"):
+            assert_bf16_close(f64_host(g[k]), f[k], f"{k} (all elements)")
+        b = oracle.mlp_bwd_shard(o["X"], o["A"], o["B"], f["U"], f["Y"], o["dZ"])
+        for k in ("dX", "dA", "dB"):
+            assert_bf16_close(f64_host(g[k]), b[k], f"{k} (all elements)")
+
     def test_outputs_finite(self, case):
         _, g = case
         for k, t in g.items():

@@ -120,8 +120,8 @@ def test_zero_table_gives_log_v():
 
 def test_full_size_sampled_rows():
     """GPT-3 vocabulary (50304 = 8 x 6288), h = 12288, 2048 rows, all eight
-    slices run on the GPU; the oracle recomputes a sample of rows over the whole
-    vocabulary."""
+    slices run on the GPU; the oracle recomputes sampled rows' logits, then
+    every row's partial sums and loss over the whole vocabulary."""
     c = CONFIGS[7]
     M, h, v, N = c["b"] * c["s"], c["h"], c["v"], c["N"]
     inp = ce_inputs(M, h, v, c["seed"], c["sigma_h"], c["sigma_w"])
@@ -157,3 +157,13 @@ def test_full_size_sampled_rows():
     held = np.stack([f64_host(x) for x in ts])
     assert np.all((held != 0).sum(axis=0) <= 1)
     assert abs(float(tot.item()) - g_rows.sum()) <= LOSS_SUM_RTOL * abs(g_rows.sum())
+    # every row: the oracle over the whole vocabulary, slice by slice
+    Hall = bf16_bits_to_f64(inp["H"])
+    full = [oracle.vocab_ce_partials(Hall, bf16_bits_to_f64(inp["E"][i * w:(i + 1) * w]), t, i * w, (i + 1) * w)
+            for i in range(N)]
+    for i in range(N):
+        np.testing.assert_allclose(f64_host(ss[i]), full[i]["sumexp"], rtol=SUMEXP_RTOL, atol=0)
+        np.testing.assert_allclose(f64_host(ts[i]), full[i]["tlogit"], rtol=0, atol=LOGIT_ATOL)
+    want_all = oracle.vocab_ce_combine([x["sumexp"] for x in full], [x["tlogit"] for x in full])
+    np.testing.assert_allclose(g_rows, want_all["loss_rows"], rtol=0, atol=LOSS_ATOL)
+    assert abs(float(tot.item()) - want_all["loss"]) <= LOSS_SUM_RTOL * abs(want_all["loss"])
