@@ -25,9 +25,13 @@
 // DMA of the ring and wait for it. A wave blocked issuing memory instructions
 // (the texture unit accepts them at its own rate) thus never holds up the MFMA
 // stream of its SIMD; each SIMD runs two MFMA waves and one DMA wave.
-// Workgroups are dispatched round-robin over the 8 XCDs; the tile index is
-// remapped so each XCD owns a contiguous range of tiles (shared operand panels
-// stay in that XCD's L2).
+// The grid is persistent: 256 workgroups (one per CU; the LDS ring allows no
+// more), each walking a list of tiles with the ring running on from one tile's
+// last k-stage into the next tile's first, so the DMA of the next tile overlaps
+// the current tile's epilogue instead of waiting for a new workgroup's launch.
+// Workgroups are dispatched round-robin over the 8 XCDs; XCD x owns a contiguous
+// range of tiles, which its 32 workgroups take round-robin (shared operand
+// panels stay in that XCD's L2).
 #include "common.hpp"
 #include "gemm_bf16.hpp"
 
@@ -44,6 +48,7 @@ constexpr int NPW = 4;                  // DMA waves
 constexpr int NT = 64 * (NCW + NPW);    // threads per workgroup
 constexpr int NS = 5;                   // LDS ring depth
 constexpr uint32_t kOOB = 0x7ffffff0u;  // buffer offset that reads as zero
+constexpr int kGrid = 256;              // persistent grid: one workgroup per CU
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (expcnt and lgkmcnt left unconstrained): vmcnt in bits [3:0] and
@@ -187,13 +192,14 @@ void gemm_bf16_kernel(GemmArgs g) {
   // ---- tile index: XCD-contiguous remap, then column-major over tiles
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int T = tiles_m * tiles_n;
-  int w = blockIdx.x;
-  {
-    const int xcd = w & 7, idx = w >> 3, base = T >> 3, rem = T & 7;
-    w = xcd * base + (xcd < rem ? xcd : rem) + idx;
-  }
-  const int tm = w % tiles_m, tn = w / tiles_m;
-  const int m0 = tm * BM, n0 = tn * BN;
+  // Persistent grid: XCD x (blockIdx % 8) owns a contiguous range of tiles, which its
+  // workgroups take round-robin; the LDS ring runs on across a workgroup's tiles.
+  const int per = gridDim.x >> 3, xcd = blockIdx.x & 7, jw = blockIdx.x >> 3;
+  const int tbase = T >> 3, trem = T & 7;
+  const int r0 = xcd * tbase + (xcd < trem ? xcd : trem), rn = tbase + (xcd < trem ? 1 : 0);
+  const int ntl = jw < rn ? (rn - jw + per - 1) / per : 0;
+  auto tile_m0 = [&](int i) { return ((r0 + jw + i * per) % tiles_m) * BM; };
+  auto tile_n0 = [&](int i) { return ((r0 + jw + i * per) / tiles_m) * BN; };
 
   // Buffer resources cover each operand exactly; the host checks sizes < 2 GiB.
   const int64_t a_elems = A_K ? (int64_t)g.M * g.lda : (int64_t)g.K * g.lda;
@@ -202,28 +208,34 @@ void gemm_bf16_kernel(GemmArgs g) {
   const i32x4 rb = make_rsrc(g.B, (uint32_t)(b_elems * 2));
 
   const int nk = (g.K + BK - 1) / BK;
+  const int total = ntl * nk;
   const uint32_t a_lds = lds_addr(&sA[0][0]), b_lds = lds_addr(&sB[0][0]);
   if (wave >= NCW) {
     // ---- DMA waves: stages 0 .. NS-2 in flight, then one refill per stage.
     const int pw = wave - NCW;
     Dma<BM, A_K> da;
     Dma<BN, B_K> db;
-    da.init(m0, g.M, g.lda, pw, lane);
-    db.init(n0, g.N, g.ldb, pw, lane);
-#pragma unroll
-    for (int st = 0; st < NS - 1; ++st) {
-      if (st < nk) {
-        da.issue(ra, a_lds + st * SA * 2, g.lda, st * BK, g.K, pw);
-        db.issue(rb, b_lds + st * SB * 2, g.ldb, st * BK, g.K, pw);
+    int itile = -1;
+    auto issue_stage = [&](int gs, int sl) __attribute__((always_inline)) {
+      const int ti = gs / nk, kt = gs - ti * nk;
+      if (ti != itile) {
+        da.init(tile_m0(ti), g.M, g.lda, pw, lane);
+        db.init(tile_n0(ti), g.N, g.ldb, pw, lane);
+        itile = ti;
       }
-    }
+      da.issue(ra, a_lds + sl * SA * 2, g.lda, kt * BK, g.K, pw);
+      db.issue(rb, b_lds + sl * SB * 2, g.ldb, kt * BK, g.K, pw);
+    };
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < total) issue_stage(st, st);
     int slot = 0;
-    for (int t = 0; t < nk; ++t) {
+    for (int t = 0; t < total; ++t) {
       // Stage t complete for this wave: at most the DMA of the later stages
       // already issued may be outstanding. The barrier then makes every DMA
       // wave's part visible, and tells that the MFMA waves are done with stage
       // t-1, whose slot is refilled below.
-      const int after = min(t + NS - 2, nk - 1) - t;
+      const int after = min(t + NS - 2, total - 1) - t;
       if (after >= 3)
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA_OPS));
       else if (after == 2)
@@ -237,72 +249,69 @@ void gemm_bf16_kernel(GemmArgs g) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      if (t + NS - 1 < nk) {
-        const int ws = slot == 0 ? NS - 1 : slot - 1;
-        da.issue(ra, a_lds + ws * SA * 2, g.lda, (t + NS - 1) * BK, g.K, pw);
-        db.issue(rb, b_lds + ws * SB * 2, g.ldb, (t + NS - 1) * BK, g.K, pw);
-      }
+      if (t + NS - 1 < total) issue_stage(t + NS - 1, slot == 0 ? NS - 1 : slot - 1);
       slot = slot == NS - 1 ? 0 : slot + 1;
     }
     return;
   }
 
   // ---- MFMA waves
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
   const int am = wm * WTM, bn = wn * WTN;
-  int slot = 0;
-  for (int t = 0; t < nk; ++t) {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    const uint16_t* a_s = sA[slot];
-    const uint16_t* b_s = sB[slot];
-    // Fragments double-buffered over the stage's k-steps.
-    constexpr int NKK = BK / 16;
-    bf16x8 fa[2][TM], fb[2][TN];
-#pragma unroll
-    for (int i = 0; i < TM; ++i) fa[0][i] = frag<BM, A_K>(a_s, am + i * 32, 0, lane);
-#pragma unroll
-    for (int j = 0; j < TN; ++j) fb[0][j] = frag<BN, B_K>(b_s, bn + j * 32, 0, lane);
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const int cb = kk & 1;
-      if (kk + 1 < NKK) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i) fa[cb ^ 1][i] = frag<BM, A_K>(a_s, am + i * 32, kk + 1, lane);
-#pragma unroll
-        for (int j = 0; j < TN; ++j) fb[cb ^ 1][j] = frag<BN, B_K>(b_s, bn + j * 32, kk + 1, lane);
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
-    }
-    slot = slot == NS - 1 ? 0 : slot + 1;
-  }
-
-  // ---- epilogue
   const int fk = lane >> 5, fr = lane & 31;
+  int slot = 0;
+  for (int it = 0; it < ntl; ++it) {
+    f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
-      store_tile<EPI>(acc[i][j], g, m0 + am + i * 32 + 4 * fk, n0 + bn + j * 32 + fr);
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int t = 0; t < nk; ++t) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const uint16_t* a_s = sA[slot];
+      const uint16_t* b_s = sB[slot];
+      constexpr int NKK = BK / 16;
+      bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[0][i] = frag<BM, A_K>(a_s, am + i * 32, 0, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[0][j] = frag<BN, B_K>(b_s, bn + j * 32, 0, lane);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int cb = kk & 1;
+        if (kk + 1 < NKK) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) fa[cb ^ 1][i] = frag<BM, A_K>(a_s, am + i * 32, kk + 1, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[cb ^ 1][j] = frag<BN, B_K>(b_s, bn + j * 32, kk + 1, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+      }
+      slot = slot == NS - 1 ? 0 : slot + 1;
+    }
+    const int m0 = tile_m0(it), n0 = tile_n0(it);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        store_tile<EPI>(acc[i][j], g, m0 + am + i * 32 + 4 * fk, n0 + bn + j * 32 + fr);
+  }
 }
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI>), dim3(tiles), dim3(NT), 0, s, g);
+  // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split
+  const int grid = tiles >= kGrid ? kGrid : ((tiles + 7) & ~7);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI>), dim3(grid), dim3(NT), 0, s, g);
   return hipGetLastError();
 }
 
