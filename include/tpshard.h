@@ -13,13 +13,21 @@
  *     row/column splits with their backward (g's backward copies dZ to every rank,
  *     f's backward adds the ranks' input gradients); 三、Self-Attention层 §3.1 —
  *     column split of the Q, K, V weights by whole heads, head count divisible
- *     by the rank count; 四、Embedding层 §4.1 — vocabulary-parallel input
- *     embedding that zeroes ids a rank does not hold.
+ *     by the rank count; 三、§3.2 — the layer's backward and its two all-reduces;
+ *     四、Embedding层 §4.1 — vocabulary-parallel input embedding that zeroes ids a
+ *     rank does not hold; §4.2 — the output layer through the same row-split table;
+ *     五、Cross-Entropy层 — the loss from per-rank sums of exp, without gathering
+ *     the logits; 二、§2.2 — an all-reduce is a reduce-scatter plus an all-gather.
+ *   www.discosf.com/news/5875844, 2.3 序列并行与激活重计算 — LayerNorm and Dropout
+ *     on each rank's slice of the sequence; activation recompute in the backward.
  *   "Megatron-LM 介绍" (apxml.com), 核心贡献 item 1 — ColumnParallelLinear.
  *
  * Common conventions for every call:
  *   - Tensor arguments are DEVICE pointers owned by the caller, row-major and
- *     contiguous, 16-byte aligned. Nothing is allocated or freed by the library.
+ *     contiguous, 16-byte aligned. Nothing is allocated or freed by the library,
+ *     no call synchronises or clears memory, and every call may be recorded in a
+ *     HIP graph. Scratch memory comes from caller workspaces sized by the
+ *     matching *_workspace() function.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream of
  *     the current device. Work is enqueued asynchronously on it; the call returns
  *     after the launches, not after the kernels finish.
