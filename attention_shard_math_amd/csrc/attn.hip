@@ -9,9 +9,17 @@
 // only move data: they load the next 64-key stage from global memory into
 // registers (buffer loads, which read as zero past the last key) and write it
 // to LDS, K as [key][d] and V transposed to [d][key] through a register
-// transpose, while the compute waves work on the current stage (two LDS slots,
-// one barrier per stage). Each SIMD thus runs one compute wave, whose MFMAs and
-// softmax arithmetic overlap with the other wave's loads and LDS writes.
+// transpose, while the compute waves work on the current stage (three LDS
+// slots, one barrier per stage). Each SIMD thus runs one compute wave, whose
+// MFMAs and softmax arithmetic overlap with the other wave's loads and LDS
+// writes.
+//
+// The compute wave is software-pipelined by one stage: the scores of stage
+// i + 1 (whose K is already in LDS) are issued in the same basic block as the
+// softmax of stage i, so the MFMA unit works on them while the VALU forms
+// exp2 and the bf16 P of stage i; the P V product of stage i follows. The
+// order of every accumulation is unchanged, so the output is bit-identical to
+// the unpipelined schedule.
 //
 // The compute wave forms the transposed scores S^T = K Q^T and the transposed
 // output O^T = V^T P^T with v_mfma_f32_32x32x16_bf16, so that in both
@@ -83,7 +91,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
   constexpr int NVT = (KVB / 8) * (D / 4);  // V tasks of 8 keys x 4 d
   constexpr int SK = KVB * D;               // elements per K (and per V^T) stage
   static_assert(KPER >= 1 && NVT <= NP && NVT % 64 == 0, "stage shape");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * SK];  // [slot][K | V^T]
+  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * 2 * SK];  // [slot][K | V^T], stage i in slot i % 3
 
   const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (item >= n_items) return;
@@ -152,13 +160,19 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
         }
       }
     };
+    // Stages 0 and 1 are in LDS before the compute waves start; during the
+    // compute waves' stage i the loaders write stage i + 2 and fetch stage i + 3.
     load_kv(0);
     store_kv(0);
-    if (nkv > 1) load_kv(KVB);
+    if (nkv > 1) {
+      load_kv(KVB);
+      store_kv(1);
+    }
+    if (nkv > 2) load_kv(2 * KVB);
     __syncthreads();
     for (int it = 0; it < nkv; ++it) {
-      if (it + 1 < nkv) store_kv((it + 1) & 1);
-      if (it + 2 < nkv) load_kv((it + 2) * KVB);
+      if (it + 2 < nkv) store_kv((it + 2) % 3);
+      if (it + 3 < nkv) load_kv((it + 3) * KVB);
       __syncthreads();
     }
     return;
@@ -185,43 +199,35 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
   float m_i = kNegInf;  // exponent reference of the row (scaled scores, log2 units)
   float l_i = 0.f;      // this lane-half's share of the row sum
 
-  __syncthreads();
-  for (int it = 0; it < nkv; ++it) {
-    const int kv0 = it * KVB;
-    const uint16_t* sK = smem + (it & 1) * 2 * SK;
-    const uint16_t* sV = sK + SK;
-    // Wave-uniform: skip the stage if its first key is above the diagonal or past the end.
-    if (!((CAUSAL && kv0 > qw) || kv0 >= s)) {
-      // K fragments of both 32-key tiles, then S^T = K Q^T.
-      bf16x8 kf[2][KS];
+  // S^T = K Q^T of one stage (two 32-key tiles), K fragments read as used.
+  auto scores = [&](const uint16_t* sK, f32x16(&st)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) st[t][e] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const int kr = 32 * t + lr;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          kf[t][ks] = *reinterpret_cast<const bf16x8*>(sK + kr * D + (((2 * ks + hh) ^ swz_k<D>(kr)) << 3));
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + kr * D + (((2 * ks + hh) ^ swz_k<D>(kr)) << 3));
+        st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], st[t], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 st[2];
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) st[t][e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) st[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t][ks], qf[ks], st[t], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // V^T fragments of tile 0 (16-key groups 0 and 1).
-      bf16x8 vf[2][DT];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-        for (int i = 0; i < DT; ++i) {
-          const int d = 32 * i + lr;
-          vf[s2][i] = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((2 * s2 + hh) ^ swz_v(d)) << 3));
-        }
-      __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // Software pipeline: while the softmax of stage i runs on the VALU, the scores
+  // of stage i + 1 run on the MFMA unit (its K is already in LDS).
+  f32x16 sc[2];
+  __syncthreads();
+  scores(smem, sc);
+  for (int it = 0; it < nkv; ++it) {
+    const int kv0 = it * KVB;
+    const uint16_t* sV = smem + (it % 3) * 2 * SK + SK;
+    // K of the next stage; on the last stage a stale slot whose scores go unused.
+    const uint16_t* sKn = smem + ((it + 1) % 3) * 2 * SK;
+    f32x16 sn[2];
+    // Wave-uniform: skip the stage if its first key is above the diagonal or past the end.
+    if (!((CAUSAL && kv0 > qw) || kv0 >= s)) {
       // S^T accumulator lane (lr, hh), reg e of tile t: key kv0 + 32t + 8(e/4) + 4hh + e%4, query qrow.
       if ((CAUSAL && kv0 + KVB - 1 > qw) || kv0 + KVB > s) {
         // key - (kv0 + 4hh) = 32t + 8(e/4) + e%4 may not exceed lim.
@@ -230,11 +236,11 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
         for (int t = 0; t < 2; ++t)
 #pragma unroll
           for (int e = 0; e < 16; ++e)
-            if (32 * t + 8 * (e >> 2) + (e & 3) > lim) st[t][e] = kNegInf;
+            if (32 * t + 8 * (e >> 2) + (e & 3) > lim) sc[t][e] = kNegInf;
       }
-      float mx = fmaxf(st[0][0], st[1][0]);
+      float mx = fmaxf(sc[0][0], sc[1][0]);
 #pragma unroll
-      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(st[0][e], st[1][e]));
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sc[0][e], sc[1][e]));
       const float mt = xhalf_max(mx) * scale_log2;
       // Raise the reference only when some row's maximum has passed it by more
       // than kTau; rows that have not keep their reference (factor 1).
@@ -250,42 +256,40 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
       }
       const float mref = m_i == kNegInf ? 0.f : m_i;
       float rs = 0.f;
+      bf16x8 pb[2][2];
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        bf16x8 pb[2];
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
           u32x4 u;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
-            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][8 * s2 + 2 * w], scale_log2, -mref));
-            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(st[t][8 * s2 + 2 * w + 1], scale_log2, -mref));
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w], scale_log2, -mref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w + 1], scale_log2, -mref));
             rs += p0 + p1;
             u[w] = cvt_bf16x2(p0, p1);
           }
-          pb[s2] = __builtin_bit_cast(bf16x8, u);
+          pb[t][s2] = __builtin_bit_cast(bf16x8, u);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        // O^T += V^T P^T over the 16-key groups 2t + s2; P^T lane (lr, hh) holds
-        // keys {4hh + 0..3, 8 + 4hh + 0..3} of the group = V^T chunk 2(2t + s2) + hh.
+      scores(sKn, sn);
+      // O^T += V^T P^T over the 16-key groups 2t + s2; P^T lane (lr, hh) holds
+      // keys {4hh + 0..3, 8 + 4hh + 0..3} of the group = V^T chunk 2(2t + s2) + hh.
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-          for (int i = 0; i < DT; ++i) ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s2][i], pb[s2], ot[i], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (t == 0) {
-#pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-            for (int i = 0; i < DT; ++i) {
-              const int d = 32 * i + lr;
-              vf[s2][i] = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((4 + 2 * s2 + hh) ^ swz_v(d)) << 3));
-            }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      }
+          for (int i = 0; i < DT; ++i) {
+            const int d = 32 * i + lr;
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((4 * t + 2 * s2 + hh) ^ swz_v(d)) << 3));
+            ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][s2], ot[i], 0, 0, 0);
+          }
       l_i += rs;
+    } else {
+      scores(sKn, sn);
     }
+    sc[0] = sn[0];
+    sc[1] = sn[1];
     __syncthreads();
   }
 

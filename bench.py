@@ -108,6 +108,32 @@ def traffic_from_profiles(key: str):
         return None
 
 
+def hbm_ceilings(torch, dev, reps=10):
+    """Practical HBM rates of plain runtime kernels at the sizes the bandwidth rows
+    move, for reading their fractions against: a fill of the gather's 402.65 MB
+    output (write only) and a 1 GiB device copy (read + write, larger than the
+    256 MB Infinity Cache). Each figure is `reps` back-to-back launches between
+    two HIP events on the current stream, so the cache's write-back is included
+    (a lone launch can leave part of its writes in the cache)."""
+    out = {}
+    fill = torch.empty(16384 * 12288, dtype=torch.bfloat16, device=dev)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for name, fn, nbytes in (("write_fill_402MB", lambda: fill.zero_(), fill.numel() * 2),
+                             ("copy_1GiB", lambda: dst.copy_(src), 2 * src.numel() * 4)):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[name] = {"ms": round(ms, 4), "gbs": round(nbytes / ms / 1e6, 1)}
+    del fill, src, dst
+    return out
+
+
 def next_rows(tp, torch, dev, randn, reps=5):
     """Rows beyond the step, timed on their own after it: the PaLM-shaped MLP shard
     (M=2048, h=18432, f=9216), forward with saved U, backward with activation
@@ -416,6 +442,7 @@ def main():
     }
     if not args.no_next:
         rec["next_rows"] = next_rows(tp, torch, dev, randn)
+        rec["hbm_ceilings"] = hbm_ceilings(torch, dev)
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline()
     if args.copy_probe:
