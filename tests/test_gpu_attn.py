@@ -30,6 +30,25 @@ def test_attn_core(b, s, Hl, d, causal):
     assert_bf16_close(f64_host(O), ref, "O")
 
 
+# The kernel keeps up to three 64-key stages of K and V in LDS: sequences of one,
+# two, three and four stages, and lengths one key past a stage boundary, exercise
+# every start-up and drain path of that ring.
+@pytest.mark.parametrize("s", [63, 64, 65, 128, 129, 192, 193, 256, 257])
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True)])
+def test_attn_core_stage_counts(s, d, causal):
+    note(f"attn_core stages s={s} d={d} causal={causal}")
+    b, Hl = 1, 2
+    rng = np.random.default_rng(500 + s + d)
+    qkv = bf16_bits(draw_normal_f32(rng, (b * s, 3 * Hl * d), 1.0))
+    O = torch.empty(b * s, Hl * d, dtype=torch.bfloat16, device=DEV)
+    tp.attn_core(bf16_dev(qkv), O, b, s, Hl, d, causal)
+    torch.cuda.synchronize()
+    q = bf16_bits_to_f64(qkv)
+    w = Hl * d
+    ref = oracle.attn_core(q[:, :w], q[:, w:2 * w], q[:, 2 * w:], b, s, Hl, d, causal)
+    assert_bf16_close(f64_host(O), ref, "O")
+
+
 @pytest.mark.parametrize("b,s,h,Hl,d", [(2, 300, 512, 2, 128), (1, 150, 256, 4, 64)])
 def test_attn_fwd_ragged(b, s, h, Hl, d):
     note(f"attn_fwd b={b} s={s} h={h} Hl={Hl} d={d}")
