@@ -2,6 +2,7 @@
 // launches on the caller's stream. No allocation, no synchronisation, no
 // exceptions across the interface. The operations and their citations are
 // documented in include/tpshard.h.
+#include <initializer_list>
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -78,6 +79,17 @@ tp_status check_opt_ptr(const char* fn, const char* name, const void* p) {
   } while (0)
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// Stream-K area of a bf16 GEMM (0 when its tiles fill whole rounds of the grid).
+size_t sk_need(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || M > kMaxDim || N > kMaxDim || K > kMaxDim) return 0;
+  return tps::gemm_bf16_sk_workspace((int)M, (int)N, (int)K);
+}
+size_t sk_max(std::initializer_list<size_t> v) {
+  size_t m = 0;
+  for (size_t x : v) m = x > m ? x : m;
+  return m;
+}
 
 tps::GemmArgs make_args(const void* A, int64_t lda, const void* B, int64_t ldb, int64_t M, int64_t N, int64_t K,
                         void* C, int64_t ldc) {
@@ -170,16 +182,21 @@ TP_API tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f, const 
   return tp_row_linear(dt, M, f, h, Y_i, B_i, Z_i, stream);
 }
 
+namespace {
+// Stream-K area shared by the four backward GEMMs (they run one after another).
+size_t mlp_bwd_sk(int64_t M, int64_t h, int64_t f) {
+  return sk_max({sk_need(M, f, h), sk_need(f, h, M), sk_need(h, f, M), sk_need(M, h, f)});
+}
+}  // namespace
+
 TP_API size_t tp_mlp_bwd_workspace(int64_t M, int64_t h, int64_t f) {
-  (void)h;
   if (M < 0 || f < 0) return 0;
-  return round256((size_t)M * (size_t)f * 2);
+  return round256((size_t)M * (size_t)f * 2) + mlp_bwd_sk(M, h, f);
 }
 
 TP_API size_t tp_mlp_bwd_recompute_workspace(int64_t M, int64_t h, int64_t f) {
-  (void)h;
   if (M < 0 || f < 0) return 0;
-  return 3 * round256((size_t)M * (size_t)f * 2);
+  return 3 * round256((size_t)M * (size_t)f * 2) + mlp_bwd_sk(M, h, f);
 }
 
 TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, const void* A_i, const void* B_i,
@@ -208,6 +225,9 @@ TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, cons
   TRY(check_opt_ptr(fn, "ws", ws));
   hipStream_t s = as_stream(stream);
   uint16_t* dU = static_cast<uint16_t*>(ws);
+  // the stream-K area follows the activations
+  void* sk = mlp_bwd_sk(M, h, f) ? static_cast<char*>(ws) + (recompute ? 3 : 1) * round256((size_t)M * (size_t)f * 2)
+                                 : nullptr;
   if (recompute) {
     const size_t act = round256((size_t)M * (size_t)f * 2);
     uint16_t* U_re = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + act);
@@ -221,18 +241,22 @@ TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, cons
     tps::GemmArgs g = make_args(dZ, h, B_i, h, M, f, h, dU, f);
     g.Uin = static_cast<const uint16_t*>(U_i);
     g.ldu = f;
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_DGELU, s), fn));
   }
   if (dB_i) {  // dB = Y^T dZ: A(m,k) = Y[k, m] (M-contig), B(k,n) = dZ[k, n] (N-contig)
     tps::GemmArgs g = make_args(Y_i, f, dZ, h, f, h, M, dB_i, h);
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, s), fn));
   }
   if (dA_i) {  // dA = X^T dU: A(m,k) = X[k, m], B(k,n) = dU[k, n]
     tps::GemmArgs g = make_args(X, h, dU, f, h, f, M, dA_i, f);
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, s), fn));
   }
   if (dX_i && M > 0) {  // dX = dU A_i^T: A = dU [M,f] (K-contig), B(k,n) = A_i[n, k] (K-contig)
     tps::GemmArgs g = make_args(dU, f, A_i, f, M, h, f, dX_i, h);
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_F32, s), fn));
   }
   return ok();
@@ -375,11 +399,18 @@ TP_API tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, i
                     fn);
 }
 
+namespace {
+// Stream-K area shared by the attention backward's four GEMMs.
+size_t attn_bwd_sk(int64_t M, int64_t h, int64_t w) {
+  return sk_max({sk_need(w, h, M), sk_need(M, w, h), sk_need(h, 3 * w, M), sk_need(M, h, 3 * w)});
+}
+}  // namespace
+
 TP_API size_t tp_attn_bwd_workspace(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head) {
-  (void)h;
   if (b < 0 || s < 0 || n_heads_local < 0 || d_head < 0) return 0;
   const size_t t = (size_t)b * (size_t)s, w = (size_t)n_heads_local * (size_t)d_head;
-  return round256(t * w * 2) + round256(t * 3 * w * 2) + tp_attn_core_bwd_workspace(b, s, n_heads_local);
+  return round256(t * w * 2) + round256(t * 3 * w * 2) + round256(tp_attn_core_bwd_workspace(b, s, n_heads_local)) +
+         attn_bwd_sk(b * s, h, n_heads_local * d_head);
 }
 
 TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head, int causal,
@@ -412,13 +443,16 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   uint16_t* dO = reinterpret_cast<uint16_t*>(wsb);
   uint16_t* dqkv = reinterpret_cast<uint16_t*>(wsb + round256((size_t)M * w * 2));
   void* core_ws = wsb + round256((size_t)M * w * 2) + round256((size_t)M * 3 * w * 2);
+  void* sk = static_cast<char*>(core_ws) + round256(tp_attn_core_bwd_workspace(b, s, n_heads_local));
   {  // dWo_i = O^T dOut: A(m,k) = O[k, m], B(k,n) = dOut[k, n]
     tps::GemmArgs g = make_args(O, w, dOut, h, w, h, M, dWo_i, h);
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, st), fn));
   }
   if (M > 0) {
     {  // dO = dOut Wo_i^T: A = dOut [M,h] (K-contig), B(k,n) = Wo_i[n, k] (K-contig)
       tps::GemmArgs g = make_args(dOut, h, Wo_i, h, M, w, h, dO, w);
+      tps::gemm_bf16_sk_attach(g, sk);
       TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_BF16, st), fn));
     }
     TRY(hip_status(tps::attn_bwd(static_cast<const uint16_t*>(QKV), static_cast<const uint16_t*>(O), dO, lse, dqkv,
@@ -427,10 +461,12 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   }
   {  // dWqkv_i = X^T dQKV: A(m,k) = X[k, m], B(k,n) = dQKV[k, n]
     tps::GemmArgs g = make_args(X, h, dqkv, 3 * w, h, 3 * w, M, dWqkv_i, 3 * w);
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, false, false, tps::EPI_F32, st), fn));
   }
   if (M > 0) {  // dX_i = dQKV Wqkv_i^T: A = dQKV [M,3w] (K-contig), B(k,n) = Wqkv_i[n, k] (K-contig)
     tps::GemmArgs g = make_args(dqkv, 3 * w, Wqkv_i, 3 * w, M, h, 3 * w, dX_i, h);
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_F32, st), fn));
   }
   return ok();
@@ -438,7 +474,8 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
 
 TP_API size_t tp_vocab_ce_workspace(int64_t M, int64_t lo, int64_t hi) {
   if (M < 0 || lo < 0 || hi <= lo) return 0;
-  return round256((size_t)M * (size_t)(hi - lo) * 4);
+  // the stream-K area (if the logits GEMM uses one) follows the logits
+  return round256((size_t)M * (size_t)(hi - lo) * 4) + sk_need(M, hi - lo, 1);
 }
 
 TP_API tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t hi, const void* H, const void* E_i,
@@ -464,6 +501,7 @@ TP_API tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t 
   float* logits = static_cast<float*>(ws);
   // logits_i = H E_i^T: A = H [M,h] (K-contig), B(k,n) = E_i[n, k] (K-contig).
   tps::GemmArgs g = make_args(H, h, E_i, h, M, V, h, logits, V);
+  tps::gemm_bf16_sk_attach(g, static_cast<char*>(ws) + round256((size_t)M * (size_t)V * 4));
   TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_F32, st), fn));
   return hip_status(tps::ce_rows(logits, M, (int)V, targets, lo, sumexp_i, tlogit_i, st), fn);
 }

@@ -49,6 +49,16 @@ constexpr int NT = 64 * (NCW + NPW);    // threads per workgroup
 constexpr int NS = 5;                   // LDS ring depth
 constexpr uint32_t kOOB = 0x7ffffff0u;  // buffer offset that reads as zero
 constexpr int kGrid = 256;              // persistent grid: one workgroup per CU
+constexpr int kBM = 256, kBN = 192;     // tile of every product
+
+// Stream-K is used when the tiles fill at most half of one round of the grid:
+// then at least half the CUs would idle for the whole product, which costs more
+// than moving the float32 partials of the split tiles (192 KB per contributor
+// and tile). With more tiles that traffic cancels the gain (measured).
+constexpr int kSkMaxTiles = kGrid / 2;
+__host__ __device__ constexpr bool sk_applies(int64_t tiles, int K) {
+  return K > 0 && tiles > 0 && tiles <= kSkMaxTiles && tiles * ((K + BK - 1) / BK) < (int64_t(1) << 30);
+}
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
 // outstanding (expcnt and lgkmcnt left unconstrained): vmcnt in bits [3:0] and
@@ -355,10 +365,217 @@ void gemm_bf16_kernel(GemmArgs g) {
   }
 }
 
+// ---------------------------------------------------------------- stream-K
+// Used when the tile count does not fill whole rounds of the 256 workgroups.
+// The T x nk (tile, k-stage) units, tiles in the order above, are cut into 256
+// equal runs, one per workgroup (XCD-contiguous: workgroup b has virtual index
+// v = (b % 8) * 32 + b / 8). A tile whose units all fall in one run is finished
+// as in the tile kernel. A tile split over c runs: each MFMA wave of every
+// contributor writes its float32 accumulators to the workspace slot of its run
+// (2 slots per run: its first and its last segment), fences, and increments the
+// tile's counter for that wave; the wave that brings the counter to c adds the
+// c partials in run order (its own from registers) and runs the epilogue. No
+// wave ever waits for another workgroup, and the sum order does not depend on
+// which contributor arrives last, so the result is reproducible.
+template <int BM, int BN, bool A_K, bool B_K, int EPI>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void gemm_bf16_sk_kernel(GemmArgs g) {
+  constexpr int WM = NCW / 2, WN = 2;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int SA = BM * BK, SB = BN * BK;
+  constexpr int DMA_OPS = (BM + BN) / 16 / NPW;
+  constexpr int64_t SLOT = (int64_t)BM * BN / 2;  // 8-byte float pairs per workspace slot
+  static_assert((NS - 2) * DMA_OPS < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint16_t sA[NS][SA];
+  __shared__ __attribute__((aligned(1024))) uint16_t sB[NS][SB];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int nk = (g.K + BK - 1) / BK;
+  const int U = tiles_m * tiles_n * nk;  // the host keeps U below 2^31
+  const int G = gridDim.x;
+  const int v = (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
+  const int per = (U + G - 1) / G;
+  const int g0 = min(U, v * per), g1 = min(U, g0 + per);
+  const int total = g1 - g0;
+  auto tile_m0 = [&](int t) { return (t % tiles_m) * BM; };
+  auto tile_n0 = [&](int t) { return (t / tiles_m) * BN; };
+  // first tile of run u (its slot 0 holds the partial of that tile)
+  auto first_tile = [&](int u) { return u * per / nk; };
+
+  const int64_t a_elems = A_K ? (int64_t)g.M * g.lda : (int64_t)g.K * g.lda;
+  const int64_t b_elems = B_K ? (int64_t)g.N * g.ldb : (int64_t)g.K * g.ldb;
+  const i32x4 ra = make_rsrc(g.A, (uint32_t)(a_elems * 2));
+  const i32x4 rb = make_rsrc(g.B, (uint32_t)(b_elems * 2));
+  const uint32_t a_lds = lds_addr(&sA[0][0]), b_lds = lds_addr(&sB[0][0]);
+
+  if (wave >= NCW) {
+    // ---- DMA waves: the same ring as the tile kernel, over this run's units.
+    const int pw = wave - NCW;
+    Dma<BM, A_K> da;
+    Dma<BN, B_K> db;
+    int itile = -1;
+    auto issue_stage = [&](int st, int sl) __attribute__((always_inline)) {
+      const int gs = g0 + st;
+      const int ti = gs / nk, kt = gs - ti * nk;
+      if (ti != itile) {
+        da.init(tile_m0(ti), g.M, g.lda, pw, lane);
+        db.init(tile_n0(ti), g.N, g.ldb, pw, lane);
+        itile = ti;
+      }
+      da.issue(ra, a_lds + sl * SA * 2, g.lda, kt * BK, g.K, pw);
+      db.issue(rb, b_lds + sl * SB * 2, g.ldb, kt * BK, g.K, pw);
+    };
+#pragma unroll
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < total) issue_stage(st, st);
+    int slot = 0;
+    for (int t = 0; t < total; ++t) {
+      const int after = min(t + NS - 2, total - 1) - t;
+      if (after >= 3)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DMA_OPS));
+      else if (after == 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * DMA_OPS));
+      else if (after == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(DMA_OPS));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      if (t + NS - 1 < total) issue_stage(t + NS - 1, slot == 0 ? NS - 1 : slot - 1);
+      slot = slot == NS - 1 ? 0 : slot + 1;
+    }
+    return;
+  }
+
+  // ---- MFMA waves: one segment (a tile's k-range inside this run) at a time.
+  const int am = wm * WTM, bn = wn * WTN;
+  const int fk = lane >> 5, fr = lane & 31;
+  uint64_t* part = reinterpret_cast<uint64_t*>(g.sk_part);
+  const int64_t wofs = (int64_t)wave * TM * TN * 8 * 64;  // this wave's float pairs inside a slot
+  int slot = 0;
+  int gs = g0;
+  while (gs < g1) {
+    const int ti = gs / nk;
+    const int kb = gs - ti * nk;
+    const int ke = min(nk, g1 - ti * nk);
+    f32x16 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int t = kb; t < ke; ++t) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const uint16_t* a_s = sA[slot];
+      const uint16_t* b_s = sB[slot];
+      constexpr int NKK = BK / 16;
+      bf16x8 fa[2][TM], fb[2][TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) fa[0][i] = frag<BM, A_K>(a_s, am + i * 32, 0, lane);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) fb[0][j] = frag<BN, B_K>(b_s, bn + j * 32, 0, lane);
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int cb = kk & 1;
+        if (kk + 1 < NKK) {
+#pragma unroll
+          for (int i = 0; i < TM; ++i) fa[cb ^ 1][i] = frag<BM, A_K>(a_s, am + i * 32, kk + 1, lane);
+#pragma unroll
+          for (int j = 0; j < TN; ++j) fb[cb ^ 1][j] = frag<BN, B_K>(b_s, bn + j * 32, kk + 1, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cb][i], fb[cb][j], acc[i][j], 0, 0, 0);
+      }
+      slot = slot == NS - 1 ? 0 : slot + 1;
+    }
+    const int m0 = tile_m0(ti), n0 = tile_n0(ti);
+    bool finish = true;
+    if (kb != 0 || ke != nk) {
+      // Split tile: publish this wave's partial, then count arrivals. The partials
+      // are written and read with device-scope (L2-coherent across XCDs) 8-byte
+      // accesses, so no cache-wide write-back or invalidate is needed: the writer
+      // waits for its stores to complete before its relaxed increment.
+      const int ua = ti * nk;
+      const int vf = ua / per, vl = (ua + nk - 1) / per;
+      const int c = vl - vf + 1;
+      uint64_t* mine = part + (2LL * v + (ti == first_tile(v) ? 0 : 1)) * SLOT + wofs;
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint64_t x = (uint64_t)__float_as_uint(acc[i][j][2 * e]) |
+                               ((uint64_t)__float_as_uint(acc[i][j][2 * e + 1]) << 32);
+            __hip_atomic_store(mine + ((i * TN + j) * 8 + e) * 64 + lane, x, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      int old = 0;
+      if (lane == 0)
+        old = __hip_atomic_fetch_add(g.sk_cnt + ti * NCW + wave, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      old = __shfl(old, 0);
+      finish = old == c - 1;
+      if (finish) {
+        // Every contributor's partial, this wave's own included (read back), in run order.
+        for (int jj = 0; jj < c; ++jj) {
+          const int u = vf + jj;
+          const uint64_t* src = part + (2LL * u + (ti == first_tile(u) ? 0 : 1)) * SLOT + wofs;
+#pragma unroll
+          for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+              for (int e = 0; e < 8; ++e) {
+                const uint64_t x = __hip_atomic_load(src + ((i * TN + j) * 8 + e) * 64 + lane, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                const float lo = __uint_as_float((uint32_t)x), hi = __uint_as_float((uint32_t)(x >> 32));
+                acc[i][j][2 * e] = jj == 0 ? lo : acc[i][j][2 * e] + lo;
+                acc[i][j][2 * e + 1] = jj == 0 ? hi : acc[i][j][2 * e + 1] + hi;
+              }
+        }
+      }
+    }
+    if (finish) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          store_tile<EPI>(acc[i][j], g, m0 + am + i * 32 + 4 * fk, n0 + bn + j * 32 + fr,
+                          m0 + am + i * 32 + 32 <= g.M && n0 + bn + j * 32 + 32 <= g.N);
+    }
+    gs = ti * nk + ke;
+  }
+}
+
+// Zeroes the stream-K arrival counters (a kernel, so the launch can be captured
+// in a HIP graph).
+__global__ __launch_bounds__(256) void sk_zero_kernel(int* cnt, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) cnt[i] = 0;
+}
+
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
+  if (g.sk_part && g.sk_cnt && sk_applies(tiles, g.K)) {
+    const int n = tiles * NCW;
+    hipLaunchKernelGGL(sk_zero_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0, s, g.sk_cnt, n);
+    hipLaunchKernelGGL((gemm_bf16_sk_kernel<BM, BN, A_K, B_K, EPI>), dim3(kGrid), dim3(NT), 0, s, g);
+    return hipGetLastError();
+  }
   // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split
   const int grid = tiles >= kGrid ? kGrid : ((tiles + 7) & ~7);
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, A_K, B_K, EPI>), dim3(grid), dim3(NT), 0, s, g);
@@ -367,8 +584,13 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
 
 }  // namespace
 
+size_t gemm_bf16_sk_workspace(int M, int N, int K) {
+  const int64_t tiles = (int64_t)((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+  return sk_applies(tiles, K) ? kSkBytes : 0;
+}
+
 hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, int epi, hipStream_t s) {
-  constexpr int BM = 256, BN = 192;
+  constexpr int BM = kBM, BN = kBN;
   // buffer loads address each operand with 32-bit byte offsets
   const int64_t a_bytes = 2 * (a_kcontig ? (int64_t)g.M * g.lda : (int64_t)g.K * g.lda);
   const int64_t b_bytes = 2 * (b_kcontig ? (int64_t)g.N * g.ldb : (int64_t)g.K * g.ldb);

@@ -211,8 +211,9 @@ def next_rows(tp, torch, dev, randn, reps=5):
     del Hh, E, tg, sums, tls, ws, rows, tot
     torch.cuda.empty_cache()
 
-    # Attention backward at the GPT-3 shard (12 heads x 128, s = 2048, h = 12288):
-    # the core alone and the whole shard (Wo, Wqkv and input-gradient GEMMs).
+    # Attention at the GPT-3 shard (12 heads x 128, s = 2048, h = 12288): the forward
+    # core alone (the step times the whole shard), and the backward, core alone and
+    # whole shard (Wo, Wqkv and input-gradient GEMMs).
     Ha, Hla, Da, Sa = 12288, 12, 128, 2048
     wa = Hla * Da
     Xa = randn((Sa, Ha), 1.0, 80)
@@ -231,9 +232,12 @@ def next_rows(tp, torch, dev, randn, reps=5):
     dWqkv = torch.empty(Ha, 3 * wa, dtype=torch.float32, device=dev)
     dWo = torch.empty(wa, Ha, dtype=torch.float32, device=dev)
     wsb = torch.empty(tp.attn_bwd_workspace(1, Sa, Ha, Hla, Da), dtype=torch.uint8, device=dev)
+    Oc = torch.empty_like(Oa)
+    core_fwd_gflop = 2 * 2 * Da * Hla * Sa * (Sa + 1) / 2 / 1e9  # S and P V, causal pairs
     core_gflop = 5 * 2 * Da * Hla * Sa * (Sa + 1) / 2 / 1e9  # dV, dP, dQ, dK + the S recompute, causal pairs
     shard_gflop = core_gflop + (2 * gemm_flops(Sa, wa, Ha) + 2 * gemm_flops(Sa, 3 * wa, Ha)) / 1e9
     for name, fn, gf in (
+            ("attn_core_fwd", lambda: tp.attn_core(QKV, Oc, 1, Sa, Hla, Da, True), core_fwd_gflop),
             ("attn_core_bwd", lambda: tp.attn_core_bwd(QKV, Oa, dOa, lse, dQKV, wsc, 1, Sa, Hla, Da, True), core_gflop),
             ("attn_shard_bwd", lambda: tp.attn_bwd(Xa, Wqkv, Wo, QKV, Oa, lse, dOut, dXa, dWqkv, dWo, wsb, 1, Sa,
                                                    Hla, Da, True), shard_gflop)):
@@ -250,7 +254,7 @@ def next_rows(tp, torch, dev, randn, reps=5):
         tf = gf * 1e9 / (ms * 1e-3) / 1e12
         out[name] = {"ms": round(ms, 4), "gflop": round(gf, 2), "tflops": round(tf, 1),
                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
-    del Xa, Wqkv, Wo, dOut, outp, QKV, Oa, lse, dOa, dQKV, wsc, dXa, dWqkv, dWo, wsb
+    del Xa, Wqkv, Wo, dOut, outp, QKV, Oa, Oc, lse, dOa, dQKV, wsc, dXa, dWqkv, dWo, wsb
     torch.cuda.empty_cache()
 
     # Sequence parallelism at the GPT-3 shard: one rank's LayerNorm over its 256
@@ -340,9 +344,8 @@ def main():
     Xa = randn((ATT_B * ATT_S, H), 1.0, 20)
     Wqkv = randn((H, 3 * w), 0.006, 21)
     Wo = randn((w, H), 0.006, 22)
-    QKV = torch.empty(ATT_B * ATT_S, 3 * w, dtype=torch.bfloat16, device=dev)
-    O = torch.empty(ATT_B * ATT_S, w, dtype=torch.bfloat16, device=dev)
     out_att = torch.empty(ATT_B * ATT_S, H, dtype=torch.float32, device=dev)
+    ws_att = torch.empty(tp.attn_fwd_workspace(ATT_B, ATT_S, ATT_HL, ATT_D), dtype=torch.uint8, device=dev)
     # ---- vocab shard 0 of 8
     per = V // VN
     E0 = randn((per, H), 0.02, 30)
@@ -356,18 +359,15 @@ def main():
         ("mlp_row_gemm", lambda: tp.row_linear(Y, B, Z)),
         ("mlp_bwd", lambda: tp.mlp_bwd(X, A, B, U, Y, dZ, dX, dA, dB, ws)),
         ("shard_sum", lambda: tp.shard_sum(parts, Zsum)),
-        ("attn_qkv_gemm", lambda: tp.column_linear(Xa, Wqkv, QKV, act=None)),
-        ("attn_core", lambda: tp.attn_core(QKV, O, ATT_B, ATT_S, ATT_HL, ATT_D, True)),
-        ("attn_wo_gemm", lambda: tp.row_linear(O, Wo, out_att)),
+        ("attn_shard", lambda: tp.attn_fwd(Xa, Wqkv, Wo, out_att, ws_att, ATT_B, ATT_S, ATT_HL, ATT_D, True)),
         ("vocab_gather", lambda: tp.vocab_embed(ids, E0, 0, per, emb)),
     ]
     flops = {
         "mlp_col_gemm_gelu": gemm_flops(M, F, H),
         "mlp_row_gemm": gemm_flops(M, H, F),
         "mlp_bwd": 4 * gemm_flops(M, F, H),
-        "attn_qkv_gemm": gemm_flops(ATT_B * ATT_S, 3 * w, H),
-        "attn_core": 2 * 2.0 * ATT_HL * ATT_D * ATT_B * (ATT_S * (ATT_S + 1) / 2),
-        "attn_wo_gemm": gemm_flops(ATT_B * ATT_S, H, w),
+        "attn_shard": gemm_flops(ATT_B * ATT_S, 3 * w, H) + 2 * 2.0 * ATT_HL * ATT_D * ATT_B * (ATT_S * (ATT_S + 1) / 2)
+        + gemm_flops(ATT_B * ATT_S, H, w),
     }
     hbm_bytes = {
         "shard_sum": (N_PARTIALS + 1) * M * H * 4.0,

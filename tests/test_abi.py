@@ -16,6 +16,10 @@ lib = tp.lib
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 P = 0x10000          # a fake, 16-byte aligned "device" pointer: never dereferenced
 MIS = 0x10002        # misaligned
+# Stream-K area a workspace includes when one of its GEMMs has at most 128 tiles of
+# 256 x 192 (half a round of the 256-workgroup grid): two float32 tile slots per
+# workgroup, then arrival counters for up to 128 tiles x 8 MFMA waves.
+SK_BYTES = 2 * 256 * 256 * 192 * 4 + 128 * 8 * 4
 
 
 def declared_functions():
@@ -65,12 +69,15 @@ class TestValidation:
     def test_mlp_bwd(self):
         M, h, f = 32, 64, 128
         need = lib.tp_mlp_bwd_workspace(M, h, f)
-        assert need == M * f * 2 and need % 256 == 0
-        assert lib.tp_mlp_bwd_workspace(3, 8, 8) == 256
+        # dU, then the stream-K area (these products have fewer tiles than the grid)
+        assert need == M * f * 2 + SK_BYTES and need % 256 == 0
+        assert lib.tp_mlp_bwd_workspace(3, 8, 8) == 256 + SK_BYTES
+        # 2048 x 6144 / 6144 x 12288 / 12288 x 6144 / 2048 x 12288 have >= 256 tiles: no area
+        assert lib.tp_mlp_bwd_workspace(2048, 12288, 6144) == 2048 * 6144 * 2
         b = lib.tp_mlp_bwd
         # U_i (or Y_i) NULL selects activation recompute, which needs the larger workspace
         need_re = lib.tp_mlp_bwd_recompute_workspace(M, h, f)
-        assert need_re == 3 * need
+        assert need_re == 3 * M * f * 2 + SK_BYTES
         assert b(M, h, f, P, P, P, None, P, P, P, P, P, P, need, None) == WORKSPACE
         assert b(M, h, f, P, P, P, P, None, P, P, P, P, P, need_re - 1, None) == WORKSPACE
         assert b(M, h, f, P, P, P, None, None, None, P, P, P, P, need_re, None) == INVALID  # dZ NULL
@@ -85,7 +92,8 @@ class TestValidation:
         assert lib.tp_attn_core(1, 16, 0, 128, 1, P, P, None) == INVALID
         assert lib.tp_attn_core(-1, 16, 2, 128, 1, P, P, None) == INVALID
         ws = lib.tp_attn_fwd_workspace(2, 100, 3, 64)
-        assert ws == 2 * 100 * 9 * 64 * 2 + 2 * 100 * 3 * 64 * 2 + (-(2 * 100 * 9 * 64 * 2) % 256) + (-(2 * 100 * 3 * 64 * 2) % 256)
+        assert ws == (2 * 100 * 9 * 64 * 2 + 2 * 100 * 3 * 64 * 2 + (-(2 * 100 * 9 * 64 * 2) % 256)
+                      + (-(2 * 100 * 3 * 64 * 2) % 256))
         assert lib.tp_attn_fwd(2, 100, 256, 3, 64, 1, P, P, P, P, P, ws - 16, None) == WORKSPACE
         assert lib.tp_attn_fwd(2, 100, 260, 3, 64, 1, P, P, P, P, P, ws, None) == UNSUPPORTED  # h % 8
 
@@ -101,7 +109,8 @@ class TestValidation:
         assert cb(0, 16, 2, 128, 1, None, None, None, None, None, None, 0, None) == OK
         need = lib.tp_attn_bwd_workspace(1, 64, 256, 2, 64)
         t, w = 64, 128
-        assert need == -(-t * w * 2 // 256) * 256 + -(-t * 3 * w * 2 // 256) * 256 + lib.tp_attn_core_bwd_workspace(1, 64, 2)
+        assert need == (-(-t * w * 2 // 256) * 256 + -(-t * 3 * w * 2 // 256) * 256
+                        + -(-lib.tp_attn_core_bwd_workspace(1, 64, 2) // 256) * 256 + SK_BYTES)
         b = lib.tp_attn_bwd
         args = [P] * 10  # X, Wqkv_i, Wo_i, QKV, O, lse, dOut, dX_i, dWqkv_i, dWo_i
         assert b(1, 64, 256, 2, 64, 1, *args, P, need - 1, None) == WORKSPACE
@@ -125,8 +134,9 @@ class TestValidation:
     def test_vocab_ce(self):
         M, h, lo, hi = 16, 64, 40, 104
         need = lib.tp_vocab_ce_workspace(M, lo, hi)
-        assert need == M * (hi - lo) * 4 and need % 256 == 0
-        assert lib.tp_vocab_ce_workspace(3, 0, 8) == 256
+        assert need == M * (hi - lo) * 4 + SK_BYTES and need % 256 == 0
+        assert lib.tp_vocab_ce_workspace(3, 0, 8) == 256 + SK_BYTES
+        assert lib.tp_vocab_ce_workspace(2048, 0, 6288) == 2048 * 6288 * 4  # 264 tiles: no area
         assert lib.tp_vocab_ce_workspace(3, 8, 8) == 0
         c = lib.tp_vocab_ce_partials
         assert c(M, h, 10, 10, P, P, P, P, P, P, need, None) == INVALID          # lo == hi

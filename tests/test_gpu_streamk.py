@@ -1,0 +1,57 @@
+"""GPU checks of the stream-K path of the bf16 GEMM, used when a product has at most
+128 tiles of 256 x 192 (half a round of the 256-workgroup grid) and the call has a
+workspace. The vocabulary-parallel logits GEMM of tp_vocab_ce_partials leaves its
+float32 output at the start of the workspace, so it can be compared with the same
+product from the tile kernel (tp_row_linear against E_i^T): every k-range must be
+summed exactly once whatever the split, and repeated calls are bit-identical
+although a split tile is finished by whichever contributing workgroup arrives last."""
+import pytest
+import torch
+
+from tests.gpu_util import DEV, note
+
+pytestmark = pytest.mark.gpu
+
+tp = pytest.importorskip("attention_shard_math_amd")
+
+
+def _logits_streamk(H, E, lo, hi):
+    M = H.shape[0]
+    V = hi - lo
+    tgt = torch.zeros(M, dtype=torch.int32, device=DEV)
+    se = torch.empty(M, dtype=torch.float32, device=DEV)
+    tl = torch.empty(M, dtype=torch.float32, device=DEV)
+    ws = torch.empty(tp.vocab_ce_workspace(M, lo, hi), dtype=torch.uint8, device=DEV)
+    tp.vocab_ce_partials(H, E, tgt, lo, hi, se, tl, ws)
+    torch.cuda.synchronize()
+    return ws[: M * V * 4].view(torch.float32).view(M, V).clone()
+
+
+# (M, h, V): 2 tiles split 16 ways; 64 tiles split 4 ways; 2 tiles split 128 ways
+# (contributors on two XCDs); and 120 tiles, each split over two or three runs.
+@pytest.mark.parametrize("M,h,V", [(300, 512, 136), (2048, 2048, 1536), (64, 12288, 384), (1920, 4096, 2880)])
+def test_streamk_matches_tile_kernel(M, h, V):
+    note(f"stream-K logits M={M} h={h} V={V}")
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M + h + V)
+    H = torch.randn(M, h, generator=g, device=DEV).to(torch.bfloat16)
+    E = (torch.randn(V, h, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    lo = 8 * V
+    sk = _logits_streamk(H, E, lo, lo + V)
+    tile = torch.empty(M, V, dtype=torch.float32, device=DEV)
+    tp.row_linear(H, E.t().contiguous(), tile)    # 'N'-layout product, tile kernel (no workspace)
+    torch.cuda.synchronize()
+    err = float((sk.double() - tile.double()).abs().max() / tile.double().abs().max())
+    assert err < 1e-5, err
+
+
+def test_streamk_repeatable():
+    note("stream-K repeatability")
+    M, h, V = 64, 12288, 384
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5)
+    H = torch.randn(M, h, generator=g, device=DEV).to(torch.bfloat16)
+    E = (torch.randn(V, h, generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    runs = [_logits_streamk(H, E, 0, V) for _ in range(3)]
+    for r in runs[1:]:
+        assert torch.equal(r, runs[0])
