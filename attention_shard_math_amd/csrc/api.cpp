@@ -301,10 +301,17 @@ TP_API tp_status tp_attn_core_train(int64_t b, int64_t s, int64_t n_heads_local,
                     fn);
 }
 
+namespace {
+// Stream-K area of the attention forward's QKV and Wo GEMMs. The workspace query has
+// no h, which sets the Wo GEMM's tile count, so the area is reserved whenever there
+// is work.
+size_t attn_fwd_sk(int64_t M, int64_t w) { return M > 0 && w > 0 ? tps::kSkBytes : 0; }
+}  // namespace
+
 TP_API size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head) {
   if (b < 0 || s < 0 || n_heads_local < 0 || d_head < 0) return 0;
   const size_t t = (size_t)b * (size_t)s, w = (size_t)n_heads_local * (size_t)d_head;
-  return round256(t * 3 * w * 2) + round256(t * w * 2);
+  return round256(t * 3 * w * 2) + round256(t * w * 2) + attn_fwd_sk(b * s, n_heads_local * d_head);
 }
 
 TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head, int causal,
@@ -327,13 +334,16 @@ TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   hipStream_t st = as_stream(stream);
   uint16_t* qkv = static_cast<uint16_t*>(ws);
   uint16_t* O = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + round256((size_t)M * 3 * w * 2));
+  void* sk = static_cast<char*>(ws) + round256((size_t)M * 3 * w * 2) + round256((size_t)M * w * 2);
   {
     tps::GemmArgs g = make_args(X, h, Wqkv_i, 3 * w, M, 3 * w, h, qkv, 3 * w);
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, true, false, tps::EPI_BF16, st), fn));
   }
   TRY(hip_status(tps::attn_fwd(qkv, O, (int)b, (int)s, (int)n_heads_local, (int)d_head, causal != 0, st), fn));
   {
     tps::GemmArgs g = make_args(O, w, Wo_i, h, M, h, w, out_partial, h);
+    tps::gemm_bf16_sk_attach(g, sk);
     TRY(hip_status(tps::gemm_bf16(g, true, false, tps::EPI_F32, st), fn));
   }
   return ok();

@@ -51,13 +51,15 @@ constexpr uint32_t kOOB = 0x7ffffff0u;  // buffer offset that reads as zero
 constexpr int kGrid = 256;              // persistent grid: one workgroup per CU
 constexpr int kBM = 256, kBN = 192;     // tile of every product
 
-// Stream-K is used when the tiles fill at most half of one round of the grid:
-// then at least half the CUs would idle for the whole product, which costs more
-// than moving the float32 partials of the split tiles (192 KB per contributor
-// and tile). With more tiles that traffic cancels the gain (measured).
-constexpr int kSkMaxTiles = kGrid / 2;
+// Stream-K is used when the last round of tiles fills at most half of the grid,
+// for up to kSkMaxTiles tiles. With a fuller last round the split does not pay:
+// the GEMMs run power-limited, so the CUs that would idle mostly let the busy ones
+// clock higher, while the split adds the partials' traffic and a second kernel
+// (measured: a 192-tile product took 6% longer, a 264-tile one 5% less).
+constexpr int kSkMaxTiles = 4096;
 __host__ __device__ constexpr bool sk_applies(int64_t tiles, int K) {
-  return K > 0 && tiles > 0 && tiles <= kSkMaxTiles && tiles * ((K + BK - 1) / BK) < (int64_t(1) << 30);
+  return K > 0 && tiles > 0 && tiles % kGrid != 0 && tiles % kGrid <= kGrid / 2 && tiles <= kSkMaxTiles &&
+         tiles * ((K + BK - 1) / BK) < (int64_t(1) << 30);
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
@@ -366,17 +368,16 @@ void gemm_bf16_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------- stream-K
-// Used when the tile count does not fill whole rounds of the 256 workgroups.
-// The T x nk (tile, k-stage) units, tiles in the order above, are cut into 256
-// equal runs, one per workgroup (XCD-contiguous: workgroup b has virtual index
+// Used when the last round of tiles would fill at most half of the 256
+// workgroups (see sk_applies). The
+// T x nk (tile, k-stage) units, tiles in the order above, are cut into 256 equal
+// runs, one per workgroup (XCD-contiguous: workgroup b has virtual index
 // v = (b % 8) * 32 + b / 8). A tile whose units all fall in one run is finished
-// as in the tile kernel. A tile split over c runs: each MFMA wave of every
-// contributor writes its float32 accumulators to the workspace slot of its run
-// (2 slots per run: its first and its last segment), fences, and increments the
-// tile's counter for that wave; the wave that brings the counter to c adds the
-// c partials in run order (its own from registers) and runs the epilogue. No
-// wave ever waits for another workgroup, and the sum order does not depend on
-// which contributor arrives last, so the result is reproducible.
+// as in the tile kernel. For a tile split over several runs, each run writes its
+// float32 accumulators to a workspace slot of its own (2 slots per run: its first
+// and its last segment); a second kernel adds a split tile's partials in run order
+// and runs the epilogue. No workgroup waits for another, and the sum order is
+// fixed, so the result is reproducible.
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gemm_bf16_sk_kernel(GemmArgs g) {
@@ -385,7 +386,7 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int SA = BM * BK, SB = BN * BK;
   constexpr int DMA_OPS = (BM + BN) / 16 / NPW;
-  constexpr int64_t SLOT = (int64_t)BM * BN / 2;  // 8-byte float pairs per workspace slot
+  constexpr int64_t SLOT = (int64_t)BM * BN / 4;  // float4 per workspace slot
   static_assert((NS - 2) * DMA_OPS < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint16_t sA[NS][SA];
@@ -456,8 +457,8 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   // ---- MFMA waves: one segment (a tile's k-range inside this run) at a time.
   const int am = wm * WTM, bn = wn * WTN;
   const int fk = lane >> 5, fr = lane & 31;
-  uint64_t* part = reinterpret_cast<uint64_t*>(g.sk_part);
-  const int64_t wofs = (int64_t)wave * TM * TN * 8 * 64;  // this wave's float pairs inside a slot
+  f32x4* part = reinterpret_cast<f32x4*>(g.sk_part);
+  const int64_t wofs = (int64_t)wave * TM * TN * 4 * 64;  // this wave's float4 inside a slot
   int slot = 0;
   int gs = g0;
   while (gs < g1) {
@@ -501,54 +502,20 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
       slot = slot == NS - 1 ? 0 : slot + 1;
     }
     const int m0 = tile_m0(ti), n0 = tile_n0(ti);
-    bool finish = true;
-    if (kb != 0 || ke != nk) {
-      // Split tile: publish this wave's partial, then count arrivals. The partials
-      // are written and read with device-scope (L2-coherent across XCDs) 8-byte
-      // accesses, so no cache-wide write-back or invalidate is needed: the writer
-      // waits for its stores to complete before its relaxed increment.
-      const int ua = ti * nk;
-      const int vf = ua / per, vl = (ua + nk - 1) / per;
-      const int c = vl - vf + 1;
-      uint64_t* mine = part + (2LL * v + (ti == first_tile(v) ? 0 : 1)) * SLOT + wofs;
+    const bool split = kb != 0 || ke != nk;
+    if (split) {
+      // This run's share of a split tile: to its slot, in accumulator order.
+      f32x4* mine = part + (2LL * v + (ti == first_tile(v) ? 0 : 1)) * SLOT + wofs;
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint64_t x = (uint64_t)__float_as_uint(acc[i][j][2 * e]) |
-                               ((uint64_t)__float_as_uint(acc[i][j][2 * e + 1]) << 32);
-            __hip_atomic_store(mine + ((i * TN + j) * 8 + e) * 64 + lane, x, __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-          }
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-      int old = 0;
-      if (lane == 0)
-        old = __hip_atomic_fetch_add(g.sk_cnt + ti * NCW + wave, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      old = __shfl(old, 0);
-      finish = old == c - 1;
-      if (finish) {
-        // Every contributor's partial, this wave's own included (read back), in run order.
-        for (int jj = 0; jj < c; ++jj) {
-          const int u = vf + jj;
-          const uint64_t* src = part + (2LL * u + (ti == first_tile(u) ? 0 : 1)) * SLOT + wofs;
-#pragma unroll
-          for (int i = 0; i < TM; ++i)
-#pragma unroll
-            for (int j = 0; j < TN; ++j)
-#pragma unroll
-              for (int e = 0; e < 8; ++e) {
-                const uint64_t x = __hip_atomic_load(src + ((i * TN + j) * 8 + e) * 64 + lane, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                const float lo = __uint_as_float((uint32_t)x), hi = __uint_as_float((uint32_t)(x >> 32));
-                acc[i][j][2 * e] = jj == 0 ? lo : acc[i][j][2 * e] + lo;
-                acc[i][j][2 * e + 1] = jj == 0 ? hi : acc[i][j][2 * e + 1] + hi;
-              }
-        }
-      }
+          for (int q = 0; q < 4; ++q)
+            mine[((i * TN + j) * 4 + q) * 64 + lane] =
+                f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     }
-    if (finish) {
+    if (!split) {
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -560,20 +527,60 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   }
 }
 
-// Zeroes the stream-K arrival counters (a kernel, so the launch can be captured
-// in a HIP graph).
-__global__ __launch_bounds__(256) void sk_zero_kernel(int* cnt, int n) {
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) cnt[i] = 0;
+// Finishes the split tiles of a stream-K launch: one workgroup per tile, laid out
+// like the MFMA waves of the product kernel (8 waves, the same accumulator tiles per
+// lane), adds the partials of the runs that cover the tile in run order and runs the
+// same epilogue. Workgroups of tiles that one run finished exit at once.
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(64 * NCW) void gemm_bf16_sk_fixup_kernel(GemmArgs g) {
+  constexpr int WM = NCW / 2, WN = 2;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int64_t SLOT = (int64_t)BM * BN / 4;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
+  const int nk = (g.K + BK - 1) / BK;
+  const int U = tiles_m * tiles_n * nk;
+  const int per = (U + kGrid - 1) / kGrid;
+  const int ti = blockIdx.x;
+  const int ua = ti * nk;
+  const int vf = ua / per, vl = (ua + nk - 1) / per;
+  if (vf == vl) return;
+  const f32x4* part = reinterpret_cast<const f32x4*>(g.sk_part);
+  const int64_t wofs = (int64_t)wave * TM * TN * 4 * 64;
+  f32x16 acc[TM][TN];
+  for (int u = vf; u <= vl; ++u) {
+    const f32x4* src = part + (2LL * u + (ti == u * per / nk ? 0 : 1)) * SLOT + wofs;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 x = src[((i * TN + j) * 4 + q) * 64 + lane];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = u == vf ? x[r] : acc[i][j][4 * q + r] + x[r];
+        }
+  }
+  const int m0 = (ti % tiles_m) * BM, n0 = (ti / tiles_m) * BN;
+  const int am = wm * WTM, bn = wn * WTN;
+  const int fk = lane >> 5, fr = lane & 31;
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      store_tile<EPI>(acc[i][j], g, m0 + am + i * 32 + 4 * fk, n0 + bn + j * 32 + fr,
+                      m0 + am + i * 32 + 32 <= g.M && n0 + bn + j * 32 + 32 <= g.N);
 }
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
 hipError_t launch(const GemmArgs& g, hipStream_t s) {
   const int tiles = ((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN);
   if (tiles == 0) return hipSuccess;
-  if (g.sk_part && g.sk_cnt && sk_applies(tiles, g.K)) {
-    const int n = tiles * NCW;
-    hipLaunchKernelGGL(sk_zero_kernel, dim3((n + 255) / 256 < 64 ? (n + 255) / 256 : 64), dim3(256), 0, s, g.sk_cnt, n);
+  if (g.sk_part && sk_applies(tiles, g.K)) {
     hipLaunchKernelGGL((gemm_bf16_sk_kernel<BM, BN, A_K, B_K, EPI>), dim3(kGrid), dim3(NT), 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_sk_fixup_kernel<BM, BN, EPI>), dim3(tiles), dim3(64 * NCW), 0, s, g);
     return hipGetLastError();
   }
   // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split

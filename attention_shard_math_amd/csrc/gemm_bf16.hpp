@@ -25,34 +25,25 @@ struct GemmArgs {
   uint16_t* U;          // EPI_GELU output (nullable)
   const uint16_t* Uin;  // EPI_DGELU input
   int64_t ldu;
-  // Stream-K workspace (nullable): when set and the tiles fill at most half a round
-  // of the persistent grid, the k-stages are split evenly over the workgroups.
-  // sk_part holds gemm_bf16_sk_workspace() bytes of partial tiles, sk_cnt points
-  // into the same area (see gemm_bf16_sk_attach).
+  // Stream-K workspace (nullable): when set and the last round of tiles fills at most
+  // half of the persistent grid, the k-stages are split evenly over the workgroups and
+  // the split tiles' float32 partials go here (kSkBytes, see gemm_bf16_sk_attach).
   float* sk_part = nullptr;
-  int* sk_cnt = nullptr;
 };
 
 // Size of the stream-K area: two float32 256 x 192 tile slots per workgroup of the
-// 256-workgroup grid, then one arrival counter per (tile, MFMA wave) for up to
-// 128 tiles.
-constexpr size_t kSkPartBytes = (size_t)2 * 256 * 256 * 192 * 4;
-constexpr size_t kSkBytes = kSkPartBytes + (size_t)128 * 8 * 4;
+// 256-workgroup grid.
+constexpr size_t kSkBytes = (size_t)2 * 256 * 256 * 192 * 4;
 
 // Workspace bytes a launch of an M x N x K product uses: kSkBytes when it runs
-// stream-K (at most 128 tiles of 256 x 192, half a round of the grid), else 0.
+// stream-K (the last round of its 256 x 192 tiles fills at most half of the
+// 256-workgroup grid; at most 4096 tiles), else 0.
 size_t gemm_bf16_sk_workspace(int M, int N, int K);
 
-// Points g's stream-K fields into `area` (kSkBytes, 256-byte aligned), or clears
-// them when the product does not run stream-K or area is null.
+// Points g's stream-K area at `area` (kSkBytes, 256-byte aligned), or clears it
+// when the product does not run stream-K or area is null.
 inline void gemm_bf16_sk_attach(GemmArgs& g, void* area) {
-  if (area == nullptr || gemm_bf16_sk_workspace(g.M, g.N, g.K) == 0) {
-    g.sk_part = nullptr;
-    g.sk_cnt = nullptr;
-    return;
-  }
-  g.sk_part = static_cast<float*>(area);
-  g.sk_cnt = reinterpret_cast<int*>(static_cast<char*>(area) + kSkPartBytes);
+  g.sk_part = (area != nullptr && gemm_bf16_sk_workspace(g.M, g.N, g.K) != 0) ? static_cast<float*>(area) : nullptr;
 }
 
 hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, int epi, hipStream_t s);

@@ -28,11 +28,12 @@
  *     no call synchronises or clears memory, and every call may be recorded in a
  *     HIP graph. Scratch memory comes from caller workspaces sized by the
  *     matching *_workspace() function. A workspace whose call runs a bf16
- *     product of at most 128 tiles of 256 x 192 output elements also holds that
- *     product's stream-K area (100.8 MB of float32 partial tiles and arrival
- *     counters, after the call's other scratch): its k-range is split over all
- *     256 workgroups and the split tiles are summed in a fixed order, so results
- *     are reproducible. Calls that share one workspace must not overlap in time.
+ *     product whose tiles of 256 x 192 output elements leave the last round of
+ *     the 256-workgroup grid at most half full also holds that product's
+ *     stream-K area (100.7 MB of float32 partial tiles, after the call's other
+ *     scratch): its k-range is split over all 256 workgroups and the split tiles
+ *     are summed in a fixed order, so results are reproducible. Calls that share
+ *     one workspace must not overlap in time.
  *   - `stream` is a hipStream_t passed as void*; NULL means the null stream of
  *     the current device. Work is enqueued asynchronously on it; the call returns
  *     after the launches, not after the kernels finish.

@@ -16,10 +16,10 @@ lib = tp.lib
 OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
 P = 0x10000          # a fake, 16-byte aligned "device" pointer: never dereferenced
 MIS = 0x10002        # misaligned
-# Stream-K area a workspace includes when one of its GEMMs has at most 128 tiles of
-# 256 x 192 (half a round of the 256-workgroup grid): two float32 tile slots per
-# workgroup, then arrival counters for up to 128 tiles x 8 MFMA waves.
-SK_BYTES = 2 * 256 * 256 * 192 * 4 + 128 * 8 * 4
+# Stream-K area a workspace includes when one of its GEMMs has a tile count (tiles of
+# 256 x 192) whose last round fills at most half of the 256-workgroup grid: two
+# float32 tile slots per workgroup.
+SK_BYTES = 2 * 256 * 256 * 192 * 4
 
 
 def declared_functions():
@@ -72,7 +72,7 @@ class TestValidation:
         # dU, then the stream-K area (these products have fewer tiles than the grid)
         assert need == M * f * 2 + SK_BYTES and need % 256 == 0
         assert lib.tp_mlp_bwd_workspace(3, 8, 8) == 256 + SK_BYTES
-        # 2048 x 6144 / 6144 x 12288 / 12288 x 6144 / 2048 x 12288 have >= 256 tiles: no area
+        # 2048 x 6144 / 6144 x 12288 / 12288 x 6144 / 2048 x 12288 fill whole rounds: no area
         assert lib.tp_mlp_bwd_workspace(2048, 12288, 6144) == 2048 * 6144 * 2
         b = lib.tp_mlp_bwd
         # U_i (or Y_i) NULL selects activation recompute, which needs the larger workspace
@@ -93,7 +93,7 @@ class TestValidation:
         assert lib.tp_attn_core(-1, 16, 2, 128, 1, P, P, None) == INVALID
         ws = lib.tp_attn_fwd_workspace(2, 100, 3, 64)
         assert ws == (2 * 100 * 9 * 64 * 2 + 2 * 100 * 3 * 64 * 2 + (-(2 * 100 * 9 * 64 * 2) % 256)
-                      + (-(2 * 100 * 3 * 64 * 2) % 256))
+                      + (-(2 * 100 * 3 * 64 * 2) % 256) + SK_BYTES)
         assert lib.tp_attn_fwd(2, 100, 256, 3, 64, 1, P, P, P, P, P, ws - 16, None) == WORKSPACE
         assert lib.tp_attn_fwd(2, 100, 260, 3, 64, 1, P, P, P, P, P, ws, None) == UNSUPPORTED  # h % 8
 
@@ -136,7 +136,8 @@ class TestValidation:
         need = lib.tp_vocab_ce_workspace(M, lo, hi)
         assert need == M * (hi - lo) * 4 + SK_BYTES and need % 256 == 0
         assert lib.tp_vocab_ce_workspace(3, 0, 8) == 256 + SK_BYTES
-        assert lib.tp_vocab_ce_workspace(2048, 0, 6288) == 2048 * 6288 * 4  # 264 tiles: no area
+        assert lib.tp_vocab_ce_workspace(2048, 0, 6144) == 2048 * 6144 * 4  # 256 tiles: no area
+        assert lib.tp_vocab_ce_workspace(2048, 0, 6288) == 2048 * 6288 * 4 + SK_BYTES  # 264 tiles
         assert lib.tp_vocab_ce_workspace(3, 8, 8) == 0
         c = lib.tp_vocab_ce_partials
         assert c(M, h, 10, 10, P, P, P, P, P, P, need, None) == INVALID          # lo == hi

@@ -1,10 +1,11 @@
-"""GPU checks of the stream-K path of the bf16 GEMM, used when a product has at most
-128 tiles of 256 x 192 (half a round of the 256-workgroup grid) and the call has a
-workspace. The vocabulary-parallel logits GEMM of tp_vocab_ce_partials leaves its
-float32 output at the start of the workspace, so it can be compared with the same
-product from the tile kernel (tp_row_linear against E_i^T): every k-range must be
-summed exactly once whatever the split, and repeated calls are bit-identical
-although a split tile is finished by whichever contributing workgroup arrives last."""
+"""GPU checks of the stream-K path of the bf16 GEMM, used when the tiles of a product
+(256 x 192) do not fill whole rounds of the 256-workgroup grid and the call has a
+workspace: the k-stages are split evenly over the workgroups, the runs write the
+float32 partials of split tiles, and a second kernel adds them in run order. The
+vocabulary-parallel logits GEMM of tp_vocab_ce_partials leaves its float32 output at
+the start of the workspace, so it can be compared with the same product from the
+tile kernel (tp_row_linear against E_i^T): every k-range must be summed exactly once
+whatever the split, and repeated calls are bit-identical."""
 import pytest
 import torch
 
@@ -28,8 +29,10 @@ def _logits_streamk(H, E, lo, hi):
 
 
 # (M, h, V): 2 tiles split 16 ways; 64 tiles split 4 ways; 2 tiles split 128 ways
-# (contributors on two XCDs); and 120 tiles, each split over two or three runs.
-@pytest.mark.parametrize("M,h,V", [(300, 512, 136), (2048, 2048, 1536), (64, 12288, 384), (1920, 4096, 2880)])
+# (runs on two XCDs); 120 tiles over two or three runs each; and 264 tiles (the GPT-3
+# cross-entropy shape's count: one round and 8 more), most split over two runs.
+@pytest.mark.parametrize("M,h,V", [(300, 512, 136), (2048, 2048, 1536), (64, 12288, 384), (1920, 4096, 2880),
+                                   (2048, 1024, 6288)])
 def test_streamk_matches_tile_kernel(M, h, V):
     note(f"stream-K logits M={M} h={h} V={V}")
     g = torch.Generator(device=DEV)
