@@ -30,8 +30,8 @@
 // last k-stage into the next tile's first, so the DMA of the next tile overlaps
 // the current tile's epilogue instead of waiting for a new workgroup's launch.
 // Workgroups are dispatched round-robin over the 8 XCDs; XCD x owns a contiguous
-// range of tiles, which its 32 workgroups take round-robin (shared operand
-// panels stay in that XCD's L2).
+// range of tiles (in the grouped order of tile_rc), which its 32 workgroups take
+// round-robin, so the operand panels they share stay in that XCD's L2.
 #include "common.hpp"
 #include "gemm_bf16.hpp"
 
@@ -159,6 +159,18 @@ __device__ __forceinline__ bf16x8 frag(const uint16_t* stage, int rb, int kk, in
   }
 }
 
+// Tile t, in the order the workgroups walk them, -> tile row m and column n:
+// groups of 4 tile-rows (all rows when their count is not a multiple of 4),
+// column-major inside a group. The 32 tiles an XCD has in flight then form a
+// 4 x 8 block, which fetches 4 A-panels of 256 rows and 8 B-panels of 192
+// columns: 9% fewer bytes than the 8 x 4 block of plain column-major order.
+__device__ __forceinline__ void tile_rc(int t, int tiles_m, int tiles_n, int& m, int& n) {
+  const int gm = (tiles_m & 3) == 0 ? 4 : tiles_m;
+  const int gs = gm * tiles_n, g = t / gs, l = t - g * gs;
+  m = g * gm + l % gm;
+  n = l / gm;
+}
+
 // ---------------------------------------------------------------- epilogue
 // 32x32 accumulator layout: lane l, register e holds row 8*(e/4) + 4*(l/32) + e%4
 // and column l%32 of the MFMA tile. `row0` already includes 4*(l/32), `col`
@@ -259,8 +271,16 @@ void gemm_bf16_kernel(GemmArgs g) {
   const int tbase = T >> 3, trem = T & 7;
   const int r0 = xcd * tbase + (xcd < trem ? xcd : trem), rn = tbase + (xcd < trem ? 1 : 0);
   const int ntl = jw < rn ? (rn - jw + per - 1) / per : 0;
-  auto tile_m0 = [&](int i) { return ((r0 + jw + i * per) % tiles_m) * BM; };
-  auto tile_n0 = [&](int i) { return ((r0 + jw + i * per) / tiles_m) * BN; };
+  auto tile_m0 = [&](int i) {
+    int m, n;
+    tile_rc(r0 + jw + i * per, tiles_m, tiles_n, m, n);
+    return m * BM;
+  };
+  auto tile_n0 = [&](int i) {
+    int m, n;
+    tile_rc(r0 + jw + i * per, tiles_m, tiles_n, m, n);
+    return n * BN;
+  };
 
   // Buffer resources cover each operand exactly; the host checks sizes < 2 GiB.
   const int64_t a_elems = A_K ? (int64_t)g.M * g.lda : (int64_t)g.K * g.lda;
@@ -403,8 +423,16 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   const int per = (U + G - 1) / G;
   const int g0 = min(U, v * per), g1 = min(U, g0 + per);
   const int total = g1 - g0;
-  auto tile_m0 = [&](int t) { return (t % tiles_m) * BM; };
-  auto tile_n0 = [&](int t) { return (t / tiles_m) * BN; };
+  auto tile_m0 = [&](int t) {
+    int m, n;
+    tile_rc(t, tiles_m, tiles_n, m, n);
+    return m * BM;
+  };
+  auto tile_n0 = [&](int t) {
+    int m, n;
+    tile_rc(t, tiles_m, tiles_n, m, n);
+    return n * BN;
+  };
   // first tile of run u (its slot 0 holds the partial of that tile)
   auto first_tile = [&](int u) { return u * per / nk; };
 
@@ -563,7 +591,9 @@ __global__ __launch_bounds__(64 * NCW) void gemm_bf16_sk_fixup_kernel(GemmArgs g
           for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = u == vf ? x[r] : acc[i][j][4 * q + r] + x[r];
         }
   }
-  const int m0 = (ti % tiles_m) * BM, n0 = (ti / tiles_m) * BN;
+  int tm, tn;
+  tile_rc(ti, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
   const int am = wm * WTM, bn = wn * WTN;
   const int fk = lane >> 5, fr = lane & 31;
 #pragma unroll
