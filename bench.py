@@ -69,7 +69,7 @@ def cpu_baseline(min_seconds: float = 10.0, max_passes: int = 12):
     from oracle.bf16 import bf16_bits_to_f64
     from workloads import CONFIGS, mlp_inputs
 
-    c = CONFIGS[3]
+    c = CONFIGS["gpt3_mlp_rank_shard"]
     Ms = c["b"] * c["s"]
     inp = mlp_inputs(Ms, c["h"], c["f"], 1, "bf16", c["seed"], c["sigma_x"], c["sigma_w"], c["sigma_dz"],
                      full=False)
@@ -308,7 +308,7 @@ def next_rows(tp, torch, dev, randn, reps=5):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build runs the rank shard on a single MI355X "
+        print("bench.py measures one GPU only: the library runs one rank's shard on a single MI355X "
               "(no collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 

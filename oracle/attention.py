@@ -7,7 +7,7 @@ produces a partial of the layer output that the all-reduce adds
 [Megatron-LM：张量并行与大规模训练, §2.2 Self-Attention 的张量并行; m.youleyou.com/
 wenzhang/3143730, 三、Self-Attention层 §3.1].
 
-Readings where the pages are silent or garbled (listed in the design doc):
+Readings where the pages are silent or garbled:
   * per head: softmax(Q K^T / sqrt(d)) V with d_k = d_v = d = h / heads
     (the single-head formula itself is missing from the extract);
   * causal: key u is visible to query t iff u <= t (diagonal included);

@@ -12,7 +12,7 @@ Backward follows the conjugate operators of the same page's ä¸€ã€åˆ‡åˆ†æƒé‡ Â
 rank forms its own weight gradients and its input-gradient partial dX_i, and f's
 backward adds the dX_i over ranks.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent:
   * GeLU is the exact erf form x*Phi(x) (not the tanh approximation);
   * no bias, LayerNorm, residual or dropout inside the block;
   * "matched" mode rounds to bfloat16 exactly where the GPU stores bf16:

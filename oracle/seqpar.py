@@ -15,7 +15,7 @@ followed by an all-gather, each moving the same volume]:
     O_i  = reduce_scatter(Z_0 .. Z_{N-1})_i = sum_j Z_j[rows of i]
     R'_i = R_i + Dropout(O_i)
 
-Readings (listed in DESIGN.md):
+Readings:
   * LayerNorm is the standard one (not written out on the pages): per row, mean
     and biased variance over h, (x - mean) / sqrt(var + eps) * gamma + beta, with
     eps = 1e-5 and float32 gamma, beta [h];

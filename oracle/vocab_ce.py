@@ -12,7 +12,7 @@ e / sum(e) into that row's cross-entropy; the rows' losses are added into a
 scalar, and a last all-reduce adds the ranks' scalars
 [same page, 五、Cross-Entropy层].
 
-Readings (listed in DESIGN.md):
+Readings:
   * e is exp(logit) itself, as the page states it: no row maximum is subtracted
     (float32 logits above about 88 would overflow; the workloads stay far below);
   * a row's loss is -log(e_t / sum(e)) = log(sum(e)) - logit_t for its target t;

@@ -65,12 +65,12 @@ def test_attn_fwd_ragged(b, s, h, Hl, d):
     assert_bf16_close(f64_host(qkv[:, 2 * w:]), r["V"], "V")
 
 
-def test_config4_full_size_sampled_rows():
-    c = CONFIGS[4]
+def test_gpt3_attn_shard_full_size_sampled_rows():
+    c = CONFIGS["gpt3_attn_rank_shard"]
     b, s, h, d = c["b"], c["s"], c["h"], c["d_head"]
     Hl = c["n_heads"] // c["N"]
     ai = attn_inputs(b, s, h, Hl, d, c["seed"], c["sigma_x"], c["sigma_w"])
-    note("attn_fwd config 4 full size")
+    note("attn_fwd GPT-3 shard full size")
     out = torch.empty(b * s, h, dtype=torch.float32, device=DEV)
     ws = torch.empty(tp.attn_fwd_workspace(b, s, Hl, d), dtype=torch.uint8, device=DEV)
     tp.attn_fwd(*(bf16_dev(ai[k]) for k in ("X", "Wqkv", "Wo")), out, ws, b, s, Hl, d, True)

@@ -116,7 +116,7 @@ def test_shard_backward(b, s, h, Hl, d):
 def test_full_size_gpt3_shard_backward():
     """GPT-3 shard: 12 local heads of 128, s = 2048, h = 12288; every output
     against the full float64 oracle."""
-    c = CONFIGS[4]
+    c = CONFIGS["gpt3_attn_rank_shard"]
     b, s, h, d = c["b"], c["s"], c["h"], c["d_head"]
     Hl = c["n_heads"] // c["N"]
     ai = attn_inputs(b, s, h, Hl, d, c["seed"], c["sigma_x"], c["sigma_w"])

@@ -45,10 +45,10 @@ def test_shard_sum_in_place():
     np.testing.assert_array_equal(dev[0].cpu().numpy(), oracle.shard_sum_f32_ordered(parts))
 
 
-def test_shard_sum_config3_full_size():
-    c = CONFIGS[3]
+def test_shard_sum_gpt3_full_size():
+    c = CONFIGS["gpt3_mlp_rank_shard"]
     numel = c["b"] * c["s"] * c["h"]
-    note(f"shard_sum config 3: 8 x {numel} fp32")
+    note(f"shard_sum GPT-3 shard: 8 x {numel} fp32")
     parts = shard_sum_inputs(c["n_partials"], numel, 2003, c["sigma_p"])
     out = torch.empty(numel, dtype=torch.float32, device=DEV)
     tp.shard_sum([f32_dev(p) for p in parts], out)
@@ -90,11 +90,11 @@ def test_gather_out_of_range_and_ragged():
     tp.vocab_embed(torch.empty(0, dtype=torch.int32, device=DEV), bf16_dev(E[lo:hi]), lo, hi, empty)
 
 
-def test_config5_full_size_all_shards():
-    c = CONFIGS[5]
+def test_vocab_embed_full_size_all_shards():
+    c = CONFIGS["vocab_parallel_embed"]
     v, h, N = c["v"], c["h"], c["N"]
     n = c["b"] * c["s"]
-    note("vocab gather config 5: generating table")
+    note("vocab gather full size: generating table")
     ei = embed_inputs(v, h, n, c["seed"], c["sigma_w"])
     E, ids = ei["E"], ei["ids"]
     assert not np.any(E == 0x8000), "table holds -0.0"
@@ -104,7 +104,7 @@ def test_config5_full_size_all_shards():
     per = v // N
     for i in range(N):
         lo, hi = i * per, (i + 1) * per
-        note(f"vocab gather config 5 shard {i}")
+        note(f"vocab gather full size shard {i}")
         out = torch.empty(n, h, dtype=torch.bfloat16, device=DEV)
         tp.vocab_embed(idt, Edev[lo:hi], lo, hi, out)
         want = bf16_dev(oracle.vocab_embed_shard(ids, E[lo:hi], lo, hi))
@@ -112,7 +112,7 @@ def test_config5_full_size_all_shards():
         assert torch.equal(out.view(torch.int16), want.view(torch.int16)), f"shard {i}"
         outs.append(out)
     tot = torch.empty_like(outs[0])
-    note("vocab gather config 5: shard-sum of 8 shards")
+    note("vocab gather full size: shard-sum of 8 shards")
     tp.shard_sum(outs, tot)
     torch.cuda.synchronize()
     assert torch.equal(tot.view(torch.int16), bf16_dev(E[ids]).view(torch.int16))

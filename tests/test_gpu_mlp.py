@@ -30,11 +30,11 @@ def _run_bwd(X, A, B, U, Y, dZ, M, h, f):
     return dX, dA, dB, ws
 
 
-def test_config1_fp32_two_shards():
-    c = CONFIGS[1]
+def test_tiny_mlp_fp32_two_shards():
+    c = CONFIGS["tiny_mlp_fp32"]
     M = c["b"] * c["s"]
     inp = mlp_inputs(M, c["h"], c["f_full"], c["N"], "f32", c["seed"], c["sigma_x"], c["sigma_w"], None)
-    note("config 1 fp32 mlp_fwd, 2 shards")
+    note("tiny fp32 mlp_fwd, 2 shards")
     X = f32_dev(inp["X"])
     Zs = []
     for i, (A_i, B_i) in enumerate(inp["shards"]):
@@ -92,8 +92,8 @@ def _bf16_mlp_case(M, h, f_full, N, seed, sigma_w, check_unsharded=True):
         assert_bf16_close(f64_host(out), oracle.mlp_fwd_full(Xo, Ao, Bo, matched=True), "sum of Z_i vs unsharded")
 
 
-def test_config2_bf16_fwd_bwd_two_shards():
-    c = CONFIGS[2]
+def test_small_mlp_bf16_fwd_bwd_two_shards():
+    c = CONFIGS["small_mlp_bf16"]
     _bf16_mlp_case(c["b"] * c["s"], c["h"], c["f_full"], c["N"], c["seed"], c["sigma_w"])
 
 
@@ -131,7 +131,7 @@ def test_column_linear_without_activation():
     assert_bf16_close(f64_host(Y), ref, "X W")
 
 
-class TestConfig3FullSize:
+class TestGpt3MlpShardFullSize:
     """GPT-3-shaped rank shard (M=2048, h=12288, f=6144) in the launch
     configuration the benchmark times; sampled outputs from the oracle."""
 
@@ -140,11 +140,11 @@ class TestConfig3FullSize:
 
     @pytest.fixture(scope="class")
     def case(self):
-        c = CONFIGS[3]
+        c = CONFIGS["gpt3_mlp_rank_shard"]
         M, h, f = c["b"] * c["s"], c["h"], c["f"]
         inp = mlp_inputs(M, h, f, 1, "bf16", c["seed"], c["sigma_x"], c["sigma_w"], c["sigma_dz"], full=False)
         A_i, B_i = inp["shards"][0]
-        note("config 3 full-size mlp_fwd + mlp_bwd")
+        note("GPT-3 shard full-size mlp_fwd + mlp_bwd")
         X, A, B, dZ = bf16_dev(inp["X"]), bf16_dev(A_i), bf16_dev(B_i), bf16_dev(inp["dZ"])
         U, Y, Z = _alloc(M, h, f, torch.bfloat16)
         tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
@@ -215,7 +215,7 @@ class TestPalmShape:
 
     @pytest.fixture(scope="class")
     def case(self):
-        c = CONFIGS[6]
+        c = CONFIGS["palm_mlp_rank_shard"]
         M, h, f = c["b"] * c["s"], c["h"], c["f"]
         inp = mlp_inputs(M, h, f, 1, "bf16", c["seed"], c["sigma_x"], c["sigma_w"], c["sigma_dz"], full=False)
         A_i, B_i = inp["shards"][0]

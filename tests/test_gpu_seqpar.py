@@ -153,7 +153,7 @@ def test_sp_mlp_block(N):
 def test_full_size_layernorm_gather_reduce_scatter():
     """GPT-3 shard: 8 ranks of 256 rows x 12288; the reduce-scatter of 8 fp32
     partials [2048, 12288] with dropout 0.9 and the residual, for every rank."""
-    c = CONFIGS[8]
+    c = CONFIGS["gpt3_sp_mlp_block"]
     s, h, N = c["s"], c["h"], c["N"]
     rows = s // N
     sp = sp_inputs(s, h, c["seed"], c["sigma_r"], c["sigma_g"], c["sigma_b"], c["keep_prob"])

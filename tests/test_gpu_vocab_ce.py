@@ -122,7 +122,7 @@ def test_full_size_sampled_rows():
     """GPT-3 vocabulary (50304 = 8 x 6288), h = 12288, 2048 rows, all eight
     slices run on the GPU; the oracle recomputes sampled rows' logits, then
     every row's partial sums and loss over the whole vocabulary."""
-    c = CONFIGS[7]
+    c = CONFIGS["vocab_parallel_ce"]
     M, h, v, N = c["b"] * c["s"], c["h"], c["v"], c["N"]
     inp = ce_inputs(M, h, v, c["seed"], c["sigma_h"], c["sigma_w"])
     t = inp["targets"]

@@ -99,8 +99,8 @@ def _f64(a, dtype):
 
 
 class TestMlpForward:
-    def test_config1_brute_force(self):
-        c = CONFIGS[1]
+    def test_tiny_mlp_brute_force(self):
+        c = CONFIGS["tiny_mlp_fp32"]
         inp = mlp_inputs(c["b"] * c["s"], c["h"], c["f_full"], c["N"], c["dtype"], c["seed"],
                          c["sigma_x"], c["sigma_w"], sigma_dz=None)
         X = _f64(inp["X"], "f32")

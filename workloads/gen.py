@@ -21,26 +21,26 @@ import torch
 
 # name -> shapes and distributions of each workload. "seed" is the generator seed.
 CONFIGS = {
-    1: dict(name="tiny_mlp_fp32", b=1, s=8, h=64, f_full=256, N=2, dtype="f32",
+    "tiny_mlp_fp32": dict(name="tiny_mlp_fp32", b=1, s=8, h=64, f_full=256, N=2, dtype="f32",
             sigma_x=1.0, sigma_w=0.02, seed=1001),
-    2: dict(name="small_mlp_bf16", b=1, s=32, h=1024, f_full=4096, N=2, dtype="bf16",
+    "small_mlp_bf16": dict(name="small_mlp_bf16", b=1, s=32, h=1024, f_full=4096, N=2, dtype="bf16",
             sigma_x=1.0, sigma_w=0.02, sigma_dz=1.0, seed=1002),
-    3: dict(name="gpt3_mlp_rank_shard", b=1, s=2048, h=12288, f=6144, N=8, dtype="bf16",
+    "gpt3_mlp_rank_shard": dict(name="gpt3_mlp_rank_shard", b=1, s=2048, h=12288, f=6144, N=8, dtype="bf16",
             sigma_x=1.0, sigma_w=0.006, sigma_dz=1.0, n_partials=8, sigma_p=1.0, seed=1003),
-    4: dict(name="gpt3_attn_rank_shard", b=1, s=2048, h=12288, n_heads=96, N=8,
+    "gpt3_attn_rank_shard": dict(name="gpt3_attn_rank_shard", b=1, s=2048, h=12288, n_heads=96, N=8,
             d_head=128, dtype="bf16", sigma_x=1.0, sigma_w=0.006, seed=1004),
-    5: dict(name="vocab_parallel_embed", v=50304, N=8, h=12288, b=8, s=2048,
+    "vocab_parallel_embed": dict(name="vocab_parallel_embed", v=50304, N=8, h=12288, b=8, s=2048,
             dtype="bf16", sigma_w=0.02, seed=1005),
     # PaLM-shaped rank shard (h = 18432, TP = 8, f = 4h/8), a second MLP shape.
-    6: dict(name="palm_mlp_rank_shard", b=1, s=2048, h=18432, f=9216, N=8, dtype="bf16",
+    "palm_mlp_rank_shard": dict(name="palm_mlp_rank_shard", b=1, s=2048, h=18432, f=9216, N=8, dtype="bf16",
             sigma_x=1.0, sigma_w=0.005, sigma_dz=1.0, seed=1006),
     # Vocabulary-parallel output layer + cross-entropy over the GPT-3 vocabulary
     # (padded to 50304 = 8 * 6288), one sequence of 2048 tokens.
-    7: dict(name="vocab_parallel_ce", v=50304, N=8, h=12288, b=1, s=2048, dtype="bf16",
+    "vocab_parallel_ce": dict(name="vocab_parallel_ce", v=50304, N=8, h=12288, b=1, s=2048, dtype="bf16",
             sigma_h=1.0, sigma_w=0.02, seed=1007),
     # Sequence-parallel MLP block at the GPT-3 shard: LayerNorm on s/N rows per rank,
     # all-gather, reduce-scatter of 8 fp32 partials fused with dropout and residual.
-    8: dict(name="gpt3_sp_mlp_block", s=2048, h=12288, f=6144, N=8, sigma_r=1.0, sigma_g=0.1,
+    "gpt3_sp_mlp_block": dict(name="gpt3_sp_mlp_block", s=2048, h=12288, f=6144, N=8, sigma_r=1.0, sigma_g=0.1,
             sigma_b=0.1, keep_prob=0.9, sigma_p=1.0, seed=1008),
 }
 
