@@ -1,0 +1,70 @@
+"""Host model of the stream-K work split of the bf16 GEMM (the same integer formulas
+the product and fixup kernels evaluate per workgroup and per tile), checked for the
+properties the kernels rely on: every (tile, k-stage) unit is covered by exactly one
+run; a run has at most two partial segments (its first and its last), so two
+workspace slots per run suffice; the slots the fixup reads for a split tile are
+distinct and are the ones its runs wrote; and the split is used only when the last
+round of tiles is at most half full."""
+import itertools
+
+import pytest
+
+GRID, BK = 256, 32
+
+
+def sk_applies(tiles, K):
+    return (K > 0 and tiles > 0 and tiles % GRID != 0 and tiles % GRID <= GRID // 2 and tiles <= 4096
+            and tiles * ((K + BK - 1) // BK) < (1 << 30))
+
+
+def runs(T, nk):
+    U = T * nk
+    per = (U + GRID - 1) // GRID
+    return U, per, [(min(U, v * per), min(U, min(U, v * per) + per)) for v in range(GRID)]
+
+
+def written_slots(T, nk):
+    """(tile, run) -> slot written by the product kernel for each split segment."""
+    U, per, rr = runs(T, nk)
+    out = {}
+    for v, (g0, g1) in enumerate(rr):
+        gs = g0
+        segs = 0
+        while gs < g1:
+            ti = gs // nk
+            kb, ke = gs - ti * nk, min(nk, g1 - ti * nk)
+            if kb != 0 or ke != nk:
+                segs += 1
+                out[(ti, v)] = 2 * v + (0 if ti == v * per // nk else 1)
+            gs = ti * nk + ke
+        assert segs <= 2
+    return out
+
+
+@pytest.mark.parametrize("T,nk", list(itertools.product([1, 2, 8, 64, 120, 264, 384, 1152, 3456], [1, 3, 16, 64, 384])))
+def test_partition(T, nk):
+    U, per, rr = runs(T, nk)
+    cover = [0] * U
+    for g0, g1 in rr:
+        assert 0 <= g0 <= g1 <= U
+        for u in range(g0, g1):
+            cover[u] += 1
+    assert all(c == 1 for c in cover)
+    w = written_slots(T, nk)
+    assert len(set(w.values())) == len(w) and all(0 <= s < 2 * GRID for s in w.values())
+    for ti in range(T):
+        ua = ti * nk
+        vf, vl = ua // per, (ua + nk - 1) // per
+        if vf == vl:
+            assert all(t != ti for (t, _) in w)  # finished by its only run, nothing written
+            continue
+        read = [2 * u + (0 if ti == u * per // nk else 1) for u in range(vf, vl + 1)]
+        assert read == [w[(ti, u)] for u in range(vf, vl + 1)]
+
+
+def test_rule():
+    assert not sk_applies(256, 12288) and not sk_applies(512, 6144)     # whole rounds
+    assert sk_applies(64, 12288) and sk_applies(264, 12288)             # last round <= half full
+    assert sk_applies(384, 12288) and sk_applies(3456, 2048)
+    assert not sk_applies(192, 12288)                                    # 3/4 full: tile kernel
+    assert not sk_applies(5000, 64) and not sk_applies(64, 0)
