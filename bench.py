@@ -12,8 +12,9 @@ synthetic input already resident in HBM:
 
 The reported value is the metric: TFLOP/s of the MLP forward + backward
 (1855.43 GFLOP per step), timed with HIP events on the launch stream over the
-timed steps. ms_per_step is the wall time of whole steps. Per-kernel times and
-roofline fractions are in "breakdown"; "roofline" is for the dominant kernel.
+timed steps. ms_per_step is the wall time of whole steps. Per-row times (mean,
+median, min and p90 over the timed steps) and roofline fractions (on the mean) are
+in "breakdown"; "roofline" is for the dominant kernel.
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -405,7 +406,10 @@ def main():
 
     breakdown = {}
     for name in ms:
-        d = {"ms": round(ms[name], 4)}
+        t = sorted(a.elapsed_time(b) for a, b in ev[name])
+        # mean (used for the rates), and the spread of the per-step HIP-event times
+        d = {"ms": round(ms[name], 4), "ms_median": round(t[len(t) // 2], 4), "ms_min": round(t[0], 4),
+             "ms_p90": round(t[min(len(t) - 1, (9 * len(t)) // 10)], 4)}
         if name in flops:
             tf = flops[name] / (ms[name] * 1e-3) / 1e12
             d.update(tflops=round(tf, 1), frac_bf16_peak=round(tf / PEAK_BF16_TFLOPS, 4))
