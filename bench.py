@@ -140,8 +140,9 @@ def next_rows(tp, torch, dev, randn, reps=5):
     (M=2048, h=18432, f=9216), forward with saved U, backward with activation
     recompute (U, Y formed again from X and A_i inside mlp_bwd); the
     vocabulary-parallel output layer + cross-entropy of one rank; the attention
-    backward (core, and the whole shard); and the sequence-parallel LayerNorm,
-    all-gather and reduce-scatter of one rank."""
+    backward (core, and the whole shard); the sequence-parallel LayerNorm,
+    all-gather and reduce-scatter of one rank; and, as context, the runtime's
+    library GEMM on the six MLP products."""
     Mp, Hp, Fp = 2048, 18432, 9216
     X = randn((Mp, Hp), 1.0, 40)
     A = randn((Hp, Fp), 0.005, 41)
@@ -302,6 +303,41 @@ def next_rows(tp, torch, dev, randn, reps=5):
         out[name] = {"ms": round(ms, 4), "bytes": nbytes, "gbs": round(gbs, 1),
                      "frac_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
     del Rr, gam, bet, Ls, Xg, parts, keep, Ro, dYs, dRs, dXs, dgs, dbs, lws, dZs
+    torch.cuda.empty_cache()
+
+    # Context, not part of the path: the runtime's library GEMM (hipBLASLt through
+    # torch.mm) on the same six MLP products of the GPT-3 shard, on this machine in this
+    # run, every operand already contiguous (transposes materialised outside the
+    # timing) and bf16 outputs without the epilogues.
+    M, H, F = 2048, 12288, 6144
+    X = randn((M, H), 1.0, 1)
+    A = randn((H, F), 0.006, 2)
+    B = randn((F, H), 0.006, 3)
+    dZ = randn((M, H), 1.0, 4)
+    Y = randn((M, F), 1.0, 5)
+    dU = randn((M, F), 1.0, 6)
+    Bt, At, Yt, Xt = B.t().contiguous(), A.t().contiguous(), Y.t().contiguous(), X.t().contiguous()
+    prods = [(X, A), (Y, B), (dZ, Bt), (Yt, dZ), (Xt, dU), (dU, At)]
+    outs = [torch.empty(a.shape[0], b.shape[1], dtype=torch.bfloat16, device=dev) for a, b in prods]
+
+    def six():
+        for (a, b), o in zip(prods, outs):
+            torch.mm(a, b, out=o)
+
+    for _ in range(2):
+        six()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        six()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    tf = 6 * gemm_flops(M, F, H) / (ms * 1e-3) / 1e12
+    out["context_library_gemm_mlp6"] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                                        "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del X, A, B, dZ, Y, dU, Bt, At, Yt, Xt, prods, outs
     torch.cuda.empty_cache()
     return out
 
