@@ -205,14 +205,15 @@ __device__ __forceinline__ float quad_x2(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, true));
 }
 
-// Epilogue of one 32x32 accumulator tile. For DGELU on a whole in-range tile, each
-// group of 4 registers (4 rows, one column per lane) is transposed across the
-// lane quad, so that lane q of a quad holds row q and the quad's 4 consecutive
-// columns: U is then read, and dU written, 8 bytes at a time instead of element
-// by element. (For the other epilogues the per-element stores measured faster.)
+// Epilogue of one 32x32 accumulator tile. For the bf16 epilogues (GeLU, bf16,
+// GeLU') on a whole in-range tile, each group of 4 registers (4 rows, one column
+// per lane) is transposed across the lane quad, so that lane q of a quad holds row
+// q and the quad's 4 consecutive columns: outputs are written (and GeLU' reads U)
+// 8 bytes at a time instead of 2. (For the float32 store the per-element stores,
+// 4 bytes each, measured faster.)
 template <int EPI>
 __device__ __forceinline__ void store_tile(const f32x16 a, const GemmArgs& g, int row0, int col, bool full) {
-  if constexpr (EPI == EPI_DGELU) {
+  if constexpr (EPI == EPI_DGELU || EPI == EPI_GELU || EPI == EPI_BF16) {
     if (full) {
       const int q = col & 3, c4 = col - q;
 #pragma unroll
@@ -231,12 +232,21 @@ __device__ __forceinline__ void store_tile(const f32x16 a, const GemmArgs& g, in
           w[j] = (((q >> 1) & 1) == ((j >> 1) & 1)) ? t[j] : p;
         }
         const int row = row0 + 8 * gr + q;
-        const uint2 uu = *reinterpret_cast<const uint2*>(g.Uin + (int64_t)row * g.ldu + c4);
-        const float u0 = bf16_bits_to_f32(uu.x & 0xffffu), u1 = bf16_bits_to_f32(uu.x >> 16);
-        const float u2 = bf16_bits_to_f32(uu.y & 0xffffu), u3 = bf16_bits_to_f32(uu.y >> 16);
-        *reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + (int64_t)row * g.ldc + c4) =
-            uint2{pack_bf16x2(w[0] * gelu_erf_prime(u0), w[1] * gelu_erf_prime(u1)),
-                  pack_bf16x2(w[2] * gelu_erf_prime(u2), w[3] * gelu_erf_prime(u3))};
+        uint2* dst = reinterpret_cast<uint2*>(static_cast<uint16_t*>(g.C) + (int64_t)row * g.ldc + c4);
+        if constexpr (EPI == EPI_DGELU) {
+          const uint2 uu = *reinterpret_cast<const uint2*>(g.Uin + (int64_t)row * g.ldu + c4);
+          const float u0 = bf16_bits_to_f32(uu.x & 0xffffu), u1 = bf16_bits_to_f32(uu.x >> 16);
+          const float u2 = bf16_bits_to_f32(uu.y & 0xffffu), u3 = bf16_bits_to_f32(uu.y >> 16);
+          *dst = uint2{pack_bf16x2(w[0] * gelu_erf_prime(u0), w[1] * gelu_erf_prime(u1)),
+                       pack_bf16x2(w[2] * gelu_erf_prime(u2), w[3] * gelu_erf_prime(u3))};
+        } else if constexpr (EPI == EPI_GELU) {
+          *dst = uint2{pack_bf16x2(gelu_erf(w[0]), gelu_erf(w[1])), pack_bf16x2(gelu_erf(w[2]), gelu_erf(w[3]))};
+          if (g.U)
+            *reinterpret_cast<uint2*>(g.U + (int64_t)row * g.ldu + c4) =
+                uint2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
+        } else {
+          *dst = uint2{pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3])};
+        }
       }
       return;
     }
