@@ -306,16 +306,20 @@ void gemm_bf16_kernel(GemmArgs g) {
     const int pw = wave - NCW;
     Dma<BM, A_K> da;
     Dma<BN, B_K> db;
-    int itile = -1;
+    // stages are issued in order: the next one's tile and k-stage are kept as counters
+    int nti = 0, nkt = 0;
     auto issue_stage = [&](int gs, int sl) __attribute__((always_inline)) {
-      const int ti = gs / nk, kt = gs - ti * nk;
-      if (ti != itile) {
-        da.init(tile_m0(ti), g.M, g.lda, pw, lane);
-        db.init(tile_n0(ti), g.N, g.ldb, pw, lane);
-        itile = ti;
+      (void)gs;
+      if (nkt == 0) {
+        da.init(tile_m0(nti), g.M, g.lda, pw, lane);
+        db.init(tile_n0(nti), g.N, g.ldb, pw, lane);
       }
-      da.issue(ra, a_lds + sl * SA * 2, g.lda, kt * BK, g.K, pw);
-      db.issue(rb, b_lds + sl * SB * 2, g.ldb, kt * BK, g.K, pw);
+      da.issue(ra, a_lds + sl * SA * 2, g.lda, nkt * BK, g.K, pw);
+      db.issue(rb, b_lds + sl * SB * 2, g.ldb, nkt * BK, g.K, pw);
+      if (++nkt == nk) {
+        nkt = 0;
+        ++nti;
+      }
     };
 #pragma unroll
     for (int st = 0; st < NS - 1; ++st)
