@@ -6,14 +6,15 @@
 namespace tps {
 
 constexpr int kSpMaxParts = 16;
-constexpr int64_t kLnMaxH = 32768;  // 32 float4 per thread of a 256-thread row
+constexpr int kLnThreads = 1024;    // threads of a LayerNorm row workgroup
+constexpr int64_t kLnMaxH = 32768;  // 8 float4 per thread of a row
 
 // Y[r] = bf16((X[r] - mean) / sqrt(var + eps) * gamma + beta), one row per workgroup.
 // X float32 [rows, h], gamma/beta float32 [h], h % 4 == 0, h <= kLnMaxH.
 hipError_t layernorm_rows(const float* X, int64_t rows, int64_t h, const float* gamma, const float* beta, float eps,
                           uint16_t* Y, hipStream_t st);
 
-constexpr int64_t kLnBwdMaxH = 24576;  // 24 float4 per thread for each of X and dY
+constexpr int64_t kLnBwdMaxH = 24576;  // 6 float4 per thread for each of X and dY
 constexpr int kLnBwdRowBlocks = 64;    // row blocks of the gamma/beta column sums
 
 // Backward of layernorm_rows over rows x h (float32 X, dY): dX (+ dRes if not null),
