@@ -4,20 +4,24 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  D = rowsum(dO * O),
 //   dQ = dS K / sqrt(d),  dK = dS^T Q / sqrt(d).
 // Three launches:
-//   * attn_bwd_rowdot — D per (query, head), 16 lanes per row of 128;
-//   * attn_bwd_dkdv   — one workgroup per (sequence, head, block of 32*NW keys),
-//     wave w owning 32 keys (their K and V fragments, dK and dV in registers);
-//     it walks the query blocks of 32 that can see its keys, with each block's Q
-//     and dO staged in LDS (double-buffered) and shared by the waves;
-//   * attn_bwd_dq     — one workgroup per (sequence, head, block of 32*NW
-//     queries), wave w owning 32 queries whose Q and dO fragments sit in
-//     registers; it walks the key blocks of 32 up to the diagonal, K and V
-//     staged in LDS.
+//   * rowdot — D per (query, head), 16 lanes per row of 128;
+//   * dkdv_dq — one grid holding the two independent walks, dK/dV items first,
+//     so that dQ items start on the CUs the dK/dV tail leaves free:
+//     - a dK/dV item is one workgroup per (sequence, head, block of 32*NW keys),
+//       wave w owning 32 keys (their K and V fragments, dK and dV in
+//       registers); it walks the query blocks of 32 that can see its keys, with
+//       each block's Q and dO staged in LDS (double-buffered) and shared by the
+//       waves;
+//     - a dQ item is one workgroup per (sequence, head, block of 32*NW
+//       queries), wave w owning 32 queries whose Q and dO fragments sit in
+//       registers; it walks the key blocks of 32 up to the diagonal, K and V
+//       staged in LDS;
+//   * combine — the walks are cut into chunks for causal balance, and this
+//     launch adds the chunks' partials of dQ, dK and dV in chunk order.
 // The staged tiles are loaded into registers two steps ahead of their use (two
 // register sets, the loop unrolled by two), so a step's compute covers the
 // global-load latency of the tile after next.
-// The two walks are cut into chunks for causal balance (see combine_kernel).
-// Both big kernels run their products on v_mfma_f32_32x32x16_bf16. The score
+// Both walks run their products on v_mfma_f32_32x32x16_bf16. The score
 // tile comes out of the MFMA with a lane owning one column and 16 rows
 // {8(e/4) + 4(l/32) + e%4}; those 16 values (8 per 16-row k-slice, packed to
 // bf16) are used directly as the k-operand of the next product, taking the
@@ -174,9 +178,8 @@ __device__ __forceinline__ void chunk_of(int r, int nblk, int R, int s, int C, i
 // out[row, col0 + d] = bf16(scale * sum_c part[c][row][d]) for every block with
 // more than one chunk. part slots: [bh][blk][kMaxChunks][R][D] float32.
 template <int D, bool CAUSAL, bool QSIDE>
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ part, uint16_t* __restrict__ out,
-                                                      int s, int Hl, int nblk, int R, int C, int col_block,
-                                                      float scale) {
+__device__ __forceinline__ void combine_part(const float* __restrict__ part, uint16_t* __restrict__ out, int s,
+                                             int Hl, int nblk, int R, int C, int col_block, float scale) {
   const int bh = blockIdx.x / nblk, blk = blockIdx.x % nblk;
   const int n = QSIDE ? q_steps<CAUSAL>(blk, R, s) : kv_steps<CAUSAL>(blk, R, s);
   const int nc = (n + C - 1) / C;
@@ -196,9 +199,22 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   }
 }
 
+// blockIdx.z: 0 = dQ (scaled), 1 = dK (scaled), 2 = dV; one launch for the three.
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partQ,
+                                                      const float* __restrict__ partK,
+                                                      const float* __restrict__ partV, uint16_t* __restrict__ out,
+                                                      int s, int Hl, int nblk, int R, int C, float scale) {
+  if (blockIdx.z == 0)
+    combine_part<D, CAUSAL, true>(partQ, out, s, Hl, nblk, R, C, 0, scale);
+  else
+    combine_part<D, CAUSAL, false>(blockIdx.z == 1 ? partK : partV, out, s, Hl, nblk, R, C, (int)blockIdx.z,
+                                   blockIdx.z == 1 ? scale : 1.f);
+}
+
 // ------------------------------------------------------------------ dK, dV
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restrict__ qkv,
+__device__ __forceinline__ void dkdv_item(int item, const uint16_t* __restrict__ qkv,
                                                        const uint16_t* __restrict__ dO,
                                                        const float* __restrict__ lse,
                                                        const float* __restrict__ Dv, uint16_t* __restrict__ dqkv,
@@ -215,9 +231,9 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
   __shared__ __attribute__((aligned(16))) float sDv[2][32];
 
   // Chunks of every head, heaviest first: rank r of all heads before rank r + 1.
-  const int bh = blockIdx.x % BH;
+  const int bh = item % BH;
   int kb, chunk;
-  chunk_of<CAUSAL, false>(blockIdx.x / BH, nkb, KB, s, C, kb, chunk);
+  chunk_of<CAUSAL, false>(item / BH, nkb, KB, s, C, kb, chunk);
   if (kb < 0) return;
   const int bi = bh / Hl, head = bh % Hl;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
@@ -360,7 +376,7 @@ __global__ __launch_bounds__(NW * 64) void dkdv_kernel(const uint16_t* __restric
 
 // ------------------------------------------------------------------ dQ
 template <int D, bool CAUSAL, int NW>
-__global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
+__device__ __forceinline__ void dq_item(int item, const uint16_t* __restrict__ qkv, const uint16_t* __restrict__ dO,
                                                      const float* __restrict__ lse, const float* __restrict__ Dv,
                                                      uint16_t* __restrict__ dqkv, float* __restrict__ partQ, int s,
                                                      int Hl, int BH, int nqb, int C, float scale_log2, float scale) {
@@ -369,9 +385,9 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
   __shared__ __attribute__((aligned(16))) uint16_t sK[2][32 * D];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2][32 * D];
 
-  const int bh = blockIdx.x % BH;
+  const int bh = item % BH;
   int qb, chunk;
-  chunk_of<CAUSAL, true>(blockIdx.x / BH, nqb, QB, s, C, qb, chunk);
+  chunk_of<CAUSAL, true>(item / BH, nqb, QB, s, C, qb, chunk);
   if (qb < 0) return;
   const int bi = bh / Hl, head = bh % Hl;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
@@ -491,6 +507,24 @@ __global__ __launch_bounds__(NW * 64) void dq_kernel(const uint16_t* __restrict_
   }
 }
 
+// The dK/dV walks (items 0 .. nk_items - 1) and the dQ walks (the rest) in one
+// grid: the two are independent, so the dQ items start on the CUs that the dK/dV
+// items' tail leaves free instead of after the whole first grid has drained.
+template <int D, bool CAUSAL, int NW>
+__global__ __launch_bounds__(NW * 64) void dkdv_dq_kernel(const uint16_t* __restrict__ qkv,
+                                                          const uint16_t* __restrict__ dO,
+                                                          const float* __restrict__ lse,
+                                                          const float* __restrict__ Dv, uint16_t* __restrict__ dqkv,
+                                                          float* __restrict__ partQ, float* __restrict__ partK,
+                                                          float* __restrict__ partV, int s, int Hl, int BH, int nblk,
+                                                          int C, int nk_items, float scale_log2, float scale) {
+  const int item = (int)blockIdx.x;
+  if (item < nk_items)
+    dkdv_item<D, CAUSAL, NW>(item, qkv, dO, lse, Dv, dqkv, partK, partV, s, Hl, BH, nblk, C, scale_log2, scale);
+  else
+    dq_item<D, CAUSAL, NW>(item - nk_items, qkv, dO, lse, Dv, dqkv, partQ, s, Hl, BH, nblk, C, scale_log2, scale);
+}
+
 // Workspace: D = rowsum(dO * O) [b*Hl*s], then the partial slots of dQ, dK, dV.
 struct BwdLayout {
   int64_t d_bytes, q_bytes, kv_bytes;
@@ -534,21 +568,16 @@ hipError_t launch_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO
     max_nc = max(max_nc, max(nq, nk));
   }
   if (max_nc > 1 && L.q_bytes == 0) return hipErrorInvalidValue;
-  if ((int64_t)BH * max(items_q, items_k) > 0x7fffffffLL) return hipErrorInvalidValue;  // grid.x range
+  if ((int64_t)BH * (items_q + items_k) > 0x7fffffffLL) return hipErrorInvalidValue;  // grid.x range
   const float scale = 1.f / sqrtf((float)D), scale_log2 = kLog2e * scale;
   hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, dO, O, Dws, s, Hl, D, rows);
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, kNW>), dim3((unsigned)((int64_t)BH * items_k)), dim3(kNW * 64), 0, st,
-                     qkv, dO, lse, Dws, dqkv, partK, partV, s, Hl, BH, L.nkb, L.C, scale_log2, scale);
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, kNW>), dim3((unsigned)((int64_t)BH * items_q)), dim3(kNW * 64), 0, st, qkv,
-                     dO, lse, Dws, dqkv, partQ, s, Hl, BH, L.nqb, L.C, scale_log2, scale);
+  hipLaunchKernelGGL((dkdv_dq_kernel<D, CAUSAL, kNW>), dim3((unsigned)((int64_t)BH * (items_k + items_q))),
+                     dim3(kNW * 64), 0, st, qkv, dO, lse, Dws, dqkv, partQ, partK, partV, s, Hl, BH, L.nqb, L.C,
+                     BH * items_k, scale_log2, scale);
   if (max_nc > 1) {
-    const dim3 grid((unsigned)((int64_t)BH * L.nqb), (unsigned)((R * D / 4 + 255) / 256));
-    hipLaunchKernelGGL((combine_kernel<D, CAUSAL, true>), grid, dim3(256), 0, st, partQ, dqkv, s, Hl, L.nqb, R, L.C, 0,
-                       scale);
-    hipLaunchKernelGGL((combine_kernel<D, CAUSAL, false>), grid, dim3(256), 0, st, partK, dqkv, s, Hl, L.nkb, R, L.C,
-                       1, scale);
-    hipLaunchKernelGGL((combine_kernel<D, CAUSAL, false>), grid, dim3(256), 0, st, partV, dqkv, s, Hl, L.nkb, R, L.C,
-                       2, 1.f);
+    const dim3 grid((unsigned)((int64_t)BH * L.nqb), (unsigned)((R * D / 4 + 255) / 256), 3);
+    hipLaunchKernelGGL((combine_kernel<D, CAUSAL>), grid, dim3(256), 0, st, partQ, partK, partV, dqkv, s, Hl, L.nqb,
+                       R, L.C, scale);
   }
   return hipGetLastError();
 }
