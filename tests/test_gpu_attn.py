@@ -49,7 +49,9 @@ def test_attn_core_stage_counts(s, d, causal):
     assert_bf16_close(f64_host(O), ref, "O")
 
 
-@pytest.mark.parametrize("b,s,h,Hl,d", [(2, 300, 512, 2, 128), (1, 150, 256, 4, 64)])
+# Ragged lengths of one to sixteen 64-key stages per query block, d = 64 and 128.
+@pytest.mark.parametrize("b,s,h,Hl,d", [(2, 300, 512, 2, 128), (1, 150, 256, 4, 64), (1, 1000, 256, 2, 128),
+                                        (2, 700, 256, 2, 64)])
 def test_attn_fwd_ragged(b, s, h, Hl, d):
     note(f"attn_fwd b={b} s={s} h={h} Hl={Hl} d={d}")
     ai = attn_inputs(b, s, h, Hl, d, 80 + s, 1.0, 0.05)
@@ -63,6 +65,9 @@ def test_attn_fwd_ragged(b, s, h, Hl, d):
     w = Hl * d
     assert_bf16_close(f64_host(qkv[:, :w]), r["Q"], "Q")
     assert_bf16_close(f64_host(qkv[:, 2 * w:]), r["V"], "V")
+    o_off = (b * s * 3 * w * 2 + 255) // 256 * 256
+    O = ws[o_off: o_off + b * s * w * 2].view(torch.bfloat16).view(b * s, w)
+    assert_bf16_close(f64_host(O), r["O"], "O")
 
 
 def test_gpt3_attn_shard_full_size_sampled_rows():
@@ -76,6 +81,10 @@ def test_gpt3_attn_shard_full_size_sampled_rows():
     tp.attn_fwd(*(bf16_dev(ai[k]) for k in ("X", "Wqkv", "Wo")), out, ws, b, s, Hl, d, True)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
-    rows = np.array([0, 1, 63, 64, 127, 128, 1000, 2047])
+    rows = np.array([0, 1, 63, 64, 127, 128, 1000, 1024, 1500, 2047])
     r = oracle.attn_shard_rows(*(bf16_bits_to_f64(ai[k]) for k in ("X", "Wqkv", "Wo")), b, s, Hl, d, rows)
     assert_bf16_close(f64_host(out[torch.from_numpy(rows).to(DEV)]), r["out"], "out rows")
+    w = Hl * d
+    o_off = (b * s * 3 * w * 2 + 255) // 256 * 256
+    O = ws[o_off: o_off + b * s * w * 2].view(torch.bfloat16).view(b * s, w)
+    assert_bf16_close(f64_host(O[torch.from_numpy(rows).to(DEV)]), r["O"], "O rows")
