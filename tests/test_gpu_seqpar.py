@@ -236,6 +236,29 @@ def test_layernorm_bwd(rows, h, res):
     _close_f32(f64_host(db), r["dbeta"], "dbeta")
 
 
+@pytest.mark.parametrize("rows,h", [(256, 12288), (100, 1032), (5, 8)])
+def test_layernorm_bwd_is_deterministic(rows, h):
+    """dgamma and dbeta are sums over the rows in a fixed order: two calls give the
+    same bits, whatever the workspace held before."""
+    note(f"layernorm_bwd determinism rows={rows} h={h}")
+    inp = sp_inputs(rows, h, seed=950 + rows, sigma_r=2.0)
+    rng = np.random.default_rng(951 + h)
+    dY = f32_dev(rng.standard_normal((rows, h)).astype(np.float32))
+    R, g = f32_dev(inp["R"]), f32_dev(inp["gamma"])
+    ws = torch.empty(tp.layernorm_bwd_workspace(rows, h), dtype=torch.uint8, device=DEV)
+    outs = []
+    for fill in (0x00, 0x7F):
+        ws.fill_(fill)
+        dX = torch.empty(rows, h, dtype=torch.float32, device=DEV)
+        dg = torch.empty(h, dtype=torch.float32, device=DEV)
+        db = torch.empty(h, dtype=torch.float32, device=DEV)
+        tp.layernorm_bwd(R, g, dY, dX, dg, db, ws)
+        torch.cuda.synchronize()
+        outs.append((dX, dg, db))
+    for a, b_ in zip(*outs):
+        assert torch.equal(a.view(torch.int32), b_.view(torch.int32))
+
+
 def test_dropout_bwd():
     for rows, h, drop in [(3, 8, False), (17, 72, True), (256, 12288, True)]:
         note(f"sp_dropout_bwd rows={rows} h={h} dropout={drop}")
