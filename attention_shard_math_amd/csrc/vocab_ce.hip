@@ -6,8 +6,9 @@
 // those partial sums over the ranks, and each row's loss is log(sum) - logit_t.
 //
 // ce_rows: one wave per row, 16-byte loads strided over the lanes (each load
-// instruction reads 1 KiB of the row), exp in float32, the lanes' partial sums
-// added in a fixed butterfly. It is HBM-bound: 4*V bytes read per row.
+// instruction reads 1 KiB of the row, four in flight per lane), exp in float32,
+// the lanes' partial sums added in a fixed butterfly. It is HBM-bound: 4*V
+// bytes read per row.
 // ce_loss: one workgroup; the partial sums are added in rank order and the
 // row losses reduced through LDS in a fixed tree, so the scalar is reproducible.
 #include "common.hpp"
@@ -26,7 +27,18 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
   float acc = 0.f;
   if ((V & 3) == 0) {  // rows start 16-byte aligned
     const f32x4* r4 = reinterpret_cast<const f32x4*>(r);
-    for (int i = lane; i < (V >> 2); i += 64) {
+    const int n4 = V >> 2;
+    int i = lane;
+    // Four loads in flight per lane (one wave per row leaves few waves per SIMD
+    // to hide the latency); the additions keep the order of the plain loop.
+    for (; i + 192 < n4; i += 256) {
+      f32x4 x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = r4[i + 64 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += (expf(x[u][0]) + expf(x[u][1])) + (expf(x[u][2]) + expf(x[u][3]));
+    }
+    for (; i < n4; i += 64) {
       const f32x4 x = r4[i];
       acc += (expf(x[0]) + expf(x[1])) + (expf(x[2]) + expf(x[3]));
     }
