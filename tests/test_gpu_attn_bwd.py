@@ -51,9 +51,13 @@ def _core_case(b, s, Hl, d, causal, seed):
     return qkv, dO, O, lse, dq, (Q, bf16_dev(dO), ws)
 
 
+# Walks longer than 16 key (or query) tiles of 32 are cut into chunks whose fp32
+# partials a combine pass adds: s = 513 and 530 (causal) and s = 600 (every block,
+# not causal) cover that path for both head sizes.
 @pytest.mark.parametrize("b,s,Hl,d,causal", [(2, 300, 2, 128, True), (1, 77, 3, 64, True),
                                               (2, 200, 2, 128, False), (1, 1, 1, 128, True),
-                                              (3, 129, 1, 64, False), (1, 513, 1, 128, True)])
+                                              (3, 129, 1, 64, False), (1, 513, 1, 128, True),
+                                              (2, 530, 1, 64, True), (1, 600, 2, 64, False)])
 def test_core_backward(b, s, Hl, d, causal):
     note(f"attn_core_bwd b={b} s={s} Hl={Hl} d={d} causal={causal}")
     qkv, dO, O, lse, dq, _ = _core_case(b, s, Hl, d, causal, 90 + s + d)
