@@ -1,6 +1,7 @@
 """The C ABI is capture-safe: no allocation, no synchronisation and no memset
-inside any call, so a whole training step of the rank shard can be recorded in
-a HIP graph (through torch.cuda.graph) and replayed. Every replay, with eager
+inside any call, so a whole training step of the rank shard (MLP, attention,
+shard-sum and the sequence-parallel kernels) can be recorded in a HIP graph
+(through torch.cuda.graph) and replayed. Every replay, with eager
 work and synchronisations in between, must reproduce the eager results bit for
 bit (the kernels are deterministic)."""
 import numpy as np
@@ -42,7 +43,22 @@ def test_step_in_a_graph_replays_bit_exactly():
     dWo = torch.empty(w, h, dtype=torch.float32, device=DEV)
     wsb = torch.empty(tp.attn_bwd_workspace(b, s, h, Hl, d), dtype=torch.uint8, device=DEV)
     tot = torch.empty(M, h, dtype=torch.float32, device=DEV)
-    outs = (U, Y, Z, dX, dA, dB, out, QKV, O, lse, dXa, dWqkv, dWo, tot)
+    # sequence-parallel kernels: 2 ranks of 128 rows over the same h
+    rng = np.random.default_rng(34)
+    Rs = torch.from_numpy(draw_normal_f32(rng, (128, h), 1.0)).to(DEV)
+    gam = torch.from_numpy(draw_normal_f32(rng, (h,), 0.1)).to(DEV) + 1.0
+    bet = torch.from_numpy(draw_normal_f32(rng, (h,), 0.1)).to(DEV)
+    dYs = torch.from_numpy(draw_normal_f32(rng, (128, h), 1.0)).to(DEV)
+    keep = torch.from_numpy((rng.random((128, h)) < 0.9).astype(np.uint8)).to(DEV)
+    Ln = torch.empty(128, h, dtype=torch.bfloat16, device=DEV)
+    Lg = torch.empty(256, h, dtype=torch.bfloat16, device=DEV)
+    Ro = torch.empty(128, h, dtype=torch.float32, device=DEV)
+    dXs = torch.empty(128, h, dtype=torch.float32, device=DEV)
+    dgs = torch.empty(h, dtype=torch.float32, device=DEV)
+    dbs = torch.empty(h, dtype=torch.float32, device=DEV)
+    dZs = torch.empty(128, h, dtype=torch.bfloat16, device=DEV)
+    lws = torch.empty(tp.layernorm_bwd_workspace(128, h), dtype=torch.uint8, device=DEV)
+    outs = (U, Y, Z, dX, dA, dB, out, QKV, O, lse, dXa, dWqkv, dWo, tot, Ln, Lg, Ro, dXs, dgs, dbs, dZs)
 
     def step():
         tp.mlp_fwd(X, A, B, Y, Z, U_i=U)
@@ -50,6 +66,11 @@ def test_step_in_a_graph_replays_bit_exactly():
         tp.attn_fwd_train(Xa, Wqkv, Wo, out, QKV, O, lse, b, s, Hl, d, True)
         tp.attn_bwd(Xa, Wqkv, Wo, QKV, O, lse, dOut, dXa, dWqkv, dWo, wsb, b, s, Hl, d, True)
         tp.shard_sum([Z, dX], tot)
+        tp.layernorm(Rs, gam, bet, Ln)
+        tp.sp_all_gather([Ln, Ln], Lg)
+        tp.sp_reduce_scatter([Z[:256], dX[:256]], 1, Rs, Ro, keep=keep, keep_prob=0.9)
+        tp.layernorm_bwd(Rs, gam, dYs, dXs, dgs, dbs, lws, dRes=Ro)
+        tp.sp_dropout_bwd(dYs, dZs, keep=keep, keep_prob=0.9)
 
     note("graph: eager step")
     side = torch.cuda.Stream()
@@ -72,5 +93,5 @@ def test_step_in_a_graph_replays_bit_exactly():
         graph.replay()
         torch.cuda.synchronize()
         for name, g, e in zip(("U", "Y", "Z", "dX", "dA", "dB", "out", "QKV", "O", "lse", "dXa", "dWqkv", "dWo",
-                               "sum"), outs, want):
+                               "sum", "ln", "gather", "rs", "ln dX", "dgamma", "dbeta", "dropout dY"), outs, want):
             assert torch.equal(g.view(torch.uint8), e.view(torch.uint8)), f"replay {r}: {name} differs"
