@@ -12,7 +12,9 @@ from ._lib import (  # noqa: F401
     lib,
     column_linear,
     row_linear,
+    linear_workspace,
     mlp_fwd,
+    mlp_fwd_workspace,
     mlp_bwd,
     mlp_bwd_workspace,
     mlp_bwd_recompute_workspace,

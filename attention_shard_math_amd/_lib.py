@@ -22,16 +22,16 @@ TP_ACT_NONE, TP_ACT_GELU = 0, 1
 _i64, _vp, _sz = C.c_int64, C.c_void_p, C.c_size_t
 
 _SIGS = {
-    "tp_column_linear": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, C.c_int, _vp],
-    "tp_row_linear": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp],
-    "tp_mlp_fwd": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
+    "tp_column_linear": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, C.c_int, _vp, _sz, _vp],
+    "tp_row_linear": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp],
+    "tp_mlp_fwd": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_mlp_bwd": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_attn_core": [_i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp],
     "tp_attn_fwd": [_i64, _i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_vocab_embed": [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp],
     "tp_shard_sum": [C.c_int, C.POINTER(_vp), C.c_int, _i64, _vp, _vp],
-    "tp_vocab_ce_partials": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
-    "tp_vocab_ce_loss": [_i64, C.POINTER(_vp), C.POINTER(_vp), C.c_int, _vp, _vp, _vp],
+    "tp_vocab_ce_partials": [_i64, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "tp_vocab_ce_loss": [_i64, C.POINTER(_vp), C.POINTER(_vp), C.POINTER(_vp), C.c_int, _vp, _vp, _vp],
     "tp_attn_core_train": [_i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp],
     "tp_attn_fwd_train": [_i64, _i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_attn_core_bwd": [_i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
@@ -51,7 +51,7 @@ lib.tp_mlp_bwd_workspace.argtypes = [_i64, _i64, _i64]
 lib.tp_mlp_bwd_workspace.restype = _sz
 lib.tp_mlp_bwd_recompute_workspace.argtypes = [_i64, _i64, _i64]
 lib.tp_mlp_bwd_recompute_workspace.restype = _sz
-lib.tp_vocab_ce_workspace.argtypes = [_i64, _i64, _i64]
+lib.tp_vocab_ce_workspace.argtypes = [_i64, _i64, _i64, _i64]
 lib.tp_layernorm_bwd_workspace.argtypes = [_i64, _i64]
 lib.tp_layernorm_bwd_workspace.restype = _sz
 lib.tp_attn_core_bwd_workspace.argtypes = [_i64, _i64, _i64]
@@ -59,8 +59,12 @@ lib.tp_attn_core_bwd_workspace.restype = _sz
 lib.tp_attn_bwd_workspace.argtypes = [_i64, _i64, _i64, _i64, _i64]
 lib.tp_attn_bwd_workspace.restype = _sz
 lib.tp_vocab_ce_workspace.restype = _sz
-lib.tp_attn_fwd_workspace.argtypes = [_i64, _i64, _i64, _i64]
+lib.tp_attn_fwd_workspace.argtypes = [_i64, _i64, _i64, _i64, _i64]
 lib.tp_attn_fwd_workspace.restype = _sz
+lib.tp_linear_workspace.argtypes = [C.c_int, _i64, _i64, _i64]
+lib.tp_linear_workspace.restype = _sz
+lib.tp_mlp_fwd_workspace.argtypes = [C.c_int, _i64, _i64, _i64]
+lib.tp_mlp_fwd_workspace.restype = _sz
 lib.tp_status_string.argtypes = [C.c_int]
 lib.tp_status_string.restype = C.c_char_p
 lib.tp_last_error.argtypes = []
@@ -107,33 +111,48 @@ def _ptr(t, shape=None, dtype=None, name="tensor"):
     return t.data_ptr()
 
 
-def column_linear(X, W, Y, U=None, act="gelu", stream=None):
+def _wsargs(ws):
+    return (None, 0) if ws is None else (_ptr(ws, name="ws"), ws.numel() * ws.element_size())
+
+
+def linear_workspace(M, K, N, dtype=torch.bfloat16) -> int:
+    return int(lib.tp_linear_workspace(TP_BF16 if dtype == torch.bfloat16 else TP_F32, M, K, N))
+
+
+def column_linear(X, W, Y, U=None, act="gelu", ws=None, stream=None):
     """Y = act(X W) (and U = X W when act is GeLU and U is given)."""
     M, K = X.shape
     N = W.shape[1]
     dt = X.dtype
     a = TP_ACT_GELU if act == "gelu" else TP_ACT_NONE
+    wp, wb = _wsargs(ws)
     _check(lib.tp_column_linear(_dt(X), M, K, N, _ptr(X, (M, K), dt, "X"), _ptr(W, (K, N), dt, "W"),
-                                _ptr(U, (M, N), dt, "U"), _ptr(Y, (M, N), dt, "Y"), a, _stream(stream)),
+                                _ptr(U, (M, N), dt, "U"), _ptr(Y, (M, N), dt, "Y"), a, wp, wb, _stream(stream)),
            "tp_column_linear")
 
 
-def row_linear(Y, W, Z, stream=None):
+def row_linear(Y, W, Z, ws=None, stream=None):
     """Z (float32) = Y W."""
     M, K = Y.shape
     N = W.shape[1]
     dt = Y.dtype
+    wp, wb = _wsargs(ws)
     _check(lib.tp_row_linear(_dt(Y), M, K, N, _ptr(Y, (M, K), dt, "Y"), _ptr(W, (K, N), dt, "W"),
-                             _ptr(Z, (M, N), torch.float32, "Z"), _stream(stream)), "tp_row_linear")
+                             _ptr(Z, (M, N), torch.float32, "Z"), wp, wb, _stream(stream)), "tp_row_linear")
 
 
-def mlp_fwd(X, A_i, B_i, Y_i, Z_i, U_i=None, stream=None):
+def mlp_fwd_workspace(M, h, f, dtype=torch.bfloat16) -> int:
+    return int(lib.tp_mlp_fwd_workspace(TP_BF16 if dtype == torch.bfloat16 else TP_F32, M, h, f))
+
+
+def mlp_fwd(X, A_i, B_i, Y_i, Z_i, U_i=None, ws=None, stream=None):
     M, h = X.shape
     f = A_i.shape[1]
     dt = X.dtype
+    wp, wb = _wsargs(ws)
     _check(lib.tp_mlp_fwd(_dt(X), M, h, f, _ptr(X, (M, h), dt, "X"), _ptr(A_i, (h, f), dt, "A_i"),
                           _ptr(B_i, (f, h), dt, "B_i"), _ptr(U_i, (M, f), dt, "U_i"), _ptr(Y_i, (M, f), dt, "Y_i"),
-                          _ptr(Z_i, (M, h), torch.float32, "Z_i"), _stream(stream)), "tp_mlp_fwd")
+                          _ptr(Z_i, (M, h), torch.float32, "Z_i"), wp, wb, _stream(stream)), "tp_mlp_fwd")
 
 
 def mlp_bwd_workspace(M, h, f) -> int:
@@ -165,8 +184,8 @@ def attn_core(QKV, O, b, s, n_heads_local, d_head, causal=True, stream=None):
                             _ptr(O, (b * s, w), bf, "O"), _stream(stream)), "tp_attn_core")
 
 
-def attn_fwd_workspace(b, s, n_heads_local, d_head) -> int:
-    return int(lib.tp_attn_fwd_workspace(b, s, n_heads_local, d_head))
+def attn_fwd_workspace(b, s, n_heads_local, d_head, h) -> int:
+    return int(lib.tp_attn_fwd_workspace(b, s, h, n_heads_local, d_head))
 
 
 def attn_fwd(X, Wqkv_i, Wo_i, out, ws, b, s, n_heads_local, d_head, causal=True, stream=None):
@@ -183,12 +202,9 @@ def attn_fwd(X, Wqkv_i, Wo_i, out, ws, b, s, n_heads_local, d_head, causal=True,
 def vocab_embed(ids, E_i, lo, hi, out, stream=None):
     n = ids.numel()
     h = E_i.shape[1]
-    _check(lib.tp_vocab_embed(_ptr(ids, dtype=torch.int32, name="ids"), n, _ptr(E_i, (hi - lo, h), None, "E_i"),
-                              lo, hi, h, _ptr(out, (n, h), E_i.dtype, "out"), _stream(stream)), "tp_vocab_embed")
-
-
-def _wsargs(ws):
-    return (None, 0) if ws is None else (_ptr(ws, name="ws"), ws.numel() * ws.element_size())
+    bf = torch.bfloat16
+    _check(lib.tp_vocab_embed(_ptr(ids, dtype=torch.int32, name="ids"), n, _ptr(E_i, (hi - lo, h), bf, "E_i"),
+                              lo, hi, h, _ptr(out, (n, h), bf, "out"), _stream(stream)), "tp_vocab_embed")
 
 
 def attn_core_train(QKV, O, lse, b, s, n_heads_local, d_head, causal=True, stream=None):
@@ -244,30 +260,35 @@ def attn_bwd(X, Wqkv_i, Wo_i, QKV, O, lse, dOut, dX_i, dWqkv_i, dWo_i, ws, b, s,
                            _ptr(dWo_i, (w, h), f32, "dWo_i"), wp, wb, _stream(stream)), "tp_attn_bwd")
 
 
-def vocab_ce_workspace(M, lo, hi):
-    return int(lib.tp_vocab_ce_workspace(M, lo, hi))
+def vocab_ce_workspace(M, h, lo, hi):
+    return int(lib.tp_vocab_ce_workspace(M, h, lo, hi))
 
 
-def vocab_ce_partials(H, E_i, targets, lo, hi, sumexp_i, tlogit_i, ws, stream=None):
+def vocab_ce_partials(H, E_i, targets, lo, hi, rowmax_i, sumexp_i, tlogit_i, ws, stream=None):
     M, h = H.shape
     V = hi - lo
+    f32 = torch.float32
     _check(lib.tp_vocab_ce_partials(M, h, lo, hi, _ptr(H, (M, h), torch.bfloat16, "H"),
                                     _ptr(E_i, (V, h), torch.bfloat16, "E_i"),
                                     _ptr(targets, (M,), torch.int32, "targets"),
-                                    _ptr(sumexp_i, (M,), torch.float32, "sumexp_i"),
-                                    _ptr(tlogit_i, (M,), torch.float32, "tlogit_i"),
-                                    _ptr(ws, name="ws"), 0 if ws is None else ws.numel() * ws.element_size(),
-                                    _stream(stream)), "tp_vocab_ce_partials")
+                                    _ptr(rowmax_i, (M,), f32, "rowmax_i"),
+                                    _ptr(sumexp_i, (M,), f32, "sumexp_i"),
+                                    _ptr(tlogit_i, (M,), f32, "tlogit_i"),
+                                    *_wsargs(ws), _stream(stream)), "tp_vocab_ce_partials")
 
 
-def vocab_ce_loss(sumexp_parts, tlogit_parts, loss_rows, loss_sum, stream=None):
+def vocab_ce_loss(rowmax_parts, sumexp_parts, tlogit_parts, loss_rows, loss_sum, stream=None):
     n = len(sumexp_parts)
-    if len(tlogit_parts) != n:
-        raise ValueError("sumexp_parts and tlogit_parts differ in length")
+    if len(tlogit_parts) != n or len(rowmax_parts) != n:
+        raise ValueError("rowmax_parts, sumexp_parts and tlogit_parts differ in length")
     M = loss_rows.numel()
-    sa = (_vp * max(n, 1))(*[_ptr(p, (M,), torch.float32, f"sumexp_parts[{i}]") for i, p in enumerate(sumexp_parts)])
-    ta = (_vp * max(n, 1))(*[_ptr(p, (M,), torch.float32, f"tlogit_parts[{i}]") for i, p in enumerate(tlogit_parts)])
-    _check(lib.tp_vocab_ce_loss(M, sa, ta, n, _ptr(loss_rows, (M,), torch.float32, "loss_rows"),
+
+    def arr(parts, name):
+        return (_vp * max(n, 1))(*[_ptr(p, (M,), torch.float32, f"{name}[{i}]") for i, p in enumerate(parts)])
+
+    _check(lib.tp_vocab_ce_loss(M, arr(rowmax_parts, "rowmax_parts"), arr(sumexp_parts, "sumexp_parts"),
+                                arr(tlogit_parts, "tlogit_parts"), n,
+                                _ptr(loss_rows, (M,), torch.float32, "loss_rows"),
                                 _ptr(loss_sum, (1,), torch.float32, "loss_sum"), _stream(stream)),
            "tp_vocab_ce_loss")
 
@@ -329,3 +350,4 @@ def shard_sum(partials, out, stream=None):
         if p.numel() != numel:
             raise ValueError(f"partials[{i}] has {p.numel()} elements, out has {numel}")
     _check(lib.tp_shard_sum(_dt(out), arr, n, numel, _ptr(out, name="out"), _stream(stream)), "tp_shard_sum")
+

@@ -16,6 +16,7 @@
 #include "bandwidth.hpp"
 #include "gemm_bf16.hpp"
 #include "gemm_f32.hpp"
+#include "api_internal.hpp"
 #include "tpshard.h"
 
 #define TP_API extern "C" __attribute__((visibility("default")))
@@ -72,6 +73,16 @@ tp_status check_opt_ptr(const char* fn, const char* name, const void* p) {
   return TP_OK;
 }
 
+// The GEMM and attention kernels address each operand through a buffer resource
+// with 32-bit byte offsets, so no operand may reach 2 GiB.
+constexpr double kMaxOperandBytes = 2147483632.0;  // 2^31 - 16
+tp_status check_bytes(const char* fn, const char* name, int64_t rows, int64_t cols, int64_t elem) {
+  if ((double)rows * (double)cols * (double)elem >= kMaxOperandBytes)
+    return fail(TP_ERR_UNSUPPORTED, "%s: %s [%lld x %lld] reaches 2 GiB; the kernels address operands with 32-bit byte offsets",
+                fn, name, (long long)rows, (long long)cols);
+  return TP_OK;
+}
+
 #define TRY(expr)                      \
   do {                                 \
     const tp_status _s = (expr);       \
@@ -123,8 +134,22 @@ TP_API const char* tp_status_string(tp_status s) {
 
 TP_API const char* tp_last_error(void) { return g_last_error.c_str(); }
 
+namespace {
+// Workspace of an optional stream-K area passed to a call that takes one: NULL
+// runs the products one tile per workgroup; a non-NULL workspace must hold `need`.
+tp_status check_opt_ws(const char* fn, const void* ws, size_t ws_bytes, size_t need) {
+  if (ws && ws_bytes < need)
+    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu", fn, need, ws_bytes);
+  return check_opt_ptr(fn, "ws", ws);
+}
+}  // namespace
+
+TP_API size_t tp_linear_workspace(tp_dtype dt, int64_t M, int64_t K, int64_t N) {
+  return dt == TP_BF16 ? sk_need(M, N, K) : 0;
+}
+
 TP_API tp_status tp_column_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N, const void* X, const void* W,
-                                  void* U_out, void* Y_out, int act, void* stream) {
+                                  void* U_out, void* Y_out, int act, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "tp_column_linear";
   if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   if (act != TP_ACT_NONE && act != TP_ACT_GELU) return fail(TP_ERR_INVALID_ARG, "%s: unknown activation %d", fn, act);
@@ -136,21 +161,25 @@ TP_API tp_status tp_column_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N, 
   TRY(check_ptr(fn, "W", W));
   TRY(check_ptr(fn, "Y_out", Y_out));
   TRY(check_opt_ptr(fn, "U_out", U_out));
+  TRY(check_opt_ws(fn, ws, ws_bytes, tp_linear_workspace(dt, M, K, N)));
   if (dt == TP_F32)
     return hip_status(tps::gemm_f32(static_cast<const float*>(X), static_cast<const float*>(W), (int)M, (int)N, (int)K,
                                     static_cast<float*>(Y_out), static_cast<float*>(U_out), act == TP_ACT_GELU,
                                     as_stream(stream)),
                       fn);
+  TRY(check_bytes(fn, "X", M, K, 2));
+  TRY(check_bytes(fn, "W", K, N, 2));
   tps::GemmArgs g = make_args(X, K, W, N, M, N, K, Y_out, N);
   g.U = static_cast<uint16_t*>(U_out);
   g.ldu = N;
+  tps::gemm_bf16_sk_attach(g, ws);
   return hip_status(tps::gemm_bf16(g, true, false, act == TP_ACT_GELU ? tps::EPI_GELU : tps::EPI_BF16,
                                    as_stream(stream)),
                     fn);
 }
 
 TP_API tp_status tp_row_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N, const void* Y, const void* W,
-                               float* Z_out, void* stream) {
+                               float* Z_out, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "tp_row_linear";
   if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   TRY(check_dims(fn, M, K, N));
@@ -158,16 +187,26 @@ TP_API tp_status tp_row_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N, con
   TRY(check_ptr(fn, "Y", Y));
   TRY(check_ptr(fn, "W", W));
   TRY(check_ptr(fn, "Z_out", Z_out));
+  TRY(check_opt_ws(fn, ws, ws_bytes, tp_linear_workspace(dt, M, K, N)));
   if (dt == TP_F32)
     return hip_status(tps::gemm_f32(static_cast<const float*>(Y), static_cast<const float*>(W), (int)M, (int)N, (int)K,
                                     Z_out, nullptr, false, as_stream(stream)),
                       fn);
+  TRY(check_bytes(fn, "Y", M, K, 2));
+  TRY(check_bytes(fn, "W", K, N, 2));
   tps::GemmArgs g = make_args(Y, K, W, N, M, N, K, Z_out, N);
+  tps::gemm_bf16_sk_attach(g, ws);
   return hip_status(tps::gemm_bf16(g, true, false, tps::EPI_F32, as_stream(stream)), fn);
 }
 
+TP_API size_t tp_mlp_fwd_workspace(tp_dtype dt, int64_t M, int64_t h, int64_t f) {
+  // the two products run one after the other and share the area
+  return sk_max({tp_linear_workspace(dt, M, h, f), tp_linear_workspace(dt, M, f, h)});
+}
+
 TP_API tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f, const void* X, const void* A_i,
-                            const void* B_i, void* U_i, void* Y_i, float* Z_i, void* stream) {
+                            const void* B_i, void* U_i, void* Y_i, float* Z_i, void* ws, size_t ws_bytes,
+                            void* stream) {
   const char* fn = "tp_mlp_fwd";
   if (dt != TP_F32 && dt != TP_BF16) return fail(TP_ERR_INVALID_ARG, "%s: unknown dtype %d", fn, (int)dt);
   TRY(check_dims(fn, M, h, f));
@@ -178,8 +217,15 @@ TP_API tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f, const 
   TRY(check_ptr(fn, "Y_i", Y_i));
   TRY(check_ptr(fn, "Z_i", Z_i));
   TRY(check_opt_ptr(fn, "U_i", U_i));
-  TRY(tp_column_linear(dt, M, h, f, X, A_i, U_i, Y_i, TP_ACT_GELU, stream));
-  return tp_row_linear(dt, M, f, h, Y_i, B_i, Z_i, stream);
+  TRY(check_opt_ws(fn, ws, ws_bytes, tp_mlp_fwd_workspace(dt, M, h, f)));
+  if (dt == TP_BF16) {  // validate both products before the first launch
+    TRY(check_bytes(fn, "X", M, h, 2));
+    TRY(check_bytes(fn, "A_i", h, f, 2));
+    TRY(check_bytes(fn, "Y_i", M, f, 2));
+    TRY(check_bytes(fn, "B_i", f, h, 2));
+  }
+  TRY(tp_column_linear(dt, M, h, f, X, A_i, U_i, Y_i, TP_ACT_GELU, ws, ws_bytes, stream));
+  return tp_row_linear(dt, M, f, h, Y_i, B_i, Z_i, ws, ws_bytes, stream);
 }
 
 namespace {
@@ -199,10 +245,23 @@ TP_API size_t tp_mlp_bwd_recompute_workspace(int64_t M, int64_t h, int64_t f) {
   return 3 * round256((size_t)M * (size_t)f * 2) + mlp_bwd_sk(M, h, f);
 }
 
-TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, const void* A_i, const void* B_i,
-                            const void* U_i, const void* Y_i, const void* dZ, float* dX_i, float* dA_i, float* dB_i,
-                            void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "tp_mlp_bwd";
+namespace tps {
+
+tp_status api_fail(tp_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+tp_status api_ok() { return ok(); }
+
+tp_status mlp_bwd_validate(const char* fn, int64_t M, int64_t h, int64_t f, const void* X, const void* A_i,
+                           const void* B_i, const void* U_i, const void* Y_i, const void* dZ, const float* dX_i,
+                           const float* dA_i, const float* dB_i) {
   TRY(check_dims(fn, M, h, f));
   TRY(check_opt_ptr(fn, "dA_i", dA_i));
   TRY(check_opt_ptr(fn, "dB_i", dB_i));
@@ -214,28 +273,18 @@ TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, cons
     TRY(check_opt_ptr(fn, "Y_i", Y_i));
     TRY(check_ptr(fn, "dZ", dZ));
     TRY(check_opt_ptr(fn, "dX_i", dX_i));
+    TRY(check_bytes(fn, "X", M, h, 2));
+    TRY(check_bytes(fn, "dZ", M, h, 2));
+    TRY(check_bytes(fn, "A_i", h, f, 2));
+    TRY(check_bytes(fn, "B_i", f, h, 2));
+    TRY(check_bytes(fn, "U_i", M, f, 2));
   }
-  // Without a saved U_i or Y_i the column GEMM + GeLU is recomputed into the
-  // workspace, with the forward's kernel, so the bits equal the forward's.
-  const bool recompute = M > 0 && (!U_i || !Y_i);
-  const size_t need = recompute ? tp_mlp_bwd_recompute_workspace(M, h, f) : tp_mlp_bwd_workspace(M, h, f);
-  if (need && (!ws || ws_bytes < need))
-    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
-                ws ? "" : " (NULL)");
-  TRY(check_opt_ptr(fn, "ws", ws));
-  hipStream_t s = as_stream(stream);
-  uint16_t* dU = static_cast<uint16_t*>(ws);
-  // the stream-K area follows the activations
-  void* sk = mlp_bwd_sk(M, h, f) ? static_cast<char*>(ws) + (recompute ? 3 : 1) * round256((size_t)M * (size_t)f * 2)
-                                 : nullptr;
-  if (recompute) {
-    const size_t act = round256((size_t)M * (size_t)f * 2);
-    uint16_t* U_re = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + act);
-    uint16_t* Y_re = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + 2 * act);
-    TRY(tp_column_linear(TP_BF16, M, h, f, X, A_i, U_re, Y_re, TP_ACT_GELU, stream));
-    if (!U_i) U_i = U_re;
-    if (!Y_i) Y_i = Y_re;
-  }
+  return TP_OK;
+}
+
+tp_status mlp_bwd_products(const char* fn, int64_t M, int64_t h, int64_t f, const void* X, const void* A_i,
+                           const void* B_i, const void* U_i, const void* Y_i, const void* dZ, float* dX_i,
+                           float* dA_i, float* dB_i, uint16_t* dU, void* sk, hipStream_t s) {
   if (M > 0) {
     // dU = (dZ B_i^T) * GeLU'(U_i): A = dZ [M,h] (K-contig), B(k,n) = B_i[n, k] (K-contig).
     tps::GemmArgs g = make_args(dZ, h, B_i, h, M, f, h, dU, f);
@@ -262,6 +311,36 @@ TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, cons
   return ok();
 }
 
+}  // namespace tps
+
+TP_API tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f, const void* X, const void* A_i, const void* B_i,
+                            const void* U_i, const void* Y_i, const void* dZ, float* dX_i, float* dA_i, float* dB_i,
+                            void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "tp_mlp_bwd";
+  TRY(tps::mlp_bwd_validate(fn, M, h, f, X, A_i, B_i, U_i, Y_i, dZ, dX_i, dA_i, dB_i));
+  // Without a saved U_i or Y_i the column GEMM + GeLU is recomputed into the
+  // workspace, with the forward's kernel, so the bits equal the forward's.
+  const bool recompute = M > 0 && (!U_i || !Y_i);
+  const size_t need = recompute ? tp_mlp_bwd_recompute_workspace(M, h, f) : tp_mlp_bwd_workspace(M, h, f);
+  if (need && (!ws || ws_bytes < need))
+    return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
+                ws ? "" : " (NULL)");
+  TRY(check_opt_ptr(fn, "ws", ws));
+  uint16_t* dU = static_cast<uint16_t*>(ws);
+  // the stream-K area follows the activations
+  void* sk = mlp_bwd_sk(M, h, f) ? static_cast<char*>(ws) + (recompute ? 3 : 1) * round256((size_t)M * (size_t)f * 2)
+                                 : nullptr;
+  if (recompute) {
+    const size_t act = round256((size_t)M * (size_t)f * 2);
+    uint16_t* U_re = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + act);
+    uint16_t* Y_re = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + 2 * act);
+    TRY(tp_column_linear(TP_BF16, M, h, f, X, A_i, U_re, Y_re, TP_ACT_GELU, nullptr, 0, stream));
+    if (!U_i) U_i = U_re;
+    if (!Y_i) Y_i = Y_re;
+  }
+  return tps::mlp_bwd_products(fn, M, h, f, X, A_i, B_i, U_i, Y_i, dZ, dX_i, dA_i, dB_i, dU, sk, as_stream(stream));
+}
+
 namespace {
 tp_status check_attn_shape(const char* fn, int64_t b, int64_t s, int64_t Hl, int64_t d) {
   if (b < 0 || s < 0 || Hl <= 0 || d <= 0)
@@ -272,6 +351,15 @@ tp_status check_attn_shape(const char* fn, int64_t b, int64_t s, int64_t Hl, int
   // The kernel addresses one sequence's K and V rows with 32-bit byte offsets.
   if ((s + 128) * 3 * Hl * d * 2 >= (int64_t)1 << 31)
     return fail(TP_ERR_UNSUPPORTED, "%s: s * 3 * n_heads_local * d_head too large for one sequence", fn);
+  return TP_OK;
+}
+
+// Byte checks of the attention shard's GEMM operands (M tokens, w = Hl * d).
+tp_status check_attn_bytes(const char* fn, int64_t M, int64_t h, int64_t w) {
+  TRY(check_bytes(fn, "X", M, h, 2));
+  TRY(check_bytes(fn, "Wqkv_i", h, 3 * w, 2));
+  TRY(check_bytes(fn, "QKV", M, 3 * w, 2));
+  TRY(check_bytes(fn, "Wo_i", w, h, 2));
   return TP_OK;
 }
 }  // namespace
@@ -302,16 +390,15 @@ TP_API tp_status tp_attn_core_train(int64_t b, int64_t s, int64_t n_heads_local,
 }
 
 namespace {
-// Stream-K area of the attention forward's QKV and Wo GEMMs. The workspace query has
-// no h, which sets the Wo GEMM's tile count, so the area is reserved whenever there
-// is work.
-size_t attn_fwd_sk(int64_t M, int64_t w) { return M > 0 && w > 0 ? tps::kSkBytes : 0; }
+// Stream-K area of the attention forward's QKV and Wo GEMMs (they run one after
+// the other and share it).
+size_t attn_fwd_sk(int64_t M, int64_t h, int64_t w) { return sk_max({sk_need(M, 3 * w, h), sk_need(M, h, w)}); }
 }  // namespace
 
-TP_API size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head) {
-  if (b < 0 || s < 0 || n_heads_local < 0 || d_head < 0) return 0;
+TP_API size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head) {
+  if (b < 0 || s < 0 || h < 0 || n_heads_local < 0 || d_head < 0) return 0;
   const size_t t = (size_t)b * (size_t)s, w = (size_t)n_heads_local * (size_t)d_head;
-  return round256(t * 3 * w * 2) + round256(t * w * 2) + attn_fwd_sk(b * s, n_heads_local * d_head);
+  return round256(t * 3 * w * 2) + round256(t * w * 2) + attn_fwd_sk(b * s, h, n_heads_local * d_head);
 }
 
 TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head, int causal,
@@ -325,7 +412,8 @@ TP_API tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   TRY(check_ptr(fn, "Wqkv_i", Wqkv_i));
   TRY(check_ptr(fn, "Wo_i", Wo_i));
   TRY(check_ptr(fn, "out_partial", out_partial));
-  const size_t need = tp_attn_fwd_workspace(b, s, n_heads_local, d_head);
+  TRY(check_attn_bytes(fn, b * s, h, n_heads_local * d_head));
+  const size_t need = tp_attn_fwd_workspace(b, s, h, n_heads_local, d_head);
   if (need && (!ws || ws_bytes < need))
     return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
                 ws ? "" : " (NULL)");
@@ -363,6 +451,7 @@ TP_API tp_status tp_attn_fwd_train(int64_t b, int64_t s, int64_t h, int64_t n_he
   TRY(check_ptr(fn, "QKV", QKV));
   TRY(check_ptr(fn, "O", O));
   TRY(check_ptr(fn, "lse", lse));
+  TRY(check_attn_bytes(fn, b * s, h, n_heads_local * d_head));
   const int64_t M = b * s, w = n_heads_local * d_head;
   hipStream_t st = as_stream(stream);
   {
@@ -442,6 +531,8 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
     TRY(check_ptr(fn, "lse", lse));
     TRY(check_ptr(fn, "dOut", dOut));
     TRY(check_ptr(fn, "dX_i", dX_i));
+    TRY(check_attn_bytes(fn, M, h, w));
+    TRY(check_bytes(fn, "dOut", M, h, 2));
   }
   const size_t need = tp_attn_bwd_workspace(b, s, h, n_heads_local, d_head);
   if (need && (!ws || ws_bytes < need))
@@ -482,15 +573,15 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   return ok();
 }
 
-TP_API size_t tp_vocab_ce_workspace(int64_t M, int64_t lo, int64_t hi) {
-  if (M < 0 || lo < 0 || hi <= lo) return 0;
+TP_API size_t tp_vocab_ce_workspace(int64_t M, int64_t h, int64_t lo, int64_t hi) {
+  if (M < 0 || h <= 0 || lo < 0 || hi <= lo) return 0;
   // the stream-K area (if the logits GEMM uses one) follows the logits
-  return round256((size_t)M * (size_t)(hi - lo) * 4) + sk_need(M, hi - lo, 1);
+  return round256((size_t)M * (size_t)(hi - lo) * 4) + sk_need(M, hi - lo, h);
 }
 
 TP_API tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t hi, const void* H, const void* E_i,
-                                      const int32_t* targets, float* sumexp_i, float* tlogit_i, void* ws,
-                                      size_t ws_bytes, void* stream) {
+                                      const int32_t* targets, float* rowmax_i, float* sumexp_i, float* tlogit_i,
+                                      void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "tp_vocab_ce_partials";
   if (lo < 0 || lo >= hi)
     return fail(TP_ERR_INVALID_ARG, "%s: need 0 <= lo < hi (got lo=%lld hi=%lld)", fn, (long long)lo, (long long)hi);
@@ -499,9 +590,12 @@ TP_API tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t 
   TRY(check_ptr(fn, "H", H));
   TRY(check_ptr(fn, "E_i", E_i));
   if (!targets) return fail(TP_ERR_INVALID_ARG, "%s: targets is NULL", fn);
+  TRY(check_ptr(fn, "rowmax_i", rowmax_i));
   TRY(check_ptr(fn, "sumexp_i", sumexp_i));
   TRY(check_ptr(fn, "tlogit_i", tlogit_i));
-  const size_t need = tp_vocab_ce_workspace(M, lo, hi);
+  TRY(check_bytes(fn, "H", M, h, 2));
+  TRY(check_bytes(fn, "E_i", hi - lo, h, 2));
+  const size_t need = tp_vocab_ce_workspace(M, h, lo, hi);
   if (!ws || ws_bytes < need)
     return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
                 ws ? "" : " (NULL)");
@@ -513,24 +607,27 @@ TP_API tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t 
   tps::GemmArgs g = make_args(H, h, E_i, h, M, V, h, logits, V);
   tps::gemm_bf16_sk_attach(g, static_cast<char*>(ws) + round256((size_t)M * (size_t)V * 4));
   TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_F32, st), fn));
-  return hip_status(tps::ce_rows(logits, M, (int)V, targets, lo, sumexp_i, tlogit_i, st), fn);
+  return hip_status(tps::ce_rows(logits, M, (int)V, targets, lo, rowmax_i, sumexp_i, tlogit_i, st), fn);
 }
 
-TP_API tp_status tp_vocab_ce_loss(int64_t M, const float* const* sumexp_parts, const float* const* tlogit_parts,
-                                  int n_parts, float* loss_rows, float* loss_sum, void* stream) {
+TP_API tp_status tp_vocab_ce_loss(int64_t M, const float* const* rowmax_parts, const float* const* sumexp_parts,
+                                  const float* const* tlogit_parts, int n_parts, float* loss_rows, float* loss_sum,
+                                  void* stream) {
   const char* fn = "tp_vocab_ce_loss";
   if (M < 0) return fail(TP_ERR_INVALID_ARG, "%s: M < 0", fn);
   if (M > kMaxDim) return fail(TP_ERR_UNSUPPORTED, "%s: M exceeds 2^31-1", fn);
   if (n_parts < 1 || n_parts > tps::kCeMaxParts)
     return fail(TP_ERR_INVALID_ARG, "%s: n_parts must be in [1, %d] (got %d)", fn, tps::kCeMaxParts, n_parts);
-  if (!sumexp_parts || !tlogit_parts) return fail(TP_ERR_INVALID_ARG, "%s: part arrays are NULL", fn);
+  if (!rowmax_parts || !sumexp_parts || !tlogit_parts) return fail(TP_ERR_INVALID_ARG, "%s: part arrays are NULL", fn);
   TRY(check_ptr(fn, "loss_sum", loss_sum));
   tps::CeParts p{};
   if (M > 0) {
     TRY(check_ptr(fn, "loss_rows", loss_rows));
     for (int i = 0; i < n_parts; ++i) {
+      TRY(check_ptr(fn, "rowmax_parts[i]", rowmax_parts[i]));
       TRY(check_ptr(fn, "sumexp_parts[i]", sumexp_parts[i]));
       TRY(check_ptr(fn, "tlogit_parts[i]", tlogit_parts[i]));
+      p.m[i] = rowmax_parts[i];
       p.s[i] = sumexp_parts[i];
       p.t[i] = tlogit_parts[i];
     }

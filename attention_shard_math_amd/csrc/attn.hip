@@ -35,6 +35,13 @@
 // rescaled. Numerator and denominator share the reference, so the result is
 // the same softmax up to rounding.
 //
+// The training variant (which also writes the log-sum-exp for the backward)
+// feeds P to the P V product as two bf16 MFMA operands, P_hi = bf16(P) and
+// P_lo = bf16(P - P_hi), so P enters the product with about 16 significant
+// bits instead of 8: the stored O then rounds to the same bf16 value as the
+// exact result in all but a small fraction of entries, which keeps the
+// weight gradients formed from O (dWo = O^T dOut) within the bf16 bar.
+//
 // Causal stages wholly above a wave's queries are skipped. Workgroup i runs on
 // XCD i % 8; each XCD takes a contiguous, head-major range of (head, query
 // block) items, heaviest query block first, so the K and V of a head are read
@@ -80,7 +87,7 @@ __device__ __forceinline__ int swz_k(int key) { return D == 128 ? (key & 15) : (
 // V^T stage rows [d][key'] of 64 keys: 16-byte chunk c of row d sits at c ^ swz_v(d).
 __device__ __forceinline__ int swz_v(int d) { return (d ^ (d >> 3)) & 7; }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool SPLIT>
 __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ O, int s,
                                                       int Hl, int nqb, int per_xcd, int n_items, float scale_log2,
                                                       float* __restrict__ lse) {
@@ -256,20 +263,23 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
       }
       const float mref = m_i == kNegInf ? 0.f : m_i;
       float rs = 0.f;
-      bf16x8 pb[2][2];
+      bf16x8 pb[2][2], pl[2][2];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          u32x4 u;
+          u32x4 u, ul;
 #pragma unroll
           for (int w = 0; w < 4; ++w) {
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w], scale_log2, -mref));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w + 1], scale_log2, -mref));
             rs += p0 + p1;
             u[w] = cvt_bf16x2(p0, p1);
+            if constexpr (SPLIT)
+              ul[w] = cvt_bf16x2(p0 - bf16_bits_to_f32(u[w] & 0xffffu), p1 - bf16_bits_to_f32(u[w] >> 16));
           }
           pb[t][s2] = __builtin_bit_cast(bf16x8, u);
+          if constexpr (SPLIT) pl[t][s2] = __builtin_bit_cast(bf16x8, ul);
         }
       scores(sKn, sn);
       // O^T += V^T P^T over the 16-key groups 2t + s2; P^T lane (lr, hh) holds
@@ -283,6 +293,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
             const int d = 32 * i + lr;
             const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((4 * t + 2 * s2 + hh) ^ swz_v(d)) << 3));
             ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][s2], ot[i], 0, 0, 0);
+            if constexpr (SPLIT) ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[t][s2], ot[i], 0, 0, 0);
           }
       l_i += rs;
     } else {
@@ -316,7 +327,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
   }
 }
 
-template <int D, bool C>
+template <int D, bool C, bool SPLIT>
 hipError_t launch_attn(const uint16_t* qkv, uint16_t* O, float* lse, int b, int s, int Hl, hipStream_t st) {
   const int nqb = (s + AQ - 1) / AQ;
   const int64_t items = (int64_t)b * Hl * nqb;
@@ -325,19 +336,28 @@ hipError_t launch_attn(const uint16_t* qkv, uint16_t* O, float* lse, int b, int 
   if (items > (1LL << 28) || (int64_t)(s + 2 * KVB) * 3 * Hl * D * 2 >= (1LL << 31)) return hipErrorInvalidValue;
   const int per_xcd = (int)((items + 7) / 8);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)D);
-  hipLaunchKernelGGL((attn_fwd_kernel<D, C>), dim3(8u * per_xcd), dim3(NT), 0, st, qkv, O, s, Hl, nqb, per_xcd,
+  hipLaunchKernelGGL((attn_fwd_kernel<D, C, SPLIT>), dim3(8u * per_xcd), dim3(NT), 0, st, qkv, O, s, Hl, nqb, per_xcd,
                      (int)items, scale_log2, lse);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t attn_fwd_d(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, bool causal, hipStream_t st,
+                      float* lse) {
+  // with lse (training) P enters the P V product as a hi/lo bf16 pair
+  if (lse)
+    return causal ? launch_attn<D, true, true>(qkv, O, lse, b, s, Hl, st)
+                  : launch_attn<D, false, true>(qkv, O, lse, b, s, Hl, st);
+  return causal ? launch_attn<D, true, false>(qkv, O, lse, b, s, Hl, st)
+                : launch_attn<D, false, false>(qkv, O, lse, b, s, Hl, st);
 }
 
 }  // namespace
 
 hipError_t attn_fwd(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, int d, bool causal, hipStream_t st,
                     float* lse) {
-  if (d == 128)
-    return causal ? launch_attn<128, true>(qkv, O, lse, b, s, Hl, st) : launch_attn<128, false>(qkv, O, lse, b, s, Hl, st);
-  if (d == 64)
-    return causal ? launch_attn<64, true>(qkv, O, lse, b, s, Hl, st) : launch_attn<64, false>(qkv, O, lse, b, s, Hl, st);
+  if (d == 128) return attn_fwd_d<128>(qkv, O, b, s, Hl, causal, st, lse);
+  if (d == 64) return attn_fwd_d<64>(qkv, O, b, s, Hl, causal, st, lse);
   return hipErrorInvalidValue;
 }
 

@@ -29,6 +29,13 @@
 // from LDS with ds_read_b64_tr_b16, whose 4-row groups are picked to match
 // the same order, so no score tile goes through LDS.
 //
+// P and dS enter the products dV = P^T dO, dK = dS^T Q and dQ = dS K as two
+// bf16 MFMA operands each, hi = bf16(x) and lo = bf16(x - hi), so they carry
+// about 16 significant bits instead of 8. The bf16-stored dQ, dK, dV then round
+// to the same value as the exact gradient in all but a small fraction of
+// entries, which keeps the weight gradients formed from them (X^T dQKV over
+// thousands of tokens) within the bf16 bar.
+//
 // LDS rows are 256 bytes (128 bf16); 16-byte chunk c of row r is stored at
 // c ^ swz(r), swz(r) = ((r & 7) << 1) | ((r >> 3) & 1), conflict-free for the
 // 16-row ds_read_b128 fragment reads and for the 4-row x 2-chunk transposing reads.
@@ -85,6 +92,16 @@ __device__ __forceinline__ bf16x8 pack8(const float* v) {
   u32x4 u;
 #pragma unroll
   for (int w = 0; w < 4; ++w) u[w] = cvt2(v[2 * w], v[2 * w + 1]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Residual of pack8: bf16(v - hi) for the values whose bf16 rounding is hi.
+__device__ __forceinline__ bf16x8 pack8_lo(const float* v, bf16x8 hi) {
+  const u32x4 h = __builtin_bit_cast(u32x4, hi);
+  u32x4 u;
+#pragma unroll
+  for (int w = 0; w < 4; ++w)
+    u[w] = cvt2(v[2 * w] - bf16_bits_to_f32(h[w] & 0xffffu), v[2 * w + 1] - bf16_bits_to_f32(h[w] >> 16));
   return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -327,12 +344,18 @@ __device__ __forceinline__ void dkdv_item(int item, const uint16_t* __restrict__
       }
       const bf16x8 pa[2] = {pack8(p), pack8(p + 8)};
       const bf16x8 sa[2] = {pack8(ds), pack8(ds + 8)};
+      const bf16x8 pl[2] = {pack8_lo(p, pa[0]), pack8_lo(p + 8, pa[1])};
+      const bf16x8 sl[2] = {pack8_lo(ds, sa[0]), pack8_lo(ds + 8, sa[1])};
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < DT; ++i) {
-          dv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], frag_tr<D>(td, 16 * t, 32 * i, lane), dv[i], 0, 0, 0);
-          dk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], frag_tr<D>(tq, 16 * t, 32 * i, lane), dk[i], 0, 0, 0);
+          const bf16x8 fo = frag_tr<D>(td, 16 * t, 32 * i, lane);
+          const bf16x8 fq = frag_tr<D>(tq, 16 * t, 32 * i, lane);
+          dv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[t], fo, dv[i], 0, 0, 0);
+          dk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sa[t], fq, dk[i], 0, 0, 0);
+          dv[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[t], fo, dv[i], 0, 0, 0);
+          dk[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl[t], fq, dk[i], 0, 0, 0);
         }
     }
     if (j + 1 < nq) put(cur, buf ^ 1);
@@ -463,11 +486,15 @@ __device__ __forceinline__ void dq_item(int item, const uint16_t* __restrict__ q
         ds[e] = pv * (dP[e] - Dq);
       }
       const bf16x8 sa[2] = {pack8(ds), pack8(ds + 8)};
+      const bf16x8 sl[2] = {pack8_lo(ds, sa[0]), pack8_lo(ds + 8, sa[1])};
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < DT; ++i)
-          dq[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_tr<D>(tk, 16 * t, 32 * i, lane), sa[t], dq[i], 0, 0, 0);
+        for (int i = 0; i < DT; ++i) {
+          const bf16x8 fk = frag_tr<D>(tk, 16 * t, 32 * i, lane);
+          dq[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, sa[t], dq[i], 0, 0, 0);
+          dq[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, sl[t], dq[i], 0, 0, 0);
+        }
     }
     if (j + 1 < nk) {
       store_rows<D, 32, NTH>(ck, sK[buf ^ 1], tid);

@@ -183,17 +183,19 @@ def next_rows(tp, torch, dev, randn, reps=5):
     Hh = randn((Mv, Hv), 1.0, 50)
     E = randn((Vs, Hv), 0.02, 51)
     tg = torch.randint(0, 50304, (Mv,), dtype=torch.int32, generator=torch.Generator().manual_seed(52)).to(dev)
+    maxs = [torch.empty(Mv, dtype=torch.float32, device=dev) for _ in range(Nv)]
     sums = [torch.empty(Mv, dtype=torch.float32, device=dev) for _ in range(Nv)]
     tls = [torch.empty(Mv, dtype=torch.float32, device=dev) for _ in range(Nv)]
-    ws = torch.empty(tp.vocab_ce_workspace(Mv, 0, Vs), dtype=torch.uint8, device=dev)
+    ws = torch.empty(tp.vocab_ce_workspace(Mv, Hv, 0, Vs), dtype=torch.uint8, device=dev)
     rows = torch.empty(Mv, dtype=torch.float32, device=dev)
     tot = torch.empty(1, dtype=torch.float32, device=dev)
-    part = lambda: tp.vocab_ce_partials(Hh, E, tg, 0, Vs, sums[0], tls[0], ws)
+    part = lambda: tp.vocab_ce_partials(Hh, E, tg, 0, Vs, maxs[0], sums[0], tls[0], ws)
     part()
     for i in range(1, Nv):
+        maxs[i].copy_(maxs[0])
         sums[i].copy_(sums[0])
         tls[i].zero_()
-    loss = lambda: tp.vocab_ce_loss(sums, tls, rows, tot)
+    loss = lambda: tp.vocab_ce_loss(maxs, sums, tls, rows, tot)
     for name, fn in (("vocab_ce_partials", part), ("vocab_ce_loss", loss)):
         for _ in range(2):
             fn()
@@ -382,7 +384,7 @@ def main():
     Wqkv = randn((H, 3 * w), 0.006, 21)
     Wo = randn((w, H), 0.006, 22)
     out_att = torch.empty(ATT_B * ATT_S, H, dtype=torch.float32, device=dev)
-    ws_att = torch.empty(tp.attn_fwd_workspace(ATT_B, ATT_S, ATT_HL, ATT_D), dtype=torch.uint8, device=dev)
+    ws_att = torch.empty(tp.attn_fwd_workspace(ATT_B, ATT_S, ATT_HL, ATT_D, h=H), dtype=torch.uint8, device=dev)
     # ---- vocab shard 0 of 8
     per = V // VN
     E0 = randn((per, H), 0.02, 30)

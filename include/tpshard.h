@@ -70,6 +70,17 @@ typedef enum tp_dtype { TP_F32 = 0, TP_BF16 = 1 } tp_dtype;
 
 typedef enum tp_activation { TP_ACT_NONE = 0, TP_ACT_GELU = 1 } tp_activation;
 
+/* Optional stream-K workspace of the linear layers and the MLP forward: `ws` may be
+ * NULL (every product then runs one output tile per workgroup); a non-NULL `ws`
+ * must hold at least the size the matching *_workspace() query returns, else
+ * TP_ERR_WORKSPACE. A bf16 product whose 256 x 192 tiles leave the last round of
+ * the 256-workgroup grid at most half full then splits its k-range over all
+ * workgroups (the query returns 0 when no product of the call does). */
+
+/* Workspace of tp_column_linear / tp_row_linear for an [M, K] x [K, N] product
+ * (0 for TP_F32, which never uses one). */
+size_t tp_linear_workspace(tp_dtype dt, int64_t M, int64_t K, int64_t N);
+
 /* Column-parallel linear layer of one rank: Y = act(X W).
  * [Megatron-LM 介绍, 核心贡献 item 1 (ColumnParallelLinear); Megatron-LM：张量并行与
  *  大规模训练, §2.1, 列并行 — the rank holds a column block W = A_i of A.]
@@ -79,18 +90,22 @@ typedef enum tp_activation { TP_ACT_NONE = 0, TP_ACT_GELU = 1 } tp_activation;
  *   U_out  [M, N]   nullable; receives X W (before the activation) when act is
  *                   TP_ACT_GELU. Must be NULL when act is TP_ACT_NONE.
  *   Y_out  [M, N]   act(X W). GeLU is the exact form u * Phi(u).
- * K and N must be multiples of 8. */
+ *   ws     nullable stream-K workspace of tp_linear_workspace(dt, M, K, N) bytes.
+ * K and N must be multiples of 8; a bf16 operand must stay below 2 GiB
+ * (TP_ERR_UNSUPPORTED otherwise). */
 tp_status tp_column_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N,
                            const void* X, const void* W, void* U_out, void* Y_out,
-                           int act, void* stream);
+                           int act, void* ws, size_t ws_bytes, void* stream);
 
 /* Row-parallel linear layer of one rank: the float32 partial Z = Y W that the
  * all-reduce adds over ranks.
  * [Megatron-LM：张量并行与大规模训练, §2.1, 行并行 — Z_i = Y_i B_i.]
  *   Y [M, K] (dt), W [K, N] (dt) the rank's row block, Z_out [M, N] float32.
- * K and N must be multiples of 8. */
+ *   ws nullable stream-K workspace of tp_linear_workspace(dt, M, K, N) bytes.
+ * K and N must be multiples of 8; bf16 operands below 2 GiB. */
 tp_status tp_row_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N,
-                        const void* Y, const void* W, float* Z_out, void* stream);
+                        const void* Y, const void* W, float* Z_out,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* MLP forward of one rank: U_i = X A_i, Y_i = GeLU(U_i), Z_i = Y_i B_i.
  * [Megatron-LM：张量并行与大规模训练, §2.1 MLP 层的张量并行 and its pseudo-code;
@@ -100,11 +115,14 @@ tp_status tp_row_linear(tp_dtype dt, int64_t M, int64_t K, int64_t N,
  *   Y_i [M, f] (dt) required — the activation, also needed by the backward.
  *   Z_i [M, h] float32 — this rank's partial of Z (sum over ranks with
  *   tp_shard_sum in place of the all-reduce).
- * h and f must be multiples of 8. Two kernels: column GEMM + GeLU epilogue,
- * then row GEMM. */
+ *   ws nullable stream-K workspace of tp_mlp_fwd_workspace(dt, M, h, f) bytes
+ *   (shared by the two products, which run one after the other).
+ * h and f must be multiples of 8; bf16 operands below 2 GiB. Two kernels:
+ * column GEMM + GeLU epilogue, then row GEMM. */
 tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f,
                      const void* X, const void* A_i, const void* B_i,
-                     void* U_i, void* Y_i, float* Z_i, void* stream);
+                     void* U_i, void* Y_i, float* Z_i, void* ws, size_t ws_bytes, void* stream);
+size_t tp_mlp_fwd_workspace(tp_dtype dt, int64_t M, int64_t h, int64_t f);
 
 /* MLP backward of one rank, bf16 inputs, float32 outputs. With the replicated
  * upstream gradient dZ (g's backward is the identity):
@@ -123,6 +141,8 @@ tp_status tp_mlp_fwd(tp_dtype dt, int64_t M, int64_t h, int64_t f,
  *   序列并行与激活重计算 (activation recomputation).]
  *   ws: device workspace of at least tp_mlp_bwd_workspace(M, h, f) bytes, or
  *   tp_mlp_bwd_recompute_workspace(M, h, f) bytes when U_i or Y_i is NULL.
+ * The backward is bf16 only (the float32 path serves the tiny forward
+ * configuration), so it takes no dtype. Operands must stay below 2 GiB.
  * Kernels run in the order [U/Y recompute], dU, dB, dA, dX on `stream`. */
 tp_status tp_mlp_bwd(int64_t M, int64_t h, int64_t f,
                      const void* X, const void* A_i, const void* B_i,
@@ -153,14 +173,16 @@ tp_status tp_attn_core(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_he
  *  Self-Attention层 §3.1 (column split of Q, K, V by heads; B split by rows).]
  *   X [b*s, h] bf16; Wqkv_i [h, 3*Hl*d] bf16; Wo_i [Hl*d, h] bf16;
  *   out_partial [b*s, h] float32.
- *   ws: at least tp_attn_fwd_workspace(b, s, Hl, d) bytes; on return it holds
+ *   ws: at least tp_attn_fwd_workspace(b, s, h, Hl, d) bytes; on return it holds
  *   QKV bf16 [b*s, 3*Hl*d] followed (at a 256-byte aligned offset) by O bf16
- *   [b*s, Hl*d]. */
+ *   [b*s, Hl*d], then the stream-K area when one of the two products uses it.
+ *   GEMM operands must stay below 2 GiB. */
 tp_status tp_attn_fwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_local,
                       int64_t d_head, int causal, const void* X, const void* Wqkv_i,
                       const void* Wo_i, float* out_partial, void* ws, size_t ws_bytes,
                       void* stream);
-size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head);
+size_t tp_attn_fwd_workspace(int64_t b, int64_t s, int64_t h, int64_t n_heads_local,
+                             int64_t d_head);
 
 /* Vocabulary-parallel input embedding of one rank (bit copy, no arithmetic):
  *   out[t, :] = E_i[ids[t] - lo, :] if lo <= ids[t] < hi, else zeros.
@@ -172,7 +194,10 @@ tp_status tp_vocab_embed(const int32_t* ids, int64_t n_tokens, const void* E_i,
                          int64_t lo, int64_t hi, int64_t h, void* out, void* stream);
 
 /* tp_attn_core that also writes the per-query log-sum-exp the backward needs:
- *   lse float32 [b, Hl, s] = log sum_u exp(q.k_u / sqrt(d)) over the visible keys. */
+ *   lse float32 [b, Hl, s] = log sum_u exp(q.k_u / sqrt(d)) over the visible keys.
+ * P enters the P V product as two bf16 operands, bf16(P) and bf16(P - bf16(P)),
+ * so the stored O (which the backward's gradients are formed from) carries
+ * about 16 bits of P instead of 8. */
 tp_status tp_attn_core_train(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
                              const void* QKV, void* O, float* lse, void* stream);
 
@@ -217,26 +242,31 @@ size_t tp_attn_bwd_workspace(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
  *  (per-rank row sums of e = exp(logit), all-reduced into the softmax
  *  denominator, then each row's cross-entropy and the scalar sum)]:
  *   logits_i = H E_i^T                       -> float32 [M, hi-lo] in the workspace
- *   sumexp_i[m] = sum_n exp(logits_i[m, n])   -> float32 [M]
+ *   rowmax_i[m] = max_n logits_i[m, n]        -> float32 [M]
+ *   sumexp_i[m] = sum_n exp(logits_i[m, n] - rowmax_i[m]) -> float32 [M]
  *   tlogit_i[m] = logits_i[m, t[m] - lo] if lo <= t[m] < hi, else 0 -> float32 [M]
  *   H [M,h] and E_i [hi-lo, h]: bf16; targets [M] int32 (device).
- *   Requires 0 <= lo < hi, h and hi-lo multiples of 8. e is exp(logit) as the
- *   page states it (no maximum subtracted): logits above ~88 overflow float32.
- *   ws: at least tp_vocab_ce_workspace(M, lo, hi) bytes. */
+ *   The page's sum of e over the rank's columns is exp(rowmax_i) * sumexp_i: it is
+ *   carried relative to the row maximum so that no logit overflows float32.
+ *   Requires 0 <= lo < hi, h and hi-lo multiples of 8, operands below 2 GiB.
+ *   ws: at least tp_vocab_ce_workspace(M, h, lo, hi) bytes. */
 tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t hi, const void* H,
-                               const void* E_i, const int32_t* targets, float* sumexp_i,
-                               float* tlogit_i, void* ws, size_t ws_bytes, void* stream);
-size_t tp_vocab_ce_workspace(int64_t M, int64_t lo, int64_t hi);
+                               const void* E_i, const int32_t* targets, float* rowmax_i,
+                               float* sumexp_i, float* tlogit_i, void* ws, size_t ws_bytes,
+                               void* stream);
+size_t tp_vocab_ce_workspace(int64_t M, int64_t h, int64_t lo, int64_t hi);
 
-/* The two all-reduce stand-ins of the vocabulary-parallel loss on one GPU, and
- * the loss itself [same page, 五、Cross-Entropy层]:
- *   S[m] = sum_i sumexp_parts[i][m] (rank order), T[m] = sum_i tlogit_parts[i][m],
- *   loss_rows[m] = log S[m] - T[m], *loss_sum = sum_m loss_rows[m] (fixed order).
- *   sumexp_parts, tlogit_parts: HOST arrays of n_parts device pointers,
- *   1 <= n_parts <= 16. loss_rows [M] and loss_sum [1]: float32 (device). */
-tp_status tp_vocab_ce_loss(int64_t M, const float* const* sumexp_parts,
-                           const float* const* tlogit_parts, int n_parts, float* loss_rows,
-                           float* loss_sum, void* stream);
+/* The all-reduce stand-ins of the vocabulary-parallel loss on one GPU, and the
+ * loss itself [same page, 五、Cross-Entropy层]:
+ *   mx[m] = max_i rowmax_parts[i][m] (a max all-reduce),
+ *   S[m] = sum_i sumexp_parts[i][m] * exp(rowmax_parts[i][m] - mx[m]) (rank order),
+ *   T[m] = sum_i tlogit_parts[i][m], loss_rows[m] = mx[m] + log S[m] - T[m],
+ *   *loss_sum = sum_m loss_rows[m] (fixed order).
+ *   rowmax_parts, sumexp_parts, tlogit_parts: HOST arrays of n_parts device
+ *   pointers, 1 <= n_parts <= 16. loss_rows [M] and loss_sum [1]: float32 (device). */
+tp_status tp_vocab_ce_loss(int64_t M, const float* const* rowmax_parts,
+                           const float* const* sumexp_parts, const float* const* tlogit_parts,
+                           int n_parts, float* loss_rows, float* loss_sum, void* stream);
 
 /* Sequence parallelism around the tensor-parallel MLP [www.discosf.com/news/5875844,
  * 2.3 序列并行与激活重计算 (LayerNorm and Dropout run on each rank's slice of the

@@ -22,7 +22,11 @@ Readings where the pages are silent or garbled:
     dK = dS^T Q / sqrt(d)); the layer's two all-reduces (forward after Wo,
     backward of the input gradient) make the rank's dX_i a partial
     [m.youleyou.com/wenzhang/3143730, 三、Self-Attention层 §3.2]. Matched mode
-    rounds dO = dOut Wo_i^T and dQKV to bfloat16, where the GPU stores them.
+    rounds dO = dOut Wo_i^T and dQKV to bfloat16, where the GPU stores them;
+  * the row term rowsum(P * dP) equals rowsum(dO * O) with O = P V exactly. A
+    training step keeps O only in its stored (bfloat16) form, so matched mode
+    forms the term from the stored O, as the backward that consumes it does;
+    the plain definition (no O given) forms rowsum(P * dP).
 """
 import numpy as np
 
@@ -100,8 +104,10 @@ def attn_shard_rows(X, Wqkv_i, Wo_i, b, s, n_heads_local, d, rows, causal=True,
     return dict(O=O, out=O @ Wo_i)
 
 
-def _head_attention_bwd(q, k, v, do, causal):
-    """Gradients of <do, softmax(q k^T / sqrt(d)) v> with respect to q, k, v."""
+def _head_attention_bwd(q, k, v, do, causal, o=None):
+    """Gradients of <do, softmax(q k^T / sqrt(d)) v> with respect to q, k, v.
+    With o (the stored head output) the row term rowsum(P * dP) is taken as
+    rowsum(do * o), its value when o = P v."""
     d = q.shape[1]
     S = (q @ k.T) / np.sqrt(d)
     if causal:
@@ -113,18 +119,21 @@ def _head_attention_bwd(q, k, v, do, causal):
     P /= P.sum(axis=1, keepdims=True)
     dV = P.T @ do
     dP = do @ v.T
-    dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+    rowterm = (P * dP).sum(axis=1, keepdims=True) if o is None else (do * o).sum(axis=1, keepdims=True)
+    dS = P * (dP - rowterm)
     return dS @ k / np.sqrt(d), dS.T @ q / np.sqrt(d), dV
 
 
-def attn_core_bwd(Q, K, V, dO, b, s, n_heads, d, causal=True):
-    """Per-sequence, per-head attention backward. All [b*s, n_heads*d]."""
+def attn_core_bwd(Q, K, V, dO, b, s, n_heads, d, causal=True, O=None):
+    """Per-sequence, per-head attention backward. All [b*s, n_heads*d]. O (optional):
+    the stored forward output, from which the row term rowsum(dO * O) is formed."""
     dQ, dK, dV = (np.empty_like(Q, dtype=np.float64) for _ in range(3))
     for bi in range(b):
         r = slice(bi * s, (bi + 1) * s)
         for j in range(n_heads):
             c = slice(j * d, (j + 1) * d)
-            dQ[r, c], dK[r, c], dV[r, c] = _head_attention_bwd(Q[r, c], K[r, c], V[r, c], dO[r, c], causal)
+            dQ[r, c], dK[r, c], dV[r, c] = _head_attention_bwd(Q[r, c], K[r, c], V[r, c], dO[r, c], causal,
+                                                               None if O is None else O[r, c])
     return dQ, dK, dV
 
 
@@ -149,6 +158,7 @@ def attn_shard_bwd(X, Wqkv_i, Wo_i, dOut, b, s, n_heads_local, d, causal=True, m
     f = attn_shard(X, Wqkv_i, Wo_i, b, s, n_heads_local, d, causal, matched)
     dWo = f["O"].T @ dOut
     dO = _r(dOut @ Wo_i.T, matched)
-    dQ, dK, dV = attn_core_bwd(f["Q"], f["K"], f["V"], dO, b, s, n_heads_local, d, causal)
+    dQ, dK, dV = attn_core_bwd(f["Q"], f["K"], f["V"], dO, b, s, n_heads_local, d, causal,
+                               O=f["O"] if matched else None)
     dQKV = _r(np.concatenate([dQ, dK, dV], axis=1), matched)
     return dict(fwd=f, dO=dO, dQKV=dQKV, dWo=dWo, dWqkv=X.T @ dQKV, dX=dQKV @ Wqkv_i.T)

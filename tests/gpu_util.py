@@ -50,6 +50,7 @@ def errors(g: np.ndarray, r: np.ndarray):
 
 def assert_bf16_close(g, r, what=""):
     rel, mae = errors(g, r)
+    note(f"{what}: normwise {rel:.3e}, mean abs {mae:.3e}")
     assert np.all(np.isfinite(g)), f"{what}: non-finite values"
     assert rel <= BF16_NORMWISE and mae <= BF16_MEAN_ABS, f"{what}: normwise {rel:.3e}, mean abs {mae:.3e}"
     return rel, mae

@@ -48,23 +48,60 @@ def _err():
 class TestValidation:
     def test_column_linear(self):
         f = lib.tp_column_linear
-        assert f(7, 4, 8, 8, P, P, None, P, 1, None) == INVALID            # dtype
-        assert f(1, 4, 8, 8, P, P, None, P, 5, None) == INVALID            # activation
-        assert f(1, 4, 8, 8, P, P, P, P, 0, None) == INVALID               # U_out without act
-        assert f(1, -1, 8, 8, P, P, None, P, 1, None) == INVALID           # M < 0
-        assert f(1, 4, 0, 8, P, P, None, P, 1, None) == INVALID            # K == 0
-        assert f(1, 4, 12, 8, P, P, None, P, 1, None) == UNSUPPORTED       # K % 8
-        assert f(1, 4, 8, 20, P, P, None, P, 1, None) == UNSUPPORTED       # N % 8
-        assert f(1, 4, 8, 8, None, P, None, P, 1, None) == INVALID         # X NULL
+        assert f(7, 4, 8, 8, P, P, None, P, 1, None, 0, None) == INVALID            # dtype
+        assert f(1, 4, 8, 8, P, P, None, P, 5, None, 0, None) == INVALID            # activation
+        assert f(1, 4, 8, 8, P, P, P, P, 0, None, 0, None) == INVALID               # U_out without act
+        assert f(1, -1, 8, 8, P, P, None, P, 1, None, 0, None) == INVALID           # M < 0
+        assert f(1, 4, 0, 8, P, P, None, P, 1, None, 0, None) == INVALID            # K == 0
+        assert f(1, 4, 12, 8, P, P, None, P, 1, None, 0, None) == UNSUPPORTED       # K % 8
+        assert f(1, 4, 8, 20, P, P, None, P, 1, None, 0, None) == UNSUPPORTED       # N % 8
+        assert f(1, 4, 8, 8, None, P, None, P, 1, None, 0, None) == INVALID         # X NULL
         assert "X is NULL" in _err()
-        assert f(1, 4, 8, 8, P, MIS, None, P, 1, None) == UNSUPPORTED      # alignment
-        assert f(1, 4, 8, 8, P, P, MIS, P, 1, None) == UNSUPPORTED
-        assert f(1, 1 << 31, 8, 8, P, P, None, P, 1, None) == UNSUPPORTED  # too large
+        assert f(1, 4, 8, 8, P, MIS, None, P, 1, None, 0, None) == UNSUPPORTED      # alignment
+        assert f(1, 4, 8, 8, P, P, MIS, P, 1, None, 0, None) == UNSUPPORTED
+        assert f(1, 1 << 31, 8, 8, P, P, None, P, 1, None, 0, None) == UNSUPPORTED  # too large
+
+    def test_linear_workspace(self):
+        # 4 x 8 x 8: one tile, a nearly empty round: the stream-K area
+        assert lib.tp_linear_workspace(1, 4, 8, 8) == SK_BYTES
+        assert lib.tp_linear_workspace(0, 4, 8, 8) == 0                      # float32: never
+        assert lib.tp_linear_workspace(1, 2048, 12288, 6144) == 0            # 256 tiles: one whole round
+        assert lib.tp_linear_workspace(1, 2048, 18432, 9216) == SK_BYTES     # 384 tiles: 1.5 rounds
+        assert lib.tp_linear_workspace(1, 4096, 18432, 9216) == 0            # 768 tiles: 3 rounds
+        f = lib.tp_column_linear
+        # a workspace is optional, but a given one must be large enough
+        assert f(1, 4, 8, 8, P, P, None, P, 1, P, SK_BYTES - 1, None) == WORKSPACE
+        assert "workspace" in _err()
+        assert f(1, 4, 8, 8, P, P, None, P, 1, MIS, SK_BYTES, None) == UNSUPPORTED
+        r = lib.tp_row_linear
+        assert r(1, 4, 8, 8, P, P, P, P, SK_BYTES - 256, None) == WORKSPACE
+        assert lib.tp_mlp_fwd_workspace(1, 2048, 12288, 6144) == 0
+        assert lib.tp_mlp_fwd_workspace(1, 2048, 18432, 9216) == SK_BYTES
+        assert lib.tp_mlp_fwd_workspace(0, 8, 64, 64) == 0
+        m = lib.tp_mlp_fwd
+        assert m(1, 4, 16, 24, P, P, P, None, P, P, P, SK_BYTES - 1, None) == WORKSPACE
+
+    def test_operands_of_two_gib_are_rejected_before_any_launch(self):
+        # [131072, 8192] bf16 is exactly 2 GiB: the kernels address operands with 32-bit offsets
+        M, K, N = 131072, 8192, 8192
+        assert lib.tp_column_linear(1, M, K, N, P, P, None, P, 1, None, 0, None) == UNSUPPORTED
+        assert "2 GiB" in _err() and "X" in _err()
+        assert lib.tp_row_linear(1, 1024, 8, 1 << 27, P, P, P, None, 0, None) == UNSUPPORTED
+        assert "W" in _err()
+        assert lib.tp_mlp_fwd(1, 16, 1 << 26, 16, P, P, P, None, P, P, None, 0, None) == UNSUPPORTED
+        b = lib.tp_mlp_bwd
+        need = lib.tp_mlp_bwd_workspace(M, K, 64)
+        assert b(M, K, 64, P, P, P, P, P, P, P, P, P, P, need, None) == UNSUPPORTED
+        need = lib.tp_attn_fwd_workspace(1, M, K, 2, 64, )
+        assert lib.tp_attn_fwd(1, M, K, 2, 64, 1, P, P, P, P, P, need, None) == UNSUPPORTED
+        need = lib.tp_vocab_ce_workspace(16, 8192, 0, 1 << 17)
+        assert lib.tp_vocab_ce_partials(16, 8192, 0, 1 << 17, P, P, P, P, P, P, P, need, None) == UNSUPPORTED
+        assert "E_i" in _err()
 
     def test_row_linear_and_mlp_fwd(self):
-        assert lib.tp_row_linear(1, 4, 8, 8, P, P, None, None) == INVALID
-        assert lib.tp_mlp_fwd(1, 4, 16, 24, P, P, P, None, None, P, None) == INVALID  # Y_i NULL
-        assert lib.tp_mlp_fwd(1, 4, 16, 20, P, P, P, None, P, P, None) == UNSUPPORTED
+        assert lib.tp_row_linear(1, 4, 8, 8, P, P, None, None, 0, None) == INVALID
+        assert lib.tp_mlp_fwd(1, 4, 16, 24, P, P, P, None, None, P, None, 0, None) == INVALID  # Y_i NULL
+        assert lib.tp_mlp_fwd(1, 4, 16, 20, P, P, P, None, P, P, None, 0, None) == UNSUPPORTED
 
     def test_mlp_bwd(self):
         M, h, f = 32, 64, 128
@@ -91,9 +128,12 @@ class TestValidation:
         assert lib.tp_attn_core(1, 16, 2, 96, 1, P, P, None) == UNSUPPORTED  # d_head
         assert lib.tp_attn_core(1, 16, 0, 128, 1, P, P, None) == INVALID
         assert lib.tp_attn_core(-1, 16, 2, 128, 1, P, P, None) == INVALID
-        ws = lib.tp_attn_fwd_workspace(2, 100, 3, 64)
+        ws = lib.tp_attn_fwd_workspace(2, 100, 256, 3, 64)
         assert ws == (2 * 100 * 9 * 64 * 2 + 2 * 100 * 3 * 64 * 2 + (-(2 * 100 * 9 * 64 * 2) % 256)
                       + (-(2 * 100 * 3 * 64 * 2) % 256) + SK_BYTES)
+        # the GPT-3 shard's QKV (192 tiles) and Wo (512 tiles) products use no stream-K area
+        t, w = 2048, 12 * 128
+        assert lib.tp_attn_fwd_workspace(1, 2048, 12288, 12, 128) == t * 3 * w * 2 + t * w * 2
         assert lib.tp_attn_fwd(2, 100, 256, 3, 64, 1, P, P, P, P, P, ws - 16, None) == WORKSPACE
         assert lib.tp_attn_fwd(2, 100, 260, 3, 64, 1, P, P, P, P, P, ws, None) == UNSUPPORTED  # h % 8
 
@@ -133,36 +173,43 @@ class TestValidation:
 
     def test_vocab_ce(self):
         M, h, lo, hi = 16, 64, 40, 104
-        need = lib.tp_vocab_ce_workspace(M, lo, hi)
+        need = lib.tp_vocab_ce_workspace(M, h, lo, hi)
         assert need == M * (hi - lo) * 4 + SK_BYTES and need % 256 == 0
-        assert lib.tp_vocab_ce_workspace(3, 0, 8) == 256 + SK_BYTES
-        assert lib.tp_vocab_ce_workspace(2048, 0, 6144) == 2048 * 6144 * 4  # 256 tiles: no area
-        assert lib.tp_vocab_ce_workspace(2048, 0, 6288) == 2048 * 6288 * 4 + SK_BYTES  # 264 tiles
-        assert lib.tp_vocab_ce_workspace(3, 8, 8) == 0
+        assert lib.tp_vocab_ce_workspace(3, 64, 0, 8) == 256 + SK_BYTES
+        assert lib.tp_vocab_ce_workspace(2048, 12288, 0, 6144) == 2048 * 6144 * 4  # 256 tiles: no area
+        assert lib.tp_vocab_ce_workspace(2048, 12288, 0, 6288) == 2048 * 6288 * 4 + SK_BYTES  # 264 tiles
+        assert lib.tp_vocab_ce_workspace(3, 64, 8, 8) == 0
+        assert lib.tp_vocab_ce_workspace(3, 0, 0, 8) == 0
         c = lib.tp_vocab_ce_partials
-        assert c(M, h, 10, 10, P, P, P, P, P, P, need, None) == INVALID          # lo == hi
-        assert c(M, h, -8, 8, P, P, P, P, P, P, need, None) == INVALID          # lo < 0
-        assert c(-1, h, lo, hi, P, P, P, P, P, P, need, None) == INVALID
-        assert c(M, h, 0, 12, P, P, P, P, P, P, need, None) == UNSUPPORTED      # slice % 8
-        assert c(M, 20, lo, hi, P, P, P, P, P, P, need, None) == UNSUPPORTED    # h % 8
-        assert c(M, h, lo, hi, P, P, None, P, P, P, need, None) == INVALID      # targets NULL
-        assert c(M, h, lo, hi, None, P, P, P, P, P, need, None) == INVALID
-        assert c(M, h, lo, hi, P, MIS, P, P, P, P, need, None) == UNSUPPORTED
-        assert c(M, h, lo, hi, P, P, P, P, P, P, need - 1, None) == WORKSPACE
-        assert c(M, h, lo, hi, P, P, P, P, P, None, need, None) == WORKSPACE
+        a7 = [P] * 7  # H, E_i, targets, rowmax_i, sumexp_i, tlogit_i, ws
+        assert c(M, h, 10, 10, *a7, need, None) == INVALID          # lo == hi
+        assert c(M, h, -8, 8, *a7, need, None) == INVALID          # lo < 0
+        assert c(-1, h, lo, hi, *a7, need, None) == INVALID
+        assert c(M, h, 0, 12, *a7, need, None) == UNSUPPORTED      # slice % 8
+        assert c(M, 20, lo, hi, *a7, need, None) == UNSUPPORTED    # h % 8
+        assert c(M, h, lo, hi, P, P, None, P, P, P, P, need, None) == INVALID      # targets NULL
+        assert c(M, h, lo, hi, None, P, P, P, P, P, P, need, None) == INVALID
+        assert c(M, h, lo, hi, P, MIS, P, P, P, P, P, need, None) == UNSUPPORTED
+        assert c(M, h, lo, hi, P, P, P, None, P, P, P, need, None) == INVALID      # rowmax_i NULL
+        assert "rowmax_i" in _err()
+        assert c(M, h, lo, hi, *a7, need - 1, None) == WORKSPACE
+        assert c(M, h, lo, hi, P, P, P, P, P, P, None, need, None) == WORKSPACE
         assert "workspace" in _err()
-        assert c(0, h, lo, hi, None, None, None, None, None, None, 0, None) == OK  # empty
+        assert c(0, h, lo, hi, None, None, None, None, None, None, None, 0, None) == OK  # empty
         arr = (C.c_void_p * 17)(*([P] * 17))
         loss = lib.tp_vocab_ce_loss
-        assert loss(M, arr, arr, 0, P, P, None) == INVALID
-        assert loss(M, arr, arr, 17, P, P, None) == INVALID
-        assert loss(-1, arr, arr, 2, P, P, None) == INVALID
-        assert loss(M, None, arr, 2, P, P, None) == INVALID
-        assert loss(M, arr, arr, 2, P, None, None) == INVALID                 # loss_sum NULL
-        assert loss(M, arr, arr, 2, None, P, None) == INVALID                 # loss_rows NULL
+        assert loss(M, arr, arr, arr, 0, P, P, None) == INVALID
+        assert loss(M, arr, arr, arr, 17, P, P, None) == INVALID
+        assert loss(-1, arr, arr, arr, 2, P, P, None) == INVALID
+        assert loss(M, None, arr, arr, 2, P, P, None) == INVALID
+        assert loss(M, arr, None, arr, 2, P, P, None) == INVALID
+        assert loss(M, arr, arr, arr, 2, P, None, None) == INVALID                 # loss_sum NULL
+        assert loss(M, arr, arr, arr, 2, None, P, None) == INVALID                 # loss_rows NULL
         bad = (C.c_void_p * 2)(P, None)
-        assert loss(M, arr, bad, 2, P, P, None) == INVALID
+        assert loss(M, arr, arr, bad, 2, P, P, None) == INVALID
         assert "tlogit_parts" in _err()
+        assert loss(M, bad, arr, arr, 2, P, P, None) == INVALID
+        assert "rowmax_parts" in _err()
 
     def test_sequence_parallel(self):
         ln = lib.tp_layernorm

@@ -56,7 +56,7 @@ def test_attn_fwd_ragged(b, s, h, Hl, d):
     note(f"attn_fwd b={b} s={s} h={h} Hl={Hl} d={d}")
     ai = attn_inputs(b, s, h, Hl, d, 80 + s, 1.0, 0.05)
     out = torch.empty(b * s, h, dtype=torch.float32, device=DEV)
-    ws = torch.empty(tp.attn_fwd_workspace(b, s, Hl, d), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(tp.attn_fwd_workspace(b, s, Hl, d, h=h), dtype=torch.uint8, device=DEV)
     tp.attn_fwd(*(bf16_dev(ai[k]) for k in ("X", "Wqkv", "Wo")), out, ws, b, s, Hl, d, True)
     torch.cuda.synchronize()
     r = oracle.attn_shard(*(bf16_bits_to_f64(ai[k]) for k in ("X", "Wqkv", "Wo")), b, s, Hl, d)
@@ -77,7 +77,7 @@ def test_gpt3_attn_shard_full_size_sampled_rows():
     ai = attn_inputs(b, s, h, Hl, d, c["seed"], c["sigma_x"], c["sigma_w"])
     note("attn_fwd GPT-3 shard full size")
     out = torch.empty(b * s, h, dtype=torch.float32, device=DEV)
-    ws = torch.empty(tp.attn_fwd_workspace(b, s, Hl, d), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(tp.attn_fwd_workspace(b, s, Hl, d, h=h), dtype=torch.uint8, device=DEV)
     tp.attn_fwd(*(bf16_dev(ai[k]) for k in ("X", "Wqkv", "Wo")), out, ws, b, s, Hl, d, True)
     torch.cuda.synchronize()
     assert torch.isfinite(out).all()
@@ -88,3 +88,28 @@ def test_gpt3_attn_shard_full_size_sampled_rows():
     o_off = (b * s * 3 * w * 2 + 255) // 256 * 256
     O = ws[o_off: o_off + b * s * w * 2].view(torch.bfloat16).view(b * s, w)
     assert_bf16_close(f64_host(O[torch.from_numpy(rows).to(DEV)]), r["O"], "O rows")
+
+
+def test_gpt3_attn_shard_full_size_every_element():
+    """The call the benchmark times (tp_attn_fwd at the GPT-3 shard, 12 local heads
+    of 128, s = 2048, h = 12288): every element of Q, K, V, O and out_partial
+    against the float64 oracle in matched mode."""
+    c = CONFIGS["gpt3_attn_rank_shard"]
+    b, s, h, d = c["b"], c["s"], c["h"], c["d_head"]
+    Hl = c["n_heads"] // c["N"]
+    ai = attn_inputs(b, s, h, Hl, d, c["seed"], c["sigma_x"], c["sigma_w"])
+    note("attn_fwd GPT-3 shard full size, every element")
+    out = torch.full((b * s, h), float("nan"), dtype=torch.float32, device=DEV)
+    ws = torch.empty(tp.attn_fwd_workspace(b, s, Hl, d, h=h), dtype=torch.uint8, device=DEV)
+    tp.attn_fwd(*(bf16_dev(ai[k]) for k in ("X", "Wqkv", "Wo")), out, ws, b, s, Hl, d, True)
+    torch.cuda.synchronize()
+    r = oracle.attn_shard(*(bf16_bits_to_f64(ai[k]) for k in ("X", "Wqkv", "Wo")), b, s, Hl, d)
+    w = Hl * d
+    qkv = f64_host(ws[: b * s * 3 * w * 2].view(torch.bfloat16).view(b * s, 3 * w))
+    assert_bf16_close(qkv[:, :w], r["Q"], "Q (all elements)")
+    assert_bf16_close(qkv[:, w:2 * w], r["K"], "K (all elements)")
+    assert_bf16_close(qkv[:, 2 * w:], r["V"], "V (all elements)")
+    o_off = (b * s * 3 * w * 2 + 255) // 256 * 256
+    O = ws[o_off: o_off + b * s * w * 2].view(torch.bfloat16).view(b * s, w)
+    assert_bf16_close(f64_host(O), r["O"], "O (all elements)")
+    assert_bf16_close(f64_host(out), r["out"], "out_partial (all elements)")

@@ -1,14 +1,14 @@
 """GPU parity of the attention backward (core and whole shard) against the
 float64 oracle, through the C ABI.
 
-Tolerance: the GPU feeds P and dS to the MFMAs as bf16 and forms rowsum(dO * O)
-from the bf16-stored O, so its gradients carry relative errors of the order of
-bf16's 2^-8 per product term. The bounds are normwise max|g - r| / max|r| <= 2e-2
-and mean|g - r| <= 5e-3 mean|r| (scales floored at 1e-2 and 1e-3, so a gradient
-that is exactly zero, as dQ with a single visible key, is held to those absolute
-bounds), against the oracle in matched mode (bf16 storage
-of Q, K, V, O, dO and dQKV where the GPU stores them). The log-sum-exp is float32
-throughout: |g - r| <= 1e-4.
+Tolerance: the bf16 bar of every other product, normwise max|g - r| / max|r|
+<= 2e-2 and mean|g - r| <= 1e-3, against the oracle in matched mode (bf16
+storage of Q, K, V, O, dO and dQKV where the GPU stores them). The kernels feed
+P and dS to the MFMAs as hi/lo bf16 pairs (and the training forward feeds P to
+P V that way), so the stored bf16 values round as the exact ones do in all but
+a small fraction of entries; the weight gradients dWo = O^T dOut and
+dWqkv = X^T dQKV, sums over every token, then stay within the bar. The
+log-sum-exp is float32 throughout: |g - r| <= 1e-4.
 """
 import numpy as np
 import pytest
@@ -16,24 +16,16 @@ import torch
 
 import oracle
 from oracle.bf16 import bf16_bits_to_f64
-from tests.gpu_util import DEV, bf16_dev, f64_host, note
+from tests.gpu_util import DEV, assert_bf16_close, bf16_dev, f64_host, note
 from workloads import CONFIGS, attn_inputs, bf16_bits, draw_normal_f32
 
 pytestmark = pytest.mark.gpu
 
 tp = pytest.importorskip("attention_shard_math_amd")
 
-NORMWISE = 2e-2
-MEAN_REL = 5e-3
-
 
 def assert_grad_close(g, r, what):
-    g, r = np.asarray(g, np.float64), np.asarray(r, np.float64)
-    assert np.all(np.isfinite(g)), f"{what}: non-finite values"
-    d = np.abs(g - r)
-    nw = d.max() / max(np.abs(r).max(), 1e-2)
-    mr = d.mean() / max(np.abs(r).mean(), 1e-3)
-    assert nw <= NORMWISE and mr <= MEAN_REL, f"{what}: normwise {nw:.3e}, mean relative {mr:.3e}"
+    assert_bf16_close(g, r, what)
 
 
 def _core_case(b, s, Hl, d, causal, seed):
@@ -99,10 +91,13 @@ def _shard_case(b, s, h, Hl, d, ai, dOut_bits, causal=True):
     return out, dX, dWqkv, dWo, ws
 
 
+# Small and ragged shards drawn with the GPT-3 shard's activation statistics: the
+# weights' sigma is 0.006 * sqrt(12288 / h), so that Q, K, V, O and the gradients
+# have the scale they have at h = 12288 (the mean-abs bar is absolute).
 @pytest.mark.parametrize("b,s,h,Hl,d", [(2, 300, 512, 2, 128), (1, 150, 256, 4, 64)])
 def test_shard_backward(b, s, h, Hl, d):
     note(f"attn_fwd_train + attn_bwd b={b} s={s} h={h} Hl={Hl} d={d}")
-    ai = attn_inputs(b, s, h, Hl, d, 180 + s, 1.0, 0.05)
+    ai = attn_inputs(b, s, h, Hl, d, 180 + s, 1.0, 0.006 * np.sqrt(12288 / h))
     dOut = bf16_bits(draw_normal_f32(np.random.default_rng(181 + s), (b * s, h), 1.0))
     out, dX, dWqkv, dWo, ws = _shard_case(b, s, h, Hl, d, ai, dOut)
     torch.cuda.synchronize()

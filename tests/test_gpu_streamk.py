@@ -20,10 +20,11 @@ def _logits_streamk(H, E, lo, hi):
     M = H.shape[0]
     V = hi - lo
     tgt = torch.zeros(M, dtype=torch.int32, device=DEV)
+    mx = torch.empty(M, dtype=torch.float32, device=DEV)
     se = torch.empty(M, dtype=torch.float32, device=DEV)
     tl = torch.empty(M, dtype=torch.float32, device=DEV)
-    ws = torch.empty(tp.vocab_ce_workspace(M, lo, hi), dtype=torch.uint8, device=DEV)
-    tp.vocab_ce_partials(H, E, tgt, lo, hi, se, tl, ws)
+    ws = torch.empty(tp.vocab_ce_workspace(M, H.shape[1], lo, hi), dtype=torch.uint8, device=DEV)
+    tp.vocab_ce_partials(H, E, tgt, lo, hi, mx, se, tl, ws)
     torch.cuda.synchronize()
     return ws[: M * V * 4].view(torch.float32).view(M, V).clone()
 

@@ -614,6 +614,22 @@ class TestAttentionBackward:
         # lse of the first query is its own scaled score
         np.testing.assert_allclose(lse[0], Q[0] @ K[0] / np.sqrt(d), rtol=1e-12)
 
+    @pytest.mark.parametrize("causal", [True, False])
+    def test_row_term_from_the_output(self, causal):
+        """rowsum(P * dP) = rowsum(dO * O) for O = P V: given the exact O, the
+        stored-output form of the backward reproduces the definition; given a
+        perturbed O, dV is unchanged and dQ, dK move."""
+        b, s, H, d = 2, 7, 2, 8
+        Q, K, V, dO = self._qkv(65, b, s, H, d)
+        O = oracle.attn_core(Q, K, V, b, s, H, d, causal)
+        ref = oracle.attn_core_bwd(Q, K, V, dO, b, s, H, d, causal)
+        via_o = oracle.attn_core_bwd(Q, K, V, dO, b, s, H, d, causal, O=O)
+        for g, r in zip(via_o, ref):
+            np.testing.assert_allclose(g, r, rtol=1e-11, atol=1e-13)
+        moved = oracle.attn_core_bwd(Q, K, V, dO, b, s, H, d, causal, O=O + 1e-3)
+        np.testing.assert_array_equal(moved[2], ref[2])
+        assert np.abs(moved[0] - ref[0]).max() > 1e-6 and np.abs(moved[1] - ref[1]).max() > 1e-6
+
     def test_shards_sum_to_full_mha_backward(self):
         rng = np.random.default_rng(64)
         b, s, Hh, d, N = 1, 6, 4, 4, 2
