@@ -18,6 +18,8 @@ from ._lib import (  # noqa: F401
     mlp_bwd,
     mlp_bwd_workspace,
     mlp_bwd_recompute_workspace,
+    mlp_bwd_noalloc,
+    mlp_bwd_noalloc_max_bytes,
     attn_core,
     attn_fwd,
     attn_fwd_workspace,

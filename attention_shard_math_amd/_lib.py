@@ -26,6 +26,7 @@ _SIGS = {
     "tp_row_linear": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_mlp_fwd": [C.c_int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_mlp_bwd": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
+    "tp_mlp_bwd_noalloc": [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp],
     "tp_attn_core": [_i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp],
     "tp_attn_fwd": [_i64, _i64, _i64, _i64, _i64, C.c_int, _vp, _vp, _vp, _vp, _vp, _sz, _vp],
     "tp_vocab_embed": [_vp, _i64, _vp, _i64, _i64, _i64, _vp, _vp],
@@ -65,6 +66,8 @@ lib.tp_linear_workspace.argtypes = [C.c_int, _i64, _i64, _i64]
 lib.tp_linear_workspace.restype = _sz
 lib.tp_mlp_fwd_workspace.argtypes = [C.c_int, _i64, _i64, _i64]
 lib.tp_mlp_fwd_workspace.restype = _sz
+lib.tp_mlp_bwd_noalloc_max_bytes.argtypes = []
+lib.tp_mlp_bwd_noalloc_max_bytes.restype = _sz
 lib.tp_status_string.argtypes = [C.c_int]
 lib.tp_status_string.restype = C.c_char_p
 lib.tp_last_error.argtypes = []
@@ -351,3 +354,18 @@ def shard_sum(partials, out, stream=None):
             raise ValueError(f"partials[{i}] has {p.numel()} elements, out has {numel}")
     _check(lib.tp_shard_sum(_dt(out), arr, n, numel, _ptr(out, name="out"), _stream(stream)), "tp_shard_sum")
 
+
+def mlp_bwd_noalloc_max_bytes() -> int:
+    return int(lib.tp_mlp_bwd_noalloc_max_bytes())
+
+
+def mlp_bwd_noalloc(X, A_i, B_i, U_i, Y_i, dZ, dX_i, dA_i, dB_i, stream=None):
+    """tp_mlp_bwd without a workspace: dU lives in the library's per-device scratch."""
+    M, h = X.shape
+    f = A_i.shape[1]
+    bf, f32 = torch.bfloat16, torch.float32
+    _check(lib.tp_mlp_bwd_noalloc(M, h, f, _ptr(X, (M, h), bf, "X"), _ptr(A_i, (h, f), bf, "A_i"),
+                                  _ptr(B_i, (f, h), bf, "B_i"), _ptr(U_i, (M, f), bf, "U_i"),
+                                  _ptr(Y_i, (M, f), bf, "Y_i"), _ptr(dZ, (M, h), bf, "dZ"),
+                                  _ptr(dX_i, (M, h), f32, "dX_i"), _ptr(dA_i, (h, f), f32, "dA_i"),
+                                  _ptr(dB_i, (f, h), f32, "dB_i"), _stream(stream)), "tp_mlp_bwd_noalloc")

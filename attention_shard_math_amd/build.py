@@ -19,7 +19,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtpshard.so")
 
-SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_f32.hip", "bandwidth.hip", "attn.hip", "attn_bwd.hip", "vocab_ce.hip", "seqpar.hip"]
+SOURCES = ["api.cpp", "gemm_bf16.hip", "gemm_f32.hip", "bandwidth.hip", "attn.hip", "attn_bwd.hip", "vocab_ce.hip",
+           "seqpar.hip", "noalloc.hip"]
 ARCH = "gfx950"
 CFLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Wall",

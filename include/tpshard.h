@@ -153,6 +153,26 @@ size_t tp_mlp_bwd_workspace(int64_t M, int64_t h, int64_t f);
 /* Workspace of tp_mlp_bwd when U_i or Y_i is NULL: dU_i, U_i and Y_i, bf16 [M, f] each. */
 size_t tp_mlp_bwd_recompute_workspace(int64_t M, int64_t h, int64_t f);
 
+/* Allocation-free MLP backward, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, products and results as tp_mlp_bwd with U_i and
+ * Y_i given, but no workspace: dU_i lives in a scratch array of the library,
+ * tp_mlp_bwd_noalloc_max_bytes() bytes (80 MiB) per device, held from the
+ * library's first use on a device until the process ends. Nothing in it needs
+ * clearing between calls; every call on one device shares it, so calls that
+ * overlap in time on one device race. The products run one tile per workgroup
+ * (no stream-K split), so results can differ from tp_mlp_bwd's by float32
+ * summation order.
+ *   M * f * 2 bytes above the scratch size -> TP_ERR_UNSUPPORTED; U_i or Y_i
+ *   NULL (activation recompute would need more scratch) -> TP_ERR_INVALID_ARG;
+ *   other arguments as tp_mlp_bwd. No hipMalloc, hipFree or allocating library
+ *   call is made; the first call on a device looks up the scratch's address. */
+tp_status tp_mlp_bwd_noalloc(int64_t M, int64_t h, int64_t f,
+                             const void* X, const void* A_i, const void* B_i,
+                             const void* U_i, const void* Y_i, const void* dZ,
+                             float* dX_i, float* dA_i, float* dB_i, void* stream);
+size_t tp_mlp_bwd_noalloc_max_bytes(void);
+
 /* Causal (or full) softmax attention over one rank's local heads, bf16.
  * [Megatron-LM：张量并行与大规模训练, §2.2; m.youleyou.com/wenzhang/3143730,
  *  三、Self-Attention层 §3.1.]

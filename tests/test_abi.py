@@ -124,6 +124,18 @@ class TestValidation:
         assert "workspace" in _err()
         assert b(M, h, f, P, P, P, P, P, None, P, P, P, P, need, None) == INVALID      # dZ NULL
 
+    def test_mlp_bwd_noalloc(self):
+        cap = lib.tp_mlp_bwd_noalloc_max_bytes()
+        assert cap == 80 << 20
+        n = lib.tp_mlp_bwd_noalloc
+        f = 8192
+        M = cap // (2 * f) + 1  # dU one row past the scratch
+        assert n(M, 64, f, P, P, P, P, P, P, P, P, P, None) == UNSUPPORTED
+        assert "scratch" in _err()
+        assert n(64, 64, 128, P, P, P, None, P, P, P, P, P, None) == INVALID     # U_i NULL: no recompute
+        assert n(64, 64, 128, P, P, P, P, P, None, P, P, P, None) == INVALID     # dZ NULL
+        assert n(64, 64, 124, P, P, P, P, P, P, P, P, P, None) == UNSUPPORTED    # f % 8
+
     def test_attention(self):
         assert lib.tp_attn_core(1, 16, 2, 96, 1, P, P, None) == UNSUPPORTED  # d_head
         assert lib.tp_attn_core(1, 16, 0, 128, 1, P, P, None) == INVALID
