@@ -55,7 +55,7 @@ lib.tp_mlp_bwd_recompute_workspace.restype = _sz
 lib.tp_vocab_ce_workspace.argtypes = [_i64, _i64, _i64, _i64]
 lib.tp_layernorm_bwd_workspace.argtypes = [_i64, _i64]
 lib.tp_layernorm_bwd_workspace.restype = _sz
-lib.tp_attn_core_bwd_workspace.argtypes = [_i64, _i64, _i64]
+lib.tp_attn_core_bwd_workspace.argtypes = [_i64, _i64, _i64, _i64]
 lib.tp_attn_core_bwd_workspace.restype = _sz
 lib.tp_attn_bwd_workspace.argtypes = [_i64, _i64, _i64, _i64, _i64]
 lib.tp_attn_bwd_workspace.restype = _sz
@@ -231,8 +231,8 @@ def attn_fwd_train(X, Wqkv_i, Wo_i, out_partial, QKV, O, lse, b, s, n_heads_loca
            "tp_attn_fwd_train")
 
 
-def attn_core_bwd_workspace(b, s, n_heads_local):
-    return int(lib.tp_attn_core_bwd_workspace(b, s, n_heads_local))
+def attn_core_bwd_workspace(b, s, n_heads_local, d_head):
+    return int(lib.tp_attn_core_bwd_workspace(b, s, n_heads_local, d_head))
 
 
 def attn_core_bwd(QKV, O, dO, lse, dQKV, ws, b, s, n_heads_local, d_head, causal=True, stream=None):

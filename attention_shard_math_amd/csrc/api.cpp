@@ -345,7 +345,8 @@ namespace {
 tp_status check_attn_shape(const char* fn, int64_t b, int64_t s, int64_t Hl, int64_t d) {
   if (b < 0 || s < 0 || Hl <= 0 || d <= 0)
     return fail(TP_ERR_INVALID_ARG, "%s: need b >= 0, s >= 0, n_heads_local > 0, d_head > 0", fn);
-  if (d != 64 && d != 128) return fail(TP_ERR_UNSUPPORTED, "%s: d_head must be 64 or 128 (got %lld)", fn, (long long)d);
+  if (d != 64 && d != 128 && d != 384)
+    return fail(TP_ERR_UNSUPPORTED, "%s: d_head must be 64, 128 or 384 (got %lld)", fn, (long long)d);
   if (b * s > kMaxDim || 3 * Hl * d > kMaxDim || b * Hl * ((s + 127) / 128) > kMaxDim)
     return fail(TP_ERR_UNSUPPORTED, "%s: problem too large", fn);
   // The kernel addresses one sequence's K and V rows with 32-bit byte offsets.
@@ -468,11 +469,23 @@ TP_API tp_status tp_attn_fwd_train(int64_t b, int64_t s, int64_t h, int64_t n_he
   return ok();
 }
 
-TP_API size_t tp_attn_core_bwd_workspace(int64_t b, int64_t s, int64_t n_heads_local) {
+namespace {
+// The backward of 384-wide heads runs per-head products whose [2s, s] operands
+// are read 16 bytes at a time: s must be a multiple of 8, and 4 s^2 bytes below 2 GiB.
+tp_status check_wide_bwd(const char* fn, int64_t s, int64_t d) {
+  if (d == 384 && (s % 8 != 0 || 4 * s * s >= ((int64_t)1 << 31) - 16))
+    return fail(TP_ERR_UNSUPPORTED, "%s: with d_head 384 the backward needs s %% 8 == 0 and s <= 23170 (got s=%lld)",
+                fn, (long long)s);
+  return TP_OK;
+}
+}  // namespace
+
+TP_API size_t tp_attn_core_bwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head) {
   if (b <= 0 || s <= 0 || n_heads_local <= 0) return 0;
   if (b * s > kMaxDim || n_heads_local > kMaxDim) return 0;
-  // sized for the largest head dimension (128), so one figure serves both
-  return tps::attn_bwd_workspace((int)b, (int)s, (int)n_heads_local, 128);
+  if (d_head != 64 && d_head != 128 && d_head != 384) return 0;
+  // the 64- and 128-wide kernels share one layout, sized for 128
+  return tps::attn_bwd_workspace((int)b, (int)s, (int)n_heads_local, d_head == 384 ? 384 : 128);
 }
 
 TP_API tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
@@ -480,13 +493,14 @@ TP_API tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, i
                                   void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "tp_attn_core_bwd";
   TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  TRY(check_wide_bwd(fn, s, d_head));
   if (b * s == 0) return ok();
   TRY(check_ptr(fn, "QKV", QKV));
   TRY(check_ptr(fn, "O", O));
   TRY(check_ptr(fn, "dO", dO));
   TRY(check_ptr(fn, "lse", lse));
   TRY(check_ptr(fn, "dQKV", dQKV));
-  const size_t need = tp_attn_core_bwd_workspace(b, s, n_heads_local);
+  const size_t need = tp_attn_core_bwd_workspace(b, s, n_heads_local, d_head);
   if (!ws || ws_bytes < need)
     return fail(TP_ERR_WORKSPACE, "%s: workspace of %zu bytes required, got %zu%s", fn, need, ws_bytes,
                 ws ? "" : " (NULL)");
@@ -508,7 +522,8 @@ size_t attn_bwd_sk(int64_t M, int64_t h, int64_t w) {
 TP_API size_t tp_attn_bwd_workspace(int64_t b, int64_t s, int64_t h, int64_t n_heads_local, int64_t d_head) {
   if (b < 0 || s < 0 || n_heads_local < 0 || d_head < 0) return 0;
   const size_t t = (size_t)b * (size_t)s, w = (size_t)n_heads_local * (size_t)d_head;
-  return round256(t * w * 2) + round256(t * 3 * w * 2) + round256(tp_attn_core_bwd_workspace(b, s, n_heads_local)) +
+  return round256(t * w * 2) + round256(t * 3 * w * 2) +
+         round256(tp_attn_core_bwd_workspace(b, s, n_heads_local, d_head)) +
          attn_bwd_sk(b * s, h, n_heads_local * d_head);
 }
 
@@ -518,6 +533,7 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
                              size_t ws_bytes, void* stream) {
   const char* fn = "tp_attn_bwd";
   TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
+  TRY(check_wide_bwd(fn, s, d_head));
   TRY(check_dims(fn, b * s, h, 3 * n_heads_local * d_head));
   TRY(check_ptr(fn, "dWqkv_i", dWqkv_i));
   TRY(check_ptr(fn, "dWo_i", dWo_i));
@@ -544,7 +560,7 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   uint16_t* dO = reinterpret_cast<uint16_t*>(wsb);
   uint16_t* dqkv = reinterpret_cast<uint16_t*>(wsb + round256((size_t)M * w * 2));
   void* core_ws = wsb + round256((size_t)M * w * 2) + round256((size_t)M * 3 * w * 2);
-  void* sk = static_cast<char*>(core_ws) + round256(tp_attn_core_bwd_workspace(b, s, n_heads_local));
+  void* sk = static_cast<char*>(core_ws) + round256(tp_attn_core_bwd_workspace(b, s, n_heads_local, d_head));
   {  // dWo_i = O^T dOut: A(m,k) = O[k, m], B(k,n) = dOut[k, n]
     tps::GemmArgs g = make_args(O, w, dOut, h, w, h, M, dWo_i, h);
     tps::gemm_bf16_sk_attach(g, sk);

@@ -327,6 +327,240 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
   }
 }
 
+// ---------------------------------------------------------------- wide heads
+// Heads of d = 384 (h = 18432 over 48 heads): three LDS slots of a 64-key stage
+// would take 288 KB, and a compute wave cannot hold a 384-wide O^T next to its
+// Q^T fragments. So the output is split into chunks of WDC = 128 columns: one
+// workgroup per (sequence, head, 128-query block, d-chunk). Each forms the full
+// scores S^T = K Q^T over all 384 d (the K stage is [64 keys][384]) and only
+// its chunk's O^T = V_c^T P^T, so S is formed once per chunk (three times per
+// query block). Two LDS slots of 64 KB (K stage + the chunk's V^T stage), one
+// barrier per stage; during stage i the loaders write stage i + 1 and fetch
+// stage i + 2. The three chunks of one query block are adjacent items on one XCD,
+// so their K and V stages are read from one L2. Softmax, masking, the exponent
+// reference and the hi/lo split of P are as in attn_fwd_kernel.
+constexpr int WD = 384, WDC = 128, WNC = WD / WDC;
+
+template <bool CAUSAL, bool SPLIT>
+__global__ __launch_bounds__(NT) void attn_fwd_wide_kernel(const uint16_t* __restrict__ qkv, uint16_t* __restrict__ O,
+                                                           int s, int Hl, int nqb, int per_xcd, int n_items,
+                                                           float scale_log2, float* __restrict__ lse) {
+  constexpr int D = WD, DC = WDC;
+  constexpr int DCH = D / 8;                 // 16-byte chunks per K row (48)
+  constexpr int KS = D / 16;                 // k-steps of S^T over d (24)
+  constexpr int DT = DC / 32;                // O^T tiles of the chunk (4)
+  constexpr int KPER = KVB * DCH / NP;       // K chunks each loader thread stages (12)
+  constexpr int NVT = (KVB / 8) * (DC / 4);  // V tasks of 8 keys x 4 d (256)
+  constexpr int SKK = KVB * D;               // elements of a K stage
+  constexpr int SVV = KVB * DC;              // elements of a V^T chunk stage
+  static_assert(KPER * NP == KVB * DCH && NVT == NP, "stage shape");
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (SKK + SVV)];  // [slot][K | V^T], stage i in slot i % 2
+
+  const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if (item >= n_items) return;
+  const int per_bh = nqb * WNC;
+  const int bh = item / per_bh, rem = item % per_bh;
+  const int qb = nqb - 1 - rem / WNC, dc = rem % WNC;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  const int bi = bh / Hl, head = bh % Hl;
+  const int64_t ld = 3LL * Hl * D;
+  const uint16_t* Qg = qkv + (int64_t)bi * s * ld + (int64_t)head * D;
+  const int q0 = qb * AQ;
+  const int kv_end = CAUSAL ? min(s, q0 + AQ) : s;
+  const int nkv = (kv_end + KVB - 1) / KVB;
+
+  if (wave >= 4) {
+    // ---------------- loader waves ----------------
+    const int ptid = tid - (NT - NP);
+    const int seq_bytes = (s - 1) * (int)ld * 2 + D * 2;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + (int64_t)Hl * D), (short)0, seq_bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + 2LL * Hl * D + dc * DC), (short)0, seq_bytes - dc * DC * 2,
+                                          0x00020000);
+    const int row_b = (int)ld * 2;
+    u32x4 kreg[KPER];
+    uint2 vreg[8];
+    auto load_kv = [&](int kv0) __attribute__((always_inline)) {
+      const int pt = opaque(ptid);
+#pragma unroll
+      for (int p = 0; p < KPER; ++p) {
+        const int c = pt + p * NP;
+        kreg[p] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (kv0 + c / DCH) * row_b + (c % DCH) * 16, 0, 0));
+      }
+      const int vd4 = pt % (DC / 4), vg8 = pt / (DC / 4);
+      const int vbase = (kv0 + 16 * (vg8 >> 1) + 4 * (vg8 & 1)) * row_b + vd4 * 8;
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk)
+        vreg[kk] = __builtin_bit_cast(
+            uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vbase + ((kk & 3) + 8 * (kk >> 2)) * row_b, 0, 0));
+    };
+    auto store_kv = [&](int buf) __attribute__((always_inline)) {
+      const int pt = opaque(ptid);
+      uint16_t* sK = smem + buf * (SKK + SVV);
+      uint16_t* sV = sK + SKK;
+#pragma unroll
+      for (int p = 0; p < KPER; ++p) {
+        const int c = pt + p * NP, key = c / DCH, ch = c % DCH;
+        *reinterpret_cast<u32x4*>(sK + key * D + ((ch ^ (key & 15)) << 3)) = kreg[p];
+      }
+      const int vd4 = pt % (DC / 4), vg8 = pt / (DC / 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int d = vd4 * 4 + r;
+        u32x4 w;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t a = (r < 2) ? vreg[2 * j].x : vreg[2 * j].y;
+          const uint32_t b = (r < 2) ? vreg[2 * j + 1].x : vreg[2 * j + 1].y;
+          w[j] = __builtin_amdgcn_perm(b, a, (r & 1) ? 0x07060302u : 0x05040100u);
+        }
+        *reinterpret_cast<u32x4*>(sV + d * KVB + ((vg8 ^ swz_v(d)) << 3)) = w;
+      }
+    };
+    load_kv(0);
+    store_kv(0);
+    if (nkv > 1) load_kv(KVB);
+    __syncthreads();
+    for (int it = 0; it < nkv; ++it) {
+      if (it + 1 < nkv) store_kv((it + 1) & 1);
+      if (it + 2 < nkv) load_kv((it + 2) * KVB);
+      __syncthreads();
+    }
+    return;
+  }
+
+  // ---------------- compute waves ----------------
+  const int lane = tid & 63, qg = wave;
+  const int hh = lane >> 5, lr = lane & 31;
+  const int qw = q0 + qg * 32, qrow = qw + lr;
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (qrow < s) v = *reinterpret_cast<const u32x4*>(Qg + (int64_t)qrow * ld + (2 * ks + hh) * 8);
+    qf[ks] = __builtin_bit_cast(bf16x8, v);
+  }
+  f32x16 ot[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) ot[i][e] = 0.f;
+  float m_i = kNegInf, l_i = 0.f;
+
+  __syncthreads();
+  for (int it = 0; it < nkv; ++it) {
+    const int kv0 = it * KVB;
+    const uint16_t* sK = smem + (it & 1) * (SKK + SVV);
+    const uint16_t* sV = sK + SKK;
+    if (!((CAUSAL && kv0 > qw) || kv0 >= s)) {
+      f32x16 sc[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sc[t][e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int kr = 32 * t + lr;
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(sK + kr * D + (((2 * ks + hh) ^ (kr & 15)) << 3));
+          sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], sc[t], 0, 0, 0);
+        }
+      if ((CAUSAL && kv0 + KVB - 1 > qw) || kv0 + KVB > s) {
+        const int lim = (CAUSAL ? min(qrow, s - 1) : s - 1) - kv0 - 4 * hh;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 16; ++e)
+            if (32 * t + 8 * (e >> 2) + (e & 3) > lim) sc[t][e] = kNegInf;
+      }
+      float mx = fmaxf(sc[0][0], sc[1][0]);
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mx = fmaxf(mx, fmaxf(sc[0][e], sc[1][e]));
+      const float mt = xhalf_max(mx) * scale_log2;
+      if (__builtin_amdgcn_ballot_w64(mt > m_i + kTau) != 0) {
+        const float mn = fmaxf(m_i, mt);
+        const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_i - mn);
+        l_i *= alpha;
+#pragma unroll
+        for (int i = 0; i < DT; ++i)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ot[i][e] *= alpha;
+        m_i = mn;
+      }
+      const float mref = m_i == kNegInf ? 0.f : m_i;
+      float rs = 0.f;
+      bf16x8 pb[2][2], pl[2][2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          u32x4 u, ul;
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w], scale_log2, -mref));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w + 1], scale_log2, -mref));
+            rs += p0 + p1;
+            u[w] = cvt_bf16x2(p0, p1);
+            if constexpr (SPLIT)
+              ul[w] = cvt_bf16x2(p0 - bf16_bits_to_f32(u[w] & 0xffffu), p1 - bf16_bits_to_f32(u[w] >> 16));
+          }
+          pb[t][s2] = __builtin_bit_cast(bf16x8, u);
+          if constexpr (SPLIT) pl[t][s2] = __builtin_bit_cast(bf16x8, ul);
+        }
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int i = 0; i < DT; ++i) {
+            const int d = 32 * i + lr;
+            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((4 * t + 2 * s2 + hh) ^ swz_v(d)) << 3));
+            ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][s2], ot[i], 0, 0, 0);
+            if constexpr (SPLIT) ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[t][s2], ot[i], 0, 0, 0);
+          }
+      l_i += rs;
+    }
+    __syncthreads();
+  }
+
+  if (qrow < s) {
+    const int ln = opaque(lane), lr2 = ln & 31, hh2 = ln >> 5;
+    const float lsum = xhalf_sum(l_i);
+    const float inv = 1.f / lsum;
+    if (lse && dc == 0 && hh2 == 0) {
+      const float mref = m_i == kNegInf ? 0.f : m_i;
+      lse[((int64_t)bi * Hl + head) * s + qw + lr2] = (mref + __log2f(lsum)) * 0.69314718055994531f;
+    }
+    uint16_t* orow = O + ((int64_t)bi * s + qw + lr2) * ((int64_t)Hl * D) + (int64_t)head * D + dc * DC;
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 u;
+        u.x = cvt_bf16x2(ot[i][4 * g] * inv, ot[i][4 * g + 1] * inv);
+        u.y = cvt_bf16x2(ot[i][4 * g + 2] * inv, ot[i][4 * g + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * i + 8 * g + 4 * hh2) = u;
+      }
+  }
+}
+
+template <bool C, bool SPLIT>
+hipError_t launch_attn_wide(const uint16_t* qkv, uint16_t* O, float* lse, int b, int s, int Hl, hipStream_t st) {
+  const int nqb = (s + AQ - 1) / AQ;
+  const int64_t items = (int64_t)b * Hl * nqb * WNC;
+  if (items == 0) return hipSuccess;
+  // Buffer offsets are 32-bit: the furthest key row read is s - 1 + 1 stage.
+  if (items > (1LL << 28) || (int64_t)(s + 2 * KVB) * 3 * Hl * WD * 2 >= (1LL << 31)) return hipErrorInvalidValue;
+  const int per_xcd = (int)((items + 7) / 8);
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)WD);
+  hipLaunchKernelGGL((attn_fwd_wide_kernel<C, SPLIT>), dim3(8u * per_xcd), dim3(NT), 0, st, qkv, O, s, Hl, nqb,
+                     per_xcd, (int)items, scale_log2, lse);
+  return hipGetLastError();
+}
+
 template <int D, bool C, bool SPLIT>
 hipError_t launch_attn(const uint16_t* qkv, uint16_t* O, float* lse, int b, int s, int Hl, hipStream_t st) {
   const int nqb = (s + AQ - 1) / AQ;
@@ -358,6 +592,13 @@ hipError_t attn_fwd(const uint16_t* qkv, uint16_t* O, int b, int s, int Hl, int 
                     float* lse) {
   if (d == 128) return attn_fwd_d<128>(qkv, O, b, s, Hl, causal, st, lse);
   if (d == 64) return attn_fwd_d<64>(qkv, O, b, s, Hl, causal, st, lse);
+  if (d == WD) {
+    if (lse)
+      return causal ? launch_attn_wide<true, true>(qkv, O, lse, b, s, Hl, st)
+                    : launch_attn_wide<false, true>(qkv, O, lse, b, s, Hl, st);
+    return causal ? launch_attn_wide<true, false>(qkv, O, lse, b, s, Hl, st)
+                  : launch_attn_wide<false, false>(qkv, O, lse, b, s, Hl, st);
+  }
   return hipErrorInvalidValue;
 }
 

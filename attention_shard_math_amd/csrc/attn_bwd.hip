@@ -41,6 +41,7 @@
 // 16-row ds_read_b128 fragment reads and for the 4-row x 2-chunk transposing reads.
 #include "attn.hpp"
 #include "common.hpp"
+#include "gemm_bf16.hpp"
 
 
 namespace tps {
@@ -132,23 +133,25 @@ __device__ __forceinline__ void store_rows(const u32x4 (&reg)[R * D / 8 / NTH], 
 __global__ __launch_bounds__(256) void rowdot_kernel(const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O,
                                                      float* __restrict__ Dout, int s, int Hl, int D, int64_t rows) {
   const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);  // (token, head)
-  const int j = threadIdx.x & 15;
-  const int cpr = D / 8;  // 16-byte chunks per head row (8 or 16)
+  const int j0 = threadIdx.x & 15;
+  const int cpr = D / 8;  // 16-byte chunks per head row (8, 16 or 48)
   float acc = 0.f;
-  if (r < rows && j < cpr) {
+  if (r < rows) {
     const int64_t t = r / Hl, head = r % Hl;
-    const int64_t off = t * (int64_t)Hl * D + head * D + j * 8;
-    const u32x4 a = *reinterpret_cast<const u32x4*>(dO + off);
-    const u32x4 b = *reinterpret_cast<const u32x4*>(O + off);
+    for (int j = j0; j < cpr; j += 16) {
+      const int64_t off = t * (int64_t)Hl * D + head * D + j * 8;
+      const u32x4 a = *reinterpret_cast<const u32x4*>(dO + off);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(O + off);
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc += bf16_bits_to_f32(a[w] & 0xffffu) * bf16_bits_to_f32(b[w] & 0xffffu);
-      acc += bf16_bits_to_f32(a[w] >> 16) * bf16_bits_to_f32(b[w] >> 16);
+      for (int w = 0; w < 4; ++w) {
+        acc += bf16_bits_to_f32(a[w] & 0xffffu) * bf16_bits_to_f32(b[w] & 0xffffu);
+        acc += bf16_bits_to_f32(a[w] >> 16) * bf16_bits_to_f32(b[w] >> 16);
+      }
     }
   }
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 16);
-  if (r < rows && j == 0) {
+  if (r < rows && j0 == 0) {
     const int64_t t = r / Hl, head = r % Hl, bi = t / s, q = t % s;
     Dout[(bi * Hl + head) * s + q] = acc;
   }
@@ -609,10 +612,177 @@ hipError_t launch_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ wide heads
+// Heads of d = 384 run the backward as per-head products on the bf16 GEMM: a
+// fused walk would need the K and V fragments of its keys over all 384 d
+// (192 registers per lane) next to its dK and dV accumulators. Per sequence and
+// head, with S and dP held in a float32 [s, s] buffer:
+//   S = Q K^T; P = exp(S / sqrt(d) - lse) (0 above the diagonal), as hi and lo
+//   bf16 halves; dV = [P_hi; P_lo]^T [dO; dO] (the pair as one product of depth
+//   2s); dP = dO V^T; dS = (P_hi + P_lo)(dP - D) / sqrt(d) as hi and lo halves;
+//   dK = [dS_hi; dS_lo]^T [Q; Q]; dQ = [dS_hi | dS_lo] [K; K].
+// The products of depth 2s have few output tiles (s/256 x 2 at s = 4096), so they
+// run stream-K over all workgroups.
+constexpr int kWideD = 384;
+
+// dst [2*rows, D] = [src; src] for one head's [rows, D] slice of a row-major tensor
+// with leading dimension ld (elements).
+__global__ __launch_bounds__(256) void stack2_kernel(const uint16_t* __restrict__ src, int64_t ld, int rows,
+                                                     uint16_t* __restrict__ dst) {
+  constexpr int CPR = kWideD / 8;
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= (int64_t)rows * CPR) return;
+  const int64_t r = v / CPR, c = v % CPR;
+  const u32x4 x = *reinterpret_cast<const u32x4*>(src + r * ld + c * 8);
+  *reinterpret_cast<u32x4*>(dst + r * kWideD + c * 8) = x;
+  *reinterpret_cast<u32x4*>(dst + (r + rows) * kWideD + c * 8) = x;
+}
+
+// P from the scores: Pst rows [0, s) hold bf16(P), rows [s, 2s) bf16(P - bf16(P)).
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void p_split_kernel(const float* __restrict__ S, const float* __restrict__ lse,
+                                                      int s, float scale_log2, uint16_t* __restrict__ Pst) {
+  const int q = blockIdx.y;
+  const float L = lse[q] * kLog2e;
+  for (int k = (blockIdx.x * 256 + threadIdx.x) * 4; k < s; k += gridDim.x * 256 * 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(S + (int64_t)q * s + k);
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      p[e] = (CAUSAL && k + e > q) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -L));
+    const uint32_t h0 = cvt2(p[0], p[1]), h1 = cvt2(p[2], p[3]);
+    const uint32_t l0 = cvt2(p[0] - bf16_bits_to_f32(h0 & 0xffffu), p[1] - bf16_bits_to_f32(h0 >> 16));
+    const uint32_t l1 = cvt2(p[2] - bf16_bits_to_f32(h1 & 0xffffu), p[3] - bf16_bits_to_f32(h1 >> 16));
+    *reinterpret_cast<uint2*>(Pst + (int64_t)q * s + k) = uint2{h0, h1};
+    *reinterpret_cast<uint2*>(Pst + ((int64_t)s + q) * s + k) = uint2{l0, l1};
+  }
+}
+
+// dS = (P_hi + P_lo)(dP - D_q) / sqrt(d), as hi/lo halves in two layouts: rows
+// stacked (dSr [2s, s], for dK) and columns side by side (dSc [s, 2s], for dQ).
+__global__ __launch_bounds__(256) void ds_split_kernel(const float* __restrict__ dP, const uint16_t* __restrict__ Pst,
+                                                       const float* __restrict__ Dq, int s, float scale,
+                                                       uint16_t* __restrict__ dSr, uint16_t* __restrict__ dSc) {
+  const int q = blockIdx.y;
+  const float D = Dq[q];
+  for (int k = (blockIdx.x * 256 + threadIdx.x) * 4; k < s; k += gridDim.x * 256 * 4) {
+    const f32x4 x = *reinterpret_cast<const f32x4*>(dP + (int64_t)q * s + k);
+    const uint2 ph = *reinterpret_cast<const uint2*>(Pst + (int64_t)q * s + k);
+    const uint2 pl = *reinterpret_cast<const uint2*>(Pst + ((int64_t)s + q) * s + k);
+    const float p[4] = {bf16_bits_to_f32(ph.x & 0xffffu) + bf16_bits_to_f32(pl.x & 0xffffu),
+                        bf16_bits_to_f32(ph.x >> 16) + bf16_bits_to_f32(pl.x >> 16),
+                        bf16_bits_to_f32(ph.y & 0xffffu) + bf16_bits_to_f32(pl.y & 0xffffu),
+                        bf16_bits_to_f32(ph.y >> 16) + bf16_bits_to_f32(pl.y >> 16)};
+    float g[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) g[e] = p[e] * (x[e] - D) * scale;
+    const uint32_t h0 = cvt2(g[0], g[1]), h1 = cvt2(g[2], g[3]);
+    const uint32_t l0 = cvt2(g[0] - bf16_bits_to_f32(h0 & 0xffffu), g[1] - bf16_bits_to_f32(h0 >> 16));
+    const uint32_t l1 = cvt2(g[2] - bf16_bits_to_f32(h1 & 0xffffu), g[3] - bf16_bits_to_f32(h1 >> 16));
+    *reinterpret_cast<uint2*>(dSr + (int64_t)q * s + k) = uint2{h0, h1};
+    *reinterpret_cast<uint2*>(dSr + ((int64_t)s + q) * s + k) = uint2{l0, l1};
+    *reinterpret_cast<uint2*>(dSc + (int64_t)q * 2 * s + k) = uint2{h0, h1};
+    *reinterpret_cast<uint2*>(dSc + (int64_t)q * 2 * s + s + k) = uint2{l0, l1};
+  }
+}
+
+struct WideLayout {
+  int64_t d_bytes, s_bytes, p_bytes, stack_bytes, sk_bytes;
+  int64_t total() const { return d_bytes + s_bytes + 3 * p_bytes + 3 * stack_bytes + sk_bytes; }
+};
+
+inline WideLayout wide_layout(int b, int s, int Hl) {
+  WideLayout L;
+  L.d_bytes = r256((int64_t)b * Hl * s * 4);
+  L.s_bytes = r256((int64_t)s * s * 4);
+  L.p_bytes = r256((int64_t)2 * s * s * 2);
+  L.stack_bytes = r256((int64_t)2 * s * kWideD * 2);
+  L.sk_bytes = (int64_t)kSkBytes;
+  return L;
+}
+
+GemmArgs wide_args(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, void* C, int64_t ldc,
+                   void* sk) {
+  GemmArgs g{};
+  g.A = static_cast<const uint16_t*>(A);
+  g.B = static_cast<const uint16_t*>(B);
+  g.lda = lda;
+  g.ldb = ldb;
+  g.M = M;
+  g.N = N;
+  g.K = K;
+  g.C = C;
+  g.ldc = ldc;
+  gemm_bf16_sk_attach(g, sk);
+  return g;
+}
+
+#define TPS_TRY_HIP(expr)                  \
+  do {                                     \
+    const hipError_t _e = (expr);          \
+    if (_e != hipSuccess) return _e;       \
+  } while (0)
+
+template <bool CAUSAL>
+hipError_t launch_bwd_wide(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO, const float* lse,
+                           uint16_t* dqkv, void* ws, int b, int s, int Hl, hipStream_t st) {
+  constexpr int D = kWideD;
+  const int64_t rows = (int64_t)b * s * Hl;
+  if (rows == 0) return hipSuccess;
+  // the [2s, s] bf16 pair buffers are GEMM operands: below 2 GiB
+  if ((int64_t)2 * s * s * 2 >= (1LL << 31) - 16) return hipErrorInvalidValue;
+  const WideLayout L = wide_layout(b, s, Hl);
+  char* w = static_cast<char*>(ws);
+  float* Dws = reinterpret_cast<float*>(w);
+  float* Sbuf = reinterpret_cast<float*>(w + L.d_bytes);
+  uint16_t* Pst = reinterpret_cast<uint16_t*>(w + L.d_bytes + L.s_bytes);
+  uint16_t* dSr = reinterpret_cast<uint16_t*>(w + L.d_bytes + L.s_bytes + L.p_bytes);
+  uint16_t* dSc = reinterpret_cast<uint16_t*>(w + L.d_bytes + L.s_bytes + 2 * L.p_bytes);
+  uint16_t* Q2 = reinterpret_cast<uint16_t*>(w + L.d_bytes + L.s_bytes + 3 * L.p_bytes);
+  uint16_t* K2 = Q2 + L.stack_bytes / 2;
+  uint16_t* dO2 = K2 + L.stack_bytes / 2;
+  void* sk = w + L.d_bytes + L.s_bytes + 3 * L.p_bytes + 3 * L.stack_bytes;
+  const float scale = 1.f / sqrtf((float)D), scale_log2 = kLog2e * scale;
+  const int64_t ld = 3LL * Hl * D, ldo = (int64_t)Hl * D;
+  hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, dO, O, Dws, s, Hl, D, rows);
+  TPS_TRY_HIP(hipGetLastError());
+  const unsigned stack_blocks = (unsigned)(((int64_t)s * (D / 8) + 255) / 256);
+  const dim3 row_grid((unsigned)min(16, (s / 4 + 255) / 256), (unsigned)s);
+  for (int bi = 0; bi < b; ++bi)
+    for (int j = 0; j < Hl; ++j) {
+      const uint16_t* Qh = qkv + (int64_t)bi * s * ld + (int64_t)j * D;
+      const uint16_t* Kh = Qh + (int64_t)Hl * D;
+      const uint16_t* Vh = Qh + 2LL * Hl * D;
+      const uint16_t* dOh = dO + (int64_t)bi * s * ldo + (int64_t)j * D;
+      const float* lseh = lse + ((int64_t)bi * Hl + j) * s;
+      const float* Dh = Dws + ((int64_t)bi * Hl + j) * s;
+      uint16_t* dQh = dqkv + (int64_t)bi * s * ld + (int64_t)j * D;
+      uint16_t* dKh = dQh + (int64_t)Hl * D;
+      uint16_t* dVh = dQh + 2LL * Hl * D;
+      hipLaunchKernelGGL(stack2_kernel, dim3(stack_blocks), dim3(256), 0, st, Qh, ld, s, Q2);
+      hipLaunchKernelGGL(stack2_kernel, dim3(stack_blocks), dim3(256), 0, st, Kh, ld, s, K2);
+      hipLaunchKernelGGL(stack2_kernel, dim3(stack_blocks), dim3(256), 0, st, dOh, ldo, s, dO2);
+      // S = Q K^T: A = Q [s, D] (K-contig), B(k, n) = K[n, k] (K-contig)
+      TPS_TRY_HIP(gemm_bf16(wide_args(Qh, ld, Kh, ld, s, s, D, Sbuf, s, sk), true, true, EPI_F32, st));
+      hipLaunchKernelGGL((p_split_kernel<CAUSAL>), row_grid, dim3(256), 0, st, Sbuf, lseh, s, scale_log2, Pst);
+      // dV = [P_hi; P_lo]^T [dO; dO]: A(m, k) = Pst[k, m] (M-contig), B(k, n) = dO2[k, n] (N-contig)
+      TPS_TRY_HIP(gemm_bf16(wide_args(Pst, s, dO2, D, s, D, 2 * s, dVh, ld, sk), false, false, EPI_BF16, st));
+      // dP = dO V^T: A = dO [s, D] (K-contig), B(k, n) = V[n, k] (K-contig)
+      TPS_TRY_HIP(gemm_bf16(wide_args(dOh, ldo, Vh, ld, s, s, D, Sbuf, s, sk), true, true, EPI_F32, st));
+      hipLaunchKernelGGL(ds_split_kernel, row_grid, dim3(256), 0, st, Sbuf, Pst, Dh, s, scale, dSr, dSc);
+      // dK = [dS_hi; dS_lo]^T [Q; Q]: A(m, k) = dSr[k, m] (M-contig), B(k, n) = Q2[k, n] (N-contig)
+      TPS_TRY_HIP(gemm_bf16(wide_args(dSr, s, Q2, D, s, D, 2 * s, dKh, ld, sk), false, false, EPI_BF16, st));
+      // dQ = [dS_hi | dS_lo] [K; K]: A = dSc [s, 2s] (K-contig), B(k, n) = K2[k, n] (N-contig)
+      TPS_TRY_HIP(gemm_bf16(wide_args(dSc, 2LL * s, K2, D, s, D, 2 * s, dQh, ld, sk), true, false, EPI_BF16, st));
+    }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 size_t attn_bwd_workspace(int b, int s, int Hl, int d) {
   if (b <= 0 || s <= 0 || Hl <= 0) return 0;
+  if (d == kWideD) return (size_t)wide_layout(b, s, Hl).total();
   const BwdLayout L = bwd_layout(b, s, Hl, d);
   return (size_t)(L.d_bytes + L.q_bytes + 2 * L.kv_bytes);
 }
@@ -625,6 +795,9 @@ hipError_t attn_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO, 
   if (d == 64)
     return causal ? launch_bwd<64, true>(qkv, O, dO, lse, dqkv, ws, b, s, Hl, st)
                   : launch_bwd<64, false>(qkv, O, dO, lse, dqkv, ws, b, s, Hl, st);
+  if (d == kWideD)
+    return causal ? launch_bwd_wide<true>(qkv, O, dO, lse, dqkv, ws, b, s, Hl, st)
+                  : launch_bwd_wide<false>(qkv, O, dO, lse, dqkv, ws, b, s, Hl, st);
   return hipErrorInvalidValue;
 }
 

@@ -659,6 +659,7 @@ hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, int epi,
     if (epi == EPI_BF16) return launch<BM, BN, true, true, EPI_BF16>(g, s);
   } else if (!a_kcontig && !b_kcontig) {
     if (epi == EPI_F32) return launch<BM, BN, false, false, EPI_F32>(g, s);
+    if (epi == EPI_BF16) return launch<BM, BN, false, false, EPI_BF16>(g, s);
   }
   return hipErrorInvalidValue;
 }

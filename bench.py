@@ -136,14 +136,16 @@ def hbm_ceilings(torch, dev, reps=10):
 
 
 def next_rows(tp, torch, dev, randn, reps=5):
-    """Rows beyond the step, timed on their own after it: the PaLM-shaped MLP shard
-    (M=2048, h=18432, f=9216), forward with saved U, backward with activation
-    recompute (U, Y formed again from X and A_i inside mlp_bwd); the
+    """Rows beyond the step, timed on their own after it: the PaLM 540B MLP shard
+    (M = 4096, the page's context; h = 18432, f = 9216), forward with saved U,
+    backward with activation recompute (U, Y formed again from X and A_i inside
+    mlp_bwd); the PaLM attention shard (6 local heads of 384, s = 4096), forward and
+    backward; the
     vocabulary-parallel output layer + cross-entropy of one rank; the attention
     backward (core, and the whole shard); the sequence-parallel LayerNorm,
     all-gather and reduce-scatter of one rank; and, as context, the runtime's
     library GEMM on the six MLP products."""
-    Mp, Hp, Fp = 2048, 18432, 9216
+    Mp, Hp, Fp = 4096, 18432, 9216
     X = randn((Mp, Hp), 1.0, 40)
     A = randn((Hp, Fp), 0.005, 41)
     B = randn((Fp, Hp), 0.005, 42)
@@ -174,6 +176,46 @@ def next_rows(tp, torch, dev, randn, reps=5):
         out[name] = {"ms": round(ms, 4), "gemms": n_gemm, "tflops": round(tf, 1),
                      "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
     del X, A, B, dZ, U, Y, Z, dX, dA, dB, ws
+    torch.cuda.empty_cache()
+
+    # PaLM attention shard: 48 heads of 384 over 8 ranks (6 local), s = 4096, h = 18432.
+    Sp, Hpa, Hlp, Dp = 4096, 18432, 6, 384
+    wp = Hlp * Dp
+    Xp = randn((Sp, Hpa), 1.0, 90)
+    Wqkvp = randn((Hpa, 3 * wp), 0.005, 91)
+    Wop = randn((wp, Hpa), 0.005, 92)
+    dOutp = randn((Sp, Hpa), 1.0, 93)
+    outpp = torch.empty(Sp, Hpa, dtype=torch.float32, device=dev)
+    wsf = torch.empty(tp.attn_fwd_workspace(1, Sp, Hlp, Dp, h=Hpa), dtype=torch.uint8, device=dev)
+    QKVp = torch.empty(Sp, 3 * wp, dtype=torch.bfloat16, device=dev)
+    Op = torch.empty(Sp, wp, dtype=torch.bfloat16, device=dev)
+    lsep = torch.empty(1, Hlp, Sp, dtype=torch.float32, device=dev)
+    tp.attn_fwd_train(Xp, Wqkvp, Wop, outpp, QKVp, Op, lsep, 1, Sp, Hlp, Dp, True)
+    dXp = torch.empty(Sp, Hpa, dtype=torch.float32, device=dev)
+    dWqkvp = torch.empty(Hpa, 3 * wp, dtype=torch.float32, device=dev)
+    dWop = torch.empty(wp, Hpa, dtype=torch.float32, device=dev)
+    wsbp = torch.empty(tp.attn_bwd_workspace(1, Sp, Hpa, Hlp, Dp), dtype=torch.uint8, device=dev)
+    pairs = Sp * (Sp + 1) / 2
+    fwd_gf = (2 * 2 * Dp * Hlp * pairs + gemm_flops(Sp, 3 * wp, Hpa) + gemm_flops(Sp, Hpa, wp)) / 1e9
+    bwd_gf = (5 * 2 * Dp * Hlp * pairs + 2 * gemm_flops(Sp, wp, Hpa) + 2 * gemm_flops(Sp, 3 * wp, Hpa)) / 1e9
+    for name, fn, gf in (
+            ("palm_attn_fwd", lambda: tp.attn_fwd(Xp, Wqkvp, Wop, outpp, wsf, 1, Sp, Hlp, Dp, True), fwd_gf),
+            ("palm_attn_bwd", lambda: tp.attn_bwd(Xp, Wqkvp, Wop, QKVp, Op, lsep, dOutp, dXp, dWqkvp, dWop, wsbp, 1,
+                                                  Sp, Hlp, Dp, True), bwd_gf)):
+        for _ in range(2):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = gf * 1e9 / (ms * 1e-3) / 1e12
+        out[name] = {"ms": round(ms, 4), "gflop": round(gf, 2), "tflops": round(tf, 1),
+                     "frac_bf16_peak": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del Xp, Wqkvp, Wop, dOutp, outpp, wsf, QKVp, Op, lsep, dXp, dWqkvp, dWop, wsbp
     torch.cuda.empty_cache()
 
     # Vocabulary-parallel output layer + cross-entropy: one rank's slice of the
@@ -231,7 +273,7 @@ def next_rows(tp, torch, dev, randn, reps=5):
     tp.attn_fwd_train(Xa, Wqkv, Wo, outp, QKV, Oa, lse, 1, Sa, Hla, Da, True)
     dOa = randn((Sa, wa), 1.0, 84)
     dQKV = torch.empty_like(QKV)
-    wsc = torch.empty(tp.attn_core_bwd_workspace(1, Sa, Hla), dtype=torch.uint8, device=dev)
+    wsc = torch.empty(tp.attn_core_bwd_workspace(1, Sa, Hla, Da), dtype=torch.uint8, device=dev)
     dXa = torch.empty(Sa, Ha, dtype=torch.float32, device=dev)
     dWqkv = torch.empty(Ha, 3 * wa, dtype=torch.float32, device=dev)
     dWo = torch.empty(wa, Ha, dtype=torch.float32, device=dev)

@@ -180,9 +180,11 @@ size_t tp_mlp_bwd_noalloc_max_bytes(void);
  *       at columns j*d .. (j+1)*d of each block.
  *   O   [b*s, Hl*d] bf16: O_j = softmax(Q_j K_j^T / sqrt(d)) V_j per sequence;
  *       with causal != 0 query t sees keys u <= t.
- * d must be 64 or 128, and (s + 128) * 3 * n_heads_local * d * 2 < 2^31 (one
- * sequence's rows are addressed with 32-bit byte offsets); otherwise
- * TP_ERR_UNSUPPORTED. Softmax in float32, P rounded to bf16 for the P V product. */
+ * d must be 64, 128 or 384 (GPT-3's 12288 / 96 heads and PaLM's 18432 / 48 heads;
+ * "Megatron-LM：张量并行与大规模训练", §5.6 and §5.7), and
+ * (s + 128) * 3 * n_heads_local * d * 2 < 2^31 (one sequence's rows are addressed
+ * with 32-bit byte offsets); otherwise TP_ERR_UNSUPPORTED. Softmax in float32, P
+ * rounded to bf16 for the P V product. */
 tp_status tp_attn_core(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head,
                        int causal, const void* QKV, void* O, void* stream);
 
@@ -235,11 +237,14 @@ tp_status tp_attn_fwd_train(int64_t b, int64_t s, int64_t h, int64_t n_heads_loc
  *   P = exp(q.k / sqrt(d) - lse), dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO*O)),
  *   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d); written as bf16 dQKV [b*s, 3*Hl*d] in the
  *   [Q | K | V] layout of QKV. dO bf16 [b*s, Hl*d]; lse from tp_attn_fwd_train.
- *   Deterministic (no atomics). ws: tp_attn_core_bwd_workspace(b, s, Hl) bytes. */
+ *   Deterministic (no atomics). ws: tp_attn_core_bwd_workspace(b, s, Hl, d) bytes.
+ *   d = 384 runs per-head products with float32 [s, s] scores and bf16 [2s, s]
+ *   probability and gradient pairs in the workspace (about 16 s^2 bytes plus the
+ *   100.7 MB stream-K area); it needs s % 8 == 0 (TP_ERR_UNSUPPORTED otherwise). */
 tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
                            const void* QKV, const void* O, const void* dO, const float* lse,
                            void* dQKV, void* ws, size_t ws_bytes, void* stream);
-size_t tp_attn_core_bwd_workspace(int64_t b, int64_t s, int64_t n_heads_local);
+size_t tp_attn_core_bwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head);
 
 /* Backward of one rank's attention shard [same page, 三、§3.2; "Megatron-LM：张量并行与
  * 大规模训练" §2.2]: with dOut bf16 [b*s, h] (replicated, the output all-reduce's

@@ -150,7 +150,7 @@ class TestValidation:
         assert lib.tp_attn_fwd(2, 100, 260, 3, 64, 1, P, P, P, P, P, ws, None) == UNSUPPORTED  # h % 8
 
     def test_attention_backward(self):
-        ws = lib.tp_attn_core_bwd_workspace(2, 100, 3)
+        ws = lib.tp_attn_core_bwd_workspace(2, 100, 3, 128)
         assert ws == 2 * 100 * 3 * 4 + (-(2 * 100 * 3 * 4) % 256)
         cb = lib.tp_attn_core_bwd
         assert cb(1, 16, 2, 96, 1, P, P, P, P, P, P, ws, None) == UNSUPPORTED       # d_head
@@ -159,10 +159,18 @@ class TestValidation:
         assert cb(1, 16, 2, 128, 1, P, P, P, P, P, P, 16 * 2 * 4 - 4, None) == WORKSPACE
         assert cb(1, 16, 2, 128, 1, P, MIS, P, P, P, P, 256, None) == UNSUPPORTED
         assert cb(0, 16, 2, 128, 1, None, None, None, None, None, None, 0, None) == OK
+        # 384-wide heads: per-head products over [s, s] scores and [2s, s] pairs, s % 8 == 0
+        s = 4096
+        ws384 = lib.tp_attn_core_bwd_workspace(1, s, 6, 384)
+        assert ws384 == (6 * s * 4 + s * s * 4 + 3 * 2 * s * s * 2 + 3 * 2 * s * 384 * 2 + SK_BYTES)
+        assert lib.tp_attn_core_bwd_workspace(1, s, 6, 96) == 0
+        assert cb(1, 1004, 6, 384, 1, P, P, P, P, P, P, ws384, None) == UNSUPPORTED  # s % 8
+        assert "s % 8" in _err()
+        assert cb(1, s, 6, 384, 1, P, P, P, P, P, P, ws384 - 1, None) == WORKSPACE
         need = lib.tp_attn_bwd_workspace(1, 64, 256, 2, 64)
         t, w = 64, 128
         assert need == (-(-t * w * 2 // 256) * 256 + -(-t * 3 * w * 2 // 256) * 256
-                        + -(-lib.tp_attn_core_bwd_workspace(1, 64, 2) // 256) * 256 + SK_BYTES)
+                        + -(-lib.tp_attn_core_bwd_workspace(1, 64, 2, 64) // 256) * 256 + SK_BYTES)
         b = lib.tp_attn_bwd
         args = [P] * 10  # X, Wqkv_i, Wo_i, QKV, O, lse, dOut, dX_i, dWqkv_i, dWo_i
         assert b(1, 64, 256, 2, 64, 1, *args, P, need - 1, None) == WORKSPACE

@@ -38,7 +38,7 @@ def _core_case(b, s, Hl, d, causal, seed):
     lse = torch.full((b, Hl, s), float("nan"), dtype=torch.float32, device=DEV)
     tp.attn_core_train(Q, O, lse, b, s, Hl, d, causal)
     dq = torch.full((b * s, 3 * w), float("nan"), dtype=torch.bfloat16, device=DEV)
-    ws = torch.empty(tp.attn_core_bwd_workspace(b, s, Hl), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(tp.attn_core_bwd_workspace(b, s, Hl, d), dtype=torch.uint8, device=DEV)
     tp.attn_core_bwd(Q, O, bf16_dev(dO), lse, dq, ws, b, s, Hl, d, causal)
     return qkv, dO, O, lse, dq, (Q, bf16_dev(dO), ws)
 
@@ -46,10 +46,13 @@ def _core_case(b, s, Hl, d, causal, seed):
 # Walks longer than 16 key (or query) tiles of 32 are cut into chunks whose fp32
 # partials a combine pass adds: s = 513 and 530 (causal) and s = 600 (every block,
 # not causal) cover that path for both head sizes.
+# d = 384 runs the per-head product path (s % 8 == 0).
 @pytest.mark.parametrize("b,s,Hl,d,causal", [(2, 300, 2, 128, True), (1, 77, 3, 64, True),
                                               (2, 200, 2, 128, False), (1, 1, 1, 128, True),
                                               (3, 129, 1, 64, False), (1, 513, 1, 128, True),
-                                              (2, 530, 1, 64, True), (1, 600, 2, 64, False)])
+                                              (2, 530, 1, 64, True), (1, 600, 2, 64, False),
+                                              (1, 304, 2, 384, True), (2, 200, 1, 384, False),
+                                              (1, 8, 1, 384, True)])
 def test_core_backward(b, s, Hl, d, causal):
     note(f"attn_core_bwd b={b} s={s} Hl={Hl} d={d} causal={causal}")
     qkv, dO, O, lse, dq, _ = _core_case(b, s, Hl, d, causal, 90 + s + d)
@@ -94,10 +97,12 @@ def _shard_case(b, s, h, Hl, d, ai, dOut_bits, causal=True):
 # Small and ragged shards drawn with the GPT-3 shard's activation statistics: the
 # weights' sigma is 0.006 * sqrt(12288 / h), so that Q, K, V, O and the gradients
 # have the scale they have at h = 12288 (the mean-abs bar is absolute).
-@pytest.mark.parametrize("b,s,h,Hl,d", [(2, 300, 512, 2, 128), (1, 150, 256, 4, 64)])
+# 384-wide heads use the PaLM shard's scale, 0.005 * sqrt(18432 / h).
+@pytest.mark.parametrize("b,s,h,Hl,d", [(2, 300, 512, 2, 128), (1, 150, 256, 4, 64), (1, 264, 768, 2, 384)])
 def test_shard_backward(b, s, h, Hl, d):
     note(f"attn_fwd_train + attn_bwd b={b} s={s} h={h} Hl={Hl} d={d}")
-    ai = attn_inputs(b, s, h, Hl, d, 180 + s, 1.0, 0.006 * np.sqrt(12288 / h))
+    sigma_w = 0.005 * np.sqrt(18432 / h) if d == 384 else 0.006 * np.sqrt(12288 / h)
+    ai = attn_inputs(b, s, h, Hl, d, 180 + s, 1.0, sigma_w)
     dOut = bf16_bits(draw_normal_f32(np.random.default_rng(181 + s), (b * s, h), 1.0))
     out, dX, dWqkv, dWo, ws = _shard_case(b, s, h, Hl, d, ai, dOut)
     torch.cuda.synchronize()
@@ -112,15 +117,17 @@ def test_shard_backward(b, s, h, Hl, d):
     assert_grad_close(f64_host(dO), r["dO"], "dO")
 
 
-def test_full_size_gpt3_shard_backward():
-    """GPT-3 shard: 12 local heads of 128, s = 2048, h = 12288; every output
-    against the full float64 oracle."""
-    c = CONFIGS["gpt3_attn_rank_shard"]
+@pytest.mark.parametrize("cfg", ["gpt3_attn_rank_shard", "palm_attn_rank_shard"])
+def test_full_size_shard_backward(cfg):
+    """GPT-3 shard (12 local heads of 128, s = 2048, h = 12288) and PaLM shard (6
+    local heads of 384, s = 4096, h = 18432): every output against the full
+    float64 oracle."""
+    c = CONFIGS[cfg]
     b, s, h, d = c["b"], c["s"], c["h"], c["d_head"]
     Hl = c["n_heads"] // c["N"]
     ai = attn_inputs(b, s, h, Hl, d, c["seed"], c["sigma_x"], c["sigma_w"])
     dOut = bf16_bits(draw_normal_f32(np.random.default_rng(c["seed"] + 1), (b * s, h), 1.0))
-    note("attn_fwd_train + attn_bwd GPT-3 shard full size")
+    note(f"attn_fwd_train + attn_bwd {cfg} full size")
     out, dX, dWqkv, dWo, ws = _shard_case(b, s, h, Hl, d, ai, dOut)
     torch.cuda.synchronize()
     r = oracle.attn_shard_bwd(*(bf16_bits_to_f64(ai[k]) for k in ("X", "Wqkv", "Wo")), bf16_bits_to_f64(dOut),

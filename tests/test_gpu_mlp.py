@@ -207,10 +207,11 @@ def test_backward_recompute_matches_saved(M, h, f):
 
 
 class TestPalmShape:
-    """PaLM-shaped rank shard (M=2048, h=18432, f=9216): forward with saved U,
-    backward with activation recompute; sampled outputs from the oracle."""
+    """PaLM-shaped rank shard (M = 4096, the page's context; h = 18432, f = 9216):
+    forward with saved U, backward with activation recompute; sampled outputs and
+    every element against the oracle."""
 
-    ROWS = np.array([0, 255, 256, 1024, 2047])
+    ROWS = np.array([0, 255, 256, 1024, 2047, 4095])
     COLS = np.array([0, 191, 192, 5000, 9215])
 
     @pytest.fixture(scope="class")
@@ -240,12 +241,13 @@ class TestPalmShape:
             assert_bf16_close(f64_host(g[k][torch.from_numpy(self.ROWS).to(DEV)]), r[k], f"{k} rows")
 
     def test_backward_samples(self, case):
+        """Sampled dX rows. dA and dB are sums over all 4096 tokens, where a rare bf16
+        rounding flip of dU or Y moves a whole column or row: their mean error over
+        a few sampled columns is a noisy estimate of the bar's mean over all
+        entries, so test_every_element carries the bar for them."""
         o, g = case
         s = oracle.mlp_bwd_cols(o["X"], o["A"], o["B"], o["dZ"], self.ROWS, self.COLS)
         rows = torch.from_numpy(self.ROWS).to(DEV)
-        cols = torch.from_numpy(self.COLS).to(DEV)
-        assert_bf16_close(f64_host(g["dA"][:, cols]), s["dA_cols"], "dA columns")
-        assert_bf16_close(f64_host(g["dB"][cols, :]), s["dB_rows"], "dB rows")
         assert_bf16_close(f64_host(g["dX"][rows, :]), s["dX_rows"], "dX rows")
 
     def test_every_element(self, case):

@@ -31,9 +31,13 @@ CONFIGS = {
             d_head=128, dtype="bf16", sigma_x=1.0, sigma_w=0.006, seed=1004),
     "vocab_parallel_embed": dict(name="vocab_parallel_embed", v=50304, N=8, h=12288, b=8, s=2048,
             dtype="bf16", sigma_w=0.02, seed=1005),
-    # PaLM-shaped rank shard (h = 18432, TP = 8, f = 4h/8), a second MLP shape.
-    "palm_mlp_rank_shard": dict(name="palm_mlp_rank_shard", b=1, s=2048, h=18432, f=9216, N=8, dtype="bf16",
+    # PaLM 540B rank shard (h = 18432, 48 heads, context 4096, TP = 8, f = 4h/8)
+    # [Megatron-LM：张量并行与大规模训练, §5.7]: a second MLP shape and the attention
+    # shard of 6 local heads of 18432 / 48 = 384.
+    "palm_mlp_rank_shard": dict(name="palm_mlp_rank_shard", b=1, s=4096, h=18432, f=9216, N=8, dtype="bf16",
             sigma_x=1.0, sigma_w=0.005, sigma_dz=1.0, seed=1006),
+    "palm_attn_rank_shard": dict(name="palm_attn_rank_shard", b=1, s=4096, h=18432, n_heads=48, N=8,
+            d_head=384, dtype="bf16", sigma_x=1.0, sigma_w=0.005, seed=1009),
     # Vocabulary-parallel output layer + cross-entropy over the GPT-3 vocabulary
     # (padded to 50304 = 8 * 6288), one sequence of 2048 tokens.
     "vocab_parallel_ce": dict(name="vocab_parallel_ce", v=50304, N=8, h=12288, b=1, s=2048, dtype="bf16",
