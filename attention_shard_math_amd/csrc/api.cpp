@@ -589,10 +589,13 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
   return ok();
 }
 
+// float32 [M][ce_slots(V)][2]: (max, sum of exp) per row and column slot
+static size_t ce_stats_bytes(int64_t M, int64_t V) { return (size_t)M * (size_t)tps::ce_slots((int)V) * 8; }
+
 TP_API size_t tp_vocab_ce_workspace(int64_t M, int64_t h, int64_t lo, int64_t hi) {
-  if (M < 0 || h <= 0 || lo < 0 || hi <= lo) return 0;
-  // the stream-K area (if the logits GEMM uses one) follows the logits
-  return round256((size_t)M * (size_t)(hi - lo) * 4) + sk_need(M, hi - lo, h);
+  if (M < 0 || h <= 0 || lo < 0 || hi <= lo || hi - lo > kMaxDim) return 0;
+  // the logits GEMM's per-slot row statistics, then its stream-K area (if it uses one)
+  return round256(ce_stats_bytes(M, hi - lo)) + sk_need(M, hi - lo, h);
 }
 
 TP_API tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t hi, const void* H, const void* E_i,
@@ -618,12 +621,17 @@ TP_API tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t 
   TRY(check_ptr(fn, "ws", ws));
   hipStream_t st = as_stream(stream);
   const int64_t V = hi - lo;
-  float* logits = static_cast<float*>(ws);
-  // logits_i = H E_i^T: A = H [M,h] (K-contig), B(k,n) = E_i[n, k] (K-contig).
-  tps::GemmArgs g = make_args(H, h, E_i, h, M, V, h, logits, V);
-  tps::gemm_bf16_sk_attach(g, static_cast<char*>(ws) + round256((size_t)M * (size_t)V * 4));
-  TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_F32, st), fn));
-  return hip_status(tps::ce_rows(logits, M, (int)V, targets, lo, rowmax_i, sumexp_i, tlogit_i, st), fn);
+  float* stats = static_cast<float*>(ws);
+  // logits_i = H E_i^T (A = H [M,h] K-contig, B(k,n) = E_i[n, k] K-contig), reduced in
+  // the GEMM's epilogue to per-slot row statistics; the logits are never stored.
+  tps::GemmArgs g = make_args(H, h, E_i, h, M, V, h, stats, 0);
+  g.ce_targets = targets;
+  g.ce_lo = lo;
+  g.ce_tlogit = tlogit_i;
+  tps::gemm_bf16_sk_attach(g, static_cast<char*>(ws) + round256(ce_stats_bytes(M, V)));
+  TRY(hip_status(tps::gemm_bf16(g, true, true, tps::EPI_CE, st), fn));
+  return hip_status(
+      tps::ce_merge(stats, M, tps::ce_slots((int)V), targets, lo, V, rowmax_i, sumexp_i, tlogit_i, st), fn);
 }
 
 TP_API tp_status tp_vocab_ce_loss(int64_t M, const float* const* rowmax_parts, const float* const* sumexp_parts,

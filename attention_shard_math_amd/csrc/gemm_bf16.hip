@@ -263,6 +263,99 @@ __device__ __forceinline__ void store_tile(const f32x16 a, const GemmArgs& g, in
   store_tile_scalar<EPI>(a, g, row0, col);
 }
 
+// Reductions over the 16 lanes of each DPP row, every lane receiving the result:
+// exchange with lane ^ 1 and lane ^ 2 (quad permutes), then with the mirrored lane
+// of the half-row (i <-> 7 - i) and of the row (i <-> 15 - i). Each step combines
+// two equal partials in either order, so all 16 lanes hold the same bits.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_mov<kDppXor1>(x);
+  x += dpp_mov<kDppXor2>(x);
+  x += dpp_mov<kDppHalfMirror>(x);
+  return x + dpp_mov<kDppMirror>(x);
+}
+__device__ __forceinline__ float row16_max(float x) {
+  x = fmaxf(x, dpp_mov<kDppXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppHalfMirror>(x));
+  return fmaxf(x, dpp_mov<kDppMirror>(x));
+}
+
+// EPI_CE on one wave's 64 x 96 sub-tile at (r0, c0): the statistics of each row
+// over each of the block's two column slots. The 16 lanes of a DPP row hold one
+// row's values in a slot (lane l: row 8(e/4) + 4(l/32) + e%4 of each 32-row tile,
+// column l%32 of each 32-column tile), so the slot reductions never leave the row.
+// The exponentials are 2^(x log2(e) - max log2(e)) with the scaling in one fma
+// (v_exp_f32 computes 2^x). The one lane that holds a row's target column stores
+// its logit directly. WHOLE: every column of the block lies below N.
+template <bool WHOLE, int TM, int TN>
+__device__ __forceinline__ void ce_epilogue(const f32x16 (&acc)[TM][TN], const GemmArgs& g, int r0, int c0,
+                                            int lane) {
+  constexpr float kLog2e = 1.44269504088896340736f;
+  constexpr float kNegInf = -__builtin_huge_valf();
+  const int fk = lane >> 5, fr = lane & 31;
+  const int nslot = ce_slots(g.N), slot = 2 * (c0 / kCeBlock) + (fr >> 4);
+  f32x2* part = static_cast<f32x2*>(g.C);
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    int tc[16];  // the rows' target columns (-1: not in this slice), fetched together
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = r0 + i * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
+      const int64_t t = row < g.M ? (int64_t)g.ce_targets[row] - g.ce_lo : -1;
+      tc[e] = t >= 0 && t < g.N ? (int)t : -1;
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int row = r0 + i * 32 + 8 * (e >> 2) + 4 * fk + (e & 3);
+      float x[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) x[j] = WHOLE || c0 + j * 32 + fr < g.N ? acc[i][j][e] : kNegInf;
+      float mx = x[0];
+#pragma unroll
+      for (int j = 1; j < TN; ++j) mx = fmaxf(mx, x[j]);
+      mx = row16_max(mx);
+      // a slot with no column (only past N) has every x = -inf: scale by 0 instead
+      const float mb = WHOLE ? mx * kLog2e : (mx == kNegInf ? 0.f : mx * kLog2e);
+      float se = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) se += __builtin_amdgcn_exp2f(__builtin_fmaf(x[j], kLog2e, -mb));
+      se = row16_sum(se);
+      const int d = tc[e] - (c0 + fr);  // the target is this lane's column j when d == 32 j
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        if (d == 32 * j) g.ce_tlogit[row] = acc[i][j][e];
+      if ((lane & 15) == 0 && row < g.M) part[(int64_t)row * nslot + slot] = f32x2{mx, se};
+    }
+  }
+}
+
+// Epilogue of one wave's 64 x 96 sub-tile at (r0, c0): per 32 x 32 tile for the
+// stored epilogues, ce_epilogue for EPI_CE.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void epilogue(const f32x16 (&acc)[TM][TN], const GemmArgs& g, int r0, int c0, int lane) {
+  const int fk = lane >> 5, fr = lane & 31;
+  if constexpr (EPI == EPI_CE) {
+    static_assert(TN * 32 == kCeBlock, "one 96-column block per wave");
+    // whole: no column of the block lies past N (every block but a slice's last)
+    if (c0 + kCeBlock <= g.N)
+      ce_epilogue<true>(acc, g, r0, c0, lane);
+    else
+      ce_epilogue<false>(acc, g, r0, c0, lane);
+  } else {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        store_tile<EPI>(acc[i][j], g, r0 + i * 32 + 4 * fk, c0 + j * 32 + fr,
+                        r0 + i * 32 + 32 <= g.M && c0 + j * 32 + 32 <= g.N);
+  }
+}
+
 // ---------------------------------------------------------------- kernel
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3)))
@@ -401,12 +494,7 @@ void gemm_bf16_kernel(GemmArgs g) {
       slot = slot == NS - 1 ? 0 : slot + 1;
     }
     const int m0 = tile_m0(it), n0 = tile_n0(it);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        store_tile<EPI>(acc[i][j], g, m0 + am + i * 32 + 4 * fk, n0 + bn + j * 32 + fr,
-                        m0 + am + i * 32 + 32 <= g.M && n0 + bn + j * 32 + 32 <= g.N);
+    epilogue<EPI>(acc, g, m0 + am, n0 + bn, lane);
   }
 }
 
@@ -569,14 +657,7 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
             mine[((i * TN + j) * 4 + q) * 64 + lane] =
                 f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     }
-    if (!split) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          store_tile<EPI>(acc[i][j], g, m0 + am + i * 32 + 4 * fk, n0 + bn + j * 32 + fr,
-                          m0 + am + i * 32 + 32 <= g.M && n0 + bn + j * 32 + 32 <= g.N);
-    }
+    if (!split) epilogue<EPI>(acc, g, m0 + am, n0 + bn, lane);
     gs = ti * nk + ke;
   }
 }
@@ -621,13 +702,7 @@ __global__ __launch_bounds__(64 * NCW) void gemm_bf16_sk_fixup_kernel(GemmArgs g
   tile_rc(ti, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int am = wm * WTM, bn = wn * WTN;
-  const int fk = lane >> 5, fr = lane & 31;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-      store_tile<EPI>(acc[i][j], g, m0 + am + i * 32 + 4 * fk, n0 + bn + j * 32 + fr,
-                      m0 + am + i * 32 + 32 <= g.M && n0 + bn + j * 32 + 32 <= g.N);
+  epilogue<EPI>(acc, g, m0 + am, n0 + bn, lane);
 }
 
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
@@ -664,6 +739,7 @@ hipError_t gemm_bf16(const GemmArgs& g, bool a_kcontig, bool b_kcontig, int epi,
     if (epi == EPI_F32) return launch<BM, BN, true, false, EPI_F32>(g, s);
   } else if (a_kcontig && b_kcontig) {
     if (epi == EPI_DGELU) return launch<BM, BN, true, true, EPI_DGELU>(g, s);
+    if (epi == EPI_CE) return launch<BM, BN, true, true, EPI_CE>(g, s);
     if (epi == EPI_F32) return launch<BM, BN, true, true, EPI_F32>(g, s);
     if (epi == EPI_BF16) return launch<BM, BN, true, true, EPI_BF16>(g, s);
   } else if (!a_kcontig && !b_kcontig) {

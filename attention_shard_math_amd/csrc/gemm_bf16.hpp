@@ -6,7 +6,17 @@
 
 namespace tps {
 
-enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_GELU = 2, EPI_DGELU = 3 };
+enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_GELU = 2, EPI_DGELU = 3, EPI_CE = 4 };
+
+// Row statistics of the vocabulary-parallel cross-entropy kept by the EPI_CE
+// epilogue, per row and per column slot: the slot's maximum logit and the sum of
+// exp(logit - maximum) over the slot, as float32 (max, sum). A slot is half of a
+// wave's 96-column block: in block b (columns 96b .. 96b+95), slot 2b + g holds
+// the columns c with (c mod 32) / 16 == g. Columns at or beyond N are left out; a
+// slot with none holds (-inf, 0). The target's logit is stored to ce_tlogit[m]
+// for the rows whose target column lies in [0, N); other rows are not written.
+constexpr int kCeBlock = 96;
+__host__ __device__ inline int ce_slots(int N) { return 4 * (N / 192 + (N % 192 != 0)); }  // four per 192-wide tile
 
 // C(m, n) = sum_k A(m, k) B(k, n).
 //   A(m, k) = A[m * lda + k] when the A operand is K-contiguous, else A[k * lda + m].
@@ -15,6 +25,9 @@ enum Epilogue { EPI_F32 = 0, EPI_BF16 = 1, EPI_GELU = 2, EPI_DGELU = 3 };
 //            EPI_BF16  C bf16
 //            EPI_GELU  C bf16 = GeLU(acc); U (nullable) bf16 = acc
 //            EPI_DGELU C bf16 = acc * GeLU'(Uin)
+//            EPI_CE    C float32 [M][ce_slots(N)][2]: per row and column slot
+//                      (max, sum exp(acc - max)); ce_tlogit[m] = acc(m, targets[m] - ce_lo)
+//                      when that column lies in [0, N)
 struct GemmArgs {
   const uint16_t* A;
   const uint16_t* B;
@@ -29,6 +42,11 @@ struct GemmArgs {
   // half of the persistent grid, the k-stages are split evenly over the workgroups and
   // the split tiles' float32 partials go here (kSkBytes, see gemm_bf16_sk_attach).
   float* sk_part = nullptr;
+  // EPI_CE: row targets (vocabulary ids), the id of output column 0, and where the
+  // targets' logits go.
+  const int32_t* ce_targets = nullptr;
+  int64_t ce_lo = 0;
+  float* ce_tlogit = nullptr;
 };
 
 // Size of the stream-K area: two float32 256 x 192 tile slots per workgroup of the

@@ -9,13 +9,15 @@
 // and the combine forms sum_i s_i exp(m_i - m) with m = max_i m_i (the max is
 // one more all-reduce); in real arithmetic that equals the plain sum of exp.
 //
-// ce_rows: one wave per row, 16-byte loads strided over the lanes (each load
-// instruction reads 1 KiB of the row, four in flight per lane); each lane keeps
-// a running (max, rescaled sum) in float32, and the lanes' pairs are merged in a
-// fixed butterfly. It is HBM-bound: 4*V bytes read per row.
-// ce_loss: one workgroup; the partials are merged in rank order and the row
-// losses reduced through LDS in a fixed tree, so the scalar is reproducible.
+// The logits themselves are never stored: the logits GEMM's epilogue reduces each
+// row over each 48-column slot (half of a wave's 96-column block) to (slot max, sum
+// of exp relative to it) and stores the target logits of the rows whose target
+// lies in the slice; ce_merge combines a row's slots in a fixed order (one wave
+// per row) and zeroes the target logit of the other rows. ce_loss: one workgroup; the partials are merged
+// in rank order and the row losses reduced through LDS in a fixed tree, so the
+// scalar is reproducible.
 #include "common.hpp"
+#include "gemm_bf16.hpp"
 #include "vocab_ce.hpp"
 
 namespace tps {
@@ -30,45 +32,23 @@ __device__ __forceinline__ void absorb_max(float& m, float& acc, float mx) {
   }
 }
 
-__global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ logits, int64_t M, int V,
-                                                      const int32_t* __restrict__ targets, int64_t lo,
-                                                      float* __restrict__ rowmax, float* __restrict__ sumexp,
-                                                      float* __restrict__ tlogit) {
+// One wave per row; lane k merges slots k, k + 64, ... then the lanes' pairs are
+// merged in a fixed butterfly (lanes without values carry -inf, 0).
+__global__ __launch_bounds__(256) void ce_merge_kernel(const f32x2* __restrict__ part, int64_t M, int nslot,
+                                                       const int32_t* __restrict__ targets, int64_t lo, int64_t V,
+                                                       float* __restrict__ rowmax, float* __restrict__ sumexp,
+                                                       float* __restrict__ tlogit) {
   const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= M) return;  // whole wave
-  const float* r = logits + row * (int64_t)V;
+  const f32x2* r = part + row * (int64_t)nslot;
   float m = -__builtin_huge_valf(), acc = 0.f;
-  if ((V & 3) == 0) {  // rows start 16-byte aligned
-    const f32x4* r4 = reinterpret_cast<const f32x4*>(r);
-    const int n4 = V >> 2;
-    int i = lane;
-    // Four loads in flight per lane (one wave per row leaves few waves per SIMD
-    // to hide the latency).
-    for (; i + 192 < n4; i += 256) {
-      f32x4 x[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) x[u] = r4[i + 64 * u];
-      float mx = m;
-#pragma unroll
-      for (int u = 0; u < 4; ++u) mx = fmaxf(mx, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
-      absorb_max(m, acc, mx);
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-        acc += (expf(x[u][0] - m) + expf(x[u][1] - m)) + (expf(x[u][2] - m) + expf(x[u][3] - m));
-    }
-    for (; i < n4; i += 64) {
-      const f32x4 x = r4[i];
-      absorb_max(m, acc, fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
-      acc += (expf(x[0] - m) + expf(x[1] - m)) + (expf(x[2] - m) + expf(x[3] - m));
-    }
-  } else {
-    for (int i = lane; i < V; i += 64) {
-      absorb_max(m, acc, r[i]);
-      acc += expf(r[i] - m);
-    }
+  for (int k = lane; k < nslot; k += 64) {
+    const f32x2 x = r[k];
+    if (x[0] == -__builtin_huge_valf()) continue;  // a slot wholly past the slice's end
+    absorb_max(m, acc, x[0]);
+    acc += x[1] * expf(x[0] - m);
   }
-  // merge the lanes' pairs in a fixed butterfly (lanes without values carry -inf, 0)
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float mo = __shfl_xor(m, o), ao = __shfl_xor(acc, o);
@@ -79,8 +59,8 @@ __global__ __launch_bounds__(256) void ce_rows_kernel(const float* __restrict__ 
   if (lane == 0) {
     rowmax[row] = m;
     sumexp[row] = acc;
-    const int64_t t = targets[row];
-    tlogit[row] = (t >= lo && t < lo + V) ? r[t - lo] : 0.f;
+    const int64_t t = (int64_t)targets[row] - lo;
+    if (t < 0 || t >= V) tlogit[row] = 0.f;  // in the slice: stored by the GEMM's epilogue
   }
 }
 
@@ -111,12 +91,12 @@ __global__ __launch_bounds__(1024) void ce_loss_kernel(CeParts p, int n, int64_t
 
 }  // namespace
 
-hipError_t ce_rows(const float* logits, int64_t M, int V, const int32_t* targets, int64_t lo, float* rowmax,
-                   float* sumexp, float* tlogit, hipStream_t st) {
+hipError_t ce_merge(const float* part, int64_t M, int nslot, const int32_t* targets, int64_t lo, int64_t V,
+                    float* rowmax, float* sumexp, float* tlogit, hipStream_t st) {
   if (M <= 0) return hipSuccess;
   const int64_t blocks = (M + 3) / 4;
-  hipLaunchKernelGGL(ce_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, st, logits, M, V, targets, lo, rowmax,
-                     sumexp, tlogit);
+  hipLaunchKernelGGL(ce_merge_kernel, dim3((unsigned)blocks), dim3(256), 0, st, reinterpret_cast<const f32x2*>(part),
+                     M, nslot, targets, lo, V, rowmax, sumexp, tlogit);
   return hipGetLastError();
 }
 

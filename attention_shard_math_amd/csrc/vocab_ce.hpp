@@ -4,11 +4,13 @@
 #include <stdint.h>
 
 namespace tps {
-// Per row m of logits [M, V] (float32, row-major): rowmax[m] = max_n logits[m, n],
-// sumexp[m] = sum_n exp(logits[m, n] - rowmax[m]); tlogit[m] = logits[m, t - lo] when
-// lo <= t = targets[m] < lo + V, else 0.
-hipError_t ce_rows(const float* logits, int64_t M, int V, const int32_t* targets, int64_t lo, float* rowmax,
-                   float* sumexp, float* tlogit, hipStream_t st);
+// Merge of the per-slot row statistics that the logits GEMM's EPI_CE epilogue
+// leaves in part, float32 [M][nslot][2] (slot maximum, sum of exp relative to
+// it): rowmax[m] = max over slots, sumexp[m] = sum_k s_k exp(m_k - rowmax[m]);
+// tlogit[m] = 0 for the rows whose target lies outside [lo, lo + V) (the epilogue
+// has stored the others).
+hipError_t ce_merge(const float* part, int64_t M, int nslot, const int32_t* targets, int64_t lo, int64_t V,
+                    float* rowmax, float* sumexp, float* tlogit, hipStream_t st);
 
 constexpr int kCeMaxParts = 16;
 struct CeParts {

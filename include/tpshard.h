@@ -266,15 +266,20 @@ size_t tp_attn_bwd_workspace(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
  *  back to the vocabulary with the row-split word embedding) and 五、Cross-Entropy层
  *  (per-rank row sums of e = exp(logit), all-reduced into the softmax
  *  denominator, then each row's cross-entropy and the scalar sum)]:
- *   logits_i = H E_i^T                       -> float32 [M, hi-lo] in the workspace
+ *   logits_i = H E_i^T                       (float32, never stored)
  *   rowmax_i[m] = max_n logits_i[m, n]        -> float32 [M]
  *   sumexp_i[m] = sum_n exp(logits_i[m, n] - rowmax_i[m]) -> float32 [M]
  *   tlogit_i[m] = logits_i[m, t[m] - lo] if lo <= t[m] < hi, else 0 -> float32 [M]
  *   H [M,h] and E_i [hi-lo, h]: bf16; targets [M] int32 (device).
  *   The page's sum of e over the rank's columns is exp(rowmax_i) * sumexp_i: it is
  *   carried relative to the row maximum so that no logit overflows float32.
+ *   The GEMM's epilogue reduces each row over each 48-column slot to (max, sum of
+ *   exp) and stores the target logits; the slots are then merged in column order,
+ *   so the results are reproducible bit for bit.
  *   Requires 0 <= lo < hi, h and hi-lo multiples of 8, operands below 2 GiB.
- *   ws: at least tp_vocab_ce_workspace(M, h, lo, hi) bytes. */
+ *   ws: at least tp_vocab_ce_workspace(M, h, lo, hi) bytes (the slot statistics,
+ *   8 bytes per row and slot, four slots per 192 columns, and the GEMM's stream-K
+ *   area); its contents on return are unspecified. */
 tp_status tp_vocab_ce_partials(int64_t M, int64_t h, int64_t lo, int64_t hi, const void* H,
                                const void* E_i, const int32_t* targets, float* rowmax_i,
                                float* sumexp_i, float* tlogit_i, void* ws, size_t ws_bytes,

@@ -192,12 +192,14 @@ class TestValidation:
         assert e(P, 4, P, 0, 10, 8, MIS, None) == UNSUPPORTED
 
     def test_vocab_ce(self):
+        # per row, 8 bytes for each 48-column slot (four per 192-column tile), rounded
+        # up to 256 bytes, then the stream-K area when the logits GEMM uses one
         M, h, lo, hi = 16, 64, 40, 104
         need = lib.tp_vocab_ce_workspace(M, h, lo, hi)
-        assert need == M * (hi - lo) * 4 + SK_BYTES and need % 256 == 0
+        assert need == 512 + SK_BYTES and need % 256 == 0             # 16 rows x 4 slots
         assert lib.tp_vocab_ce_workspace(3, 64, 0, 8) == 256 + SK_BYTES
-        assert lib.tp_vocab_ce_workspace(2048, 12288, 0, 6144) == 2048 * 6144 * 4  # 256 tiles: no area
-        assert lib.tp_vocab_ce_workspace(2048, 12288, 0, 6288) == 2048 * 6288 * 4 + SK_BYTES  # 264 tiles
+        assert lib.tp_vocab_ce_workspace(2048, 12288, 0, 6144) == 2048 * 128 * 8  # 256 tiles: no area
+        assert lib.tp_vocab_ce_workspace(2048, 12288, 0, 6288) == 2048 * 132 * 8 + SK_BYTES  # 264 tiles
         assert lib.tp_vocab_ce_workspace(3, 64, 8, 8) == 0
         assert lib.tp_vocab_ce_workspace(3, 0, 0, 8) == 0
         c = lib.tp_vocab_ce_partials

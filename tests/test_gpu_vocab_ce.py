@@ -10,7 +10,7 @@ Tolerance: the inputs are bf16 and used exactly by both sides, and the GPU keeps
 every intermediate in float32 (logits accumulated over h terms, exp, the row
 sums, the rank sums, log). The expected error of a logit is about
 u32 * sqrt(h/2) of its row's scale (u32 = 2^-24, so ~5e-6 at h = 12288, logit
-sigma ~2.2); the bounds below leave a factor of >= 10: logits, row maxima and
+sigma ~2.2); the bounds below leave a factor of >= 10: row maxima and
 target logits 1e-4 absolute, the per-rank log-sum-exp 1e-4 absolute (a 1e-4
 relative bound on the sum of exp), row losses 2e-4 absolute, the scalar loss
 1e-5 relative.
@@ -57,7 +57,12 @@ def _assert_lse(m, s, sumexp_ref, what):
     np.testing.assert_allclose(g, np.log(sumexp_ref), rtol=0, atol=LSE_ATOL, err_msg=what)
 
 
-@pytest.mark.parametrize("M,h,v,N", [(300, 328, 2080, 4), (37, 64, 520, 1), (1, 8, 64, 8), (515, 256, 1536, 16)])
+# The logits GEMM reduces each 96-column block of a row in its epilogue. The cases
+# cover a slice ending inside a block (520 = 5 * 96 + 40), blocks wholly past the
+# slice's end (264 and 8 columns), stream-K with every tile split (37 x 520), and
+# 256 tiles that fill the grid (2048 x 6144: the tile kernel, no stream-K).
+@pytest.mark.parametrize("M,h,v,N", [(300, 328, 2080, 4), (37, 64, 520, 1), (1, 8, 64, 8), (515, 256, 1536, 16),
+                                     (100, 64, 528, 2), (2048, 64, 6144, 1)])
 def test_small_against_oracle(M, h, v, N):
     inp = ce_inputs(M, h, v, seed=4242 + M, sigma_h=1.0, sigma_w=0.3)
     t = inp["targets"].copy()
@@ -71,11 +76,9 @@ def test_small_against_oracle(M, h, v, N):
     for i in range(N):
         lo, hi = i * w, (i + 1) * w
         note(f"vocab_ce_partials M={M} h={h} slice [{lo},{hi}) of {v}")
-        m, s, tl, ws = _rank(Hd, Ed[lo:hi], td, lo, hi)
+        m, s, tl, _ = _rank(Hd, Ed[lo:hi], td, lo, hi)
         torch.cuda.synchronize()
         r = oracle.vocab_ce_partials(Ho, Eo[lo:hi], t, lo, hi)
-        logits = ws[:M * w * 4].view(torch.float32).view(M, w)
-        np.testing.assert_allclose(f64_host(logits), r["logits"], rtol=0, atol=LOGIT_ATOL)
         np.testing.assert_allclose(f64_host(m), r["logits"].max(axis=1), rtol=0, atol=LOGIT_ATOL)
         _assert_lse(m, s, r["sumexp"], "rank log-sum-exp")
         np.testing.assert_allclose(f64_host(tl), r["tlogit"], rtol=0, atol=LOGIT_ATOL)
@@ -169,7 +172,7 @@ def test_large_logits_do_not_overflow(M, h, v, N):
 
 def test_full_size_sampled_rows():
     """GPT-3 vocabulary (50304 = 8 x 6288), h = 12288, 2048 rows, all eight
-    slices run on the GPU; the oracle recomputes sampled rows' logits, then
+    slices run on the GPU; the oracle recomputes sampled rows' partial sums, then
     every row's partial sums and loss over the whole vocabulary."""
     c = CONFIGS["vocab_parallel_ce"]
     M, h, v, N = c["b"] * c["s"], c["h"], c["v"], c["N"]
@@ -177,13 +180,12 @@ def test_full_size_sampled_rows():
     t = inp["targets"]
     Hd, Ed, td = bf16_dev(inp["H"]), bf16_dev(inp["E"]), torch.from_numpy(t).to(DEV)
     w = v // N
-    ms, ss, ts, logit_rows = [], [], [], []
+    ms, ss, ts = [], [], []
     rows_s = np.array([0, 1, 777, 1500, M - 2, M - 1])
     rows_d = torch.from_numpy(rows_s).to(DEV)
     for i in range(N):
         note(f"vocab_ce_partials full size slice {i}/{N}")
-        m, s, tl, ws = _rank(Hd, Ed[i * w:(i + 1) * w], td, i * w, (i + 1) * w)
-        logit_rows.append(ws[:M * w * 4].view(torch.float32).view(M, w)[rows_d].cpu())
+        m, s, tl, _ = _rank(Hd, Ed[i * w:(i + 1) * w], td, i * w, (i + 1) * w)
         ms.append(m)
         ss.append(s)
         ts.append(tl)
@@ -194,8 +196,6 @@ def test_full_size_sampled_rows():
     refs = [oracle.vocab_ce_partials(Ho, bf16_bits_to_f64(inp["E"][i * w:(i + 1) * w]), t[rows_s], i * w,
                                      (i + 1) * w) for i in range(N)]
     for i in range(N):
-        np.testing.assert_allclose(logit_rows[i].numpy().astype(np.float64), refs[i]["logits"], rtol=0,
-                                   atol=LOGIT_ATOL)
         np.testing.assert_allclose(f64_host(ms[i])[rows_s], refs[i]["logits"].max(axis=1), rtol=0,
                                    atol=LOGIT_ATOL)
         _assert_lse(ms[i][rows_d], ss[i][rows_d], refs[i]["sumexp"], "sampled rows' log-sum-exp")
