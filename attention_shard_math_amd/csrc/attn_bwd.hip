@@ -39,6 +39,8 @@
 // LDS rows are 256 bytes (128 bf16); 16-byte chunk c of row r is stored at
 // c ^ swz(r), swz(r) = ((r & 7) << 1) | ((r >> 3) & 1), conflict-free for the
 // 16-row ds_read_b128 fragment reads and for the 4-row x 2-chunk transposing reads.
+#include <type_traits>
+
 #include "attn.hpp"
 #include "common.hpp"
 #include "gemm_bf16.hpp"
@@ -331,20 +333,29 @@ __device__ __forceinline__ void dkdv_item(int item, const uint16_t* __restrict__
       }
       const int key = kw + lr;
       float p[16], ds[16];
+      // P and dS. Causal: the mask is evaluated only where it can apply, when some
+      // key of the wave's 32 lies above a query of the block or past the sequence end
+      auto softmax = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 L = *reinterpret_cast<const float4*>(&sL[buf][8 * g + 4 * hh]);
-        const float4 Dd = *reinterpret_cast<const float4*>(&sDv[buf][8 * g + 4 * hh]);
-        const float Lv[4] = {L.x, L.y, L.z, L.w}, Dq[4] = {Dd.x, Dd.y, Dd.z, Dd.w};
+        for (int g = 0; g < 4; ++g) {
+          const float4 L = *reinterpret_cast<const float4*>(&sL[buf][8 * g + 4 * hh]);
+          const float4 Dd = *reinterpret_cast<const float4*>(&sDv[buf][8 * g + 4 * hh]);
+          const float Lv[4] = {L.x, L.y, L.z, L.w}, Dq[4] = {Dd.x, Dd.y, Dd.z, Dd.w};
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int e = 4 * g + c, q = q0 + 8 * g + 4 * hh + c;
-          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], scale_log2, -Lv[c]));
-          if ((CAUSAL && key > q) || key >= s) pv = 0.f;
-          p[e] = pv;
-          ds[e] = pv * (dP[e] - Dq[c]);
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * g + c, q = q0 + 8 * g + 4 * hh + c;
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], scale_log2, -Lv[c]));
+            if constexpr (decltype(masked)::value)
+              if ((CAUSAL && key > q) || key >= s) pv = 0.f;
+            p[e] = pv;
+            ds[e] = pv * (dP[e] - Dq[c]);
+          }
         }
-      }
+      };
+      if (!CAUSAL || kw + 31 > q0 || kw + 31 >= s)  // full attention keeps one path
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
       const bf16x8 pa[2] = {pack8(p), pack8(p + 8)};
       const bf16x8 sa[2] = {pack8(ds), pack8(ds + 8)};
       const bf16x8 pl[2] = {pack8_lo(p, pa[0]), pack8_lo(p + 8, pa[1])};
@@ -481,13 +492,21 @@ __device__ __forceinline__ void dq_item(int item, const uint16_t* __restrict__ q
         dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag_rows<D>(tv, 0, kk, lane), of[kk], dP, 0, 0, 0);
       }
       float ds[16];
+      // causal: the mask only where some key of the 32 lies above a query of the wave or past the end
+      auto softmax = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + 8 * (e >> 2) + 4 * hh + (e & 3);
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], scale_log2, -Lq));
-        if ((CAUSAL && key > qrow) || key >= s) pv = 0.f;
-        ds[e] = pv * (dP[e] - Dq);
-      }
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e], scale_log2, -Lq));
+          if constexpr (decltype(masked)::value)
+            if ((CAUSAL && key > qrow) || key >= s) pv = 0.f;
+          ds[e] = pv * (dP[e] - Dq);
+        }
+      };
+      if (!CAUSAL || k0 + 31 > qw || k0 + 31 >= s)  // full attention keeps one path
+        softmax(std::true_type{});
+      else
+        softmax(std::false_type{});
       const bf16x8 sa[2] = {pack8(ds), pack8(ds + 8)};
       const bf16x8 sl[2] = {pack8_lo(ds, sa[0]), pack8_lo(ds + 8, sa[1])};
 #pragma unroll
