@@ -115,47 +115,59 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
     // ---------------- loader waves ----------------
     const int ptid = tid - (NT - NP);
     // Range of one sequence's K (or V) rows: a load past the last key returns zeros.
+    // Each stage's descriptors start at its first key (the range shortened to
+    // match), so the per-thread offsets below stay fixed for the whole walk and a
+    // stage costs the loaders only scalar address arithmetic.
     const int seq_bytes = (s - 1) * (int)ld * 2 + D * 2;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + (int64_t)Hl * D), (short)0, seq_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + 2LL * Hl * D), (short)0, seq_bytes, 0x00020000);
     const int row_b = (int)ld * 2;
+    const char* kbase = reinterpret_cast<const char*>(Qg + (int64_t)Hl * D);
+    const char* vbase = reinterpret_cast<const char*>(Qg + 2LL * Hl * D);
+    auto rsrc_at = [&](const char* base, int kv0) __attribute__((always_inline)) {
+      return __builtin_amdgcn_make_buffer_rsrc((void*)(base + (int64_t)kv0 * row_b), (short)0,
+                                               seq_bytes - kv0 * row_b, 0x00020000);
+    };
+    // K: chunk c = ptid + p * NP is 16 bytes of key c / DCH, stored at [key][d] with
+    // the chunk swizzle. V: task (vd4, vg8) takes d = 4*vd4 .. 4*vd4+3 of the 8 keys
+    // that V^T chunk vg8 holds, keys 16*(vg8/2) + 4*(vg8%2) + {0..3, 8..11}.
+    const bool vtask = NVT == NP || ptid < NVT;
+    const int vd4 = ptid % (D / 4), vg8 = ptid / (D / 4);
+    int kg[KPER], kl[KPER], vg[8], vl[4];
+#pragma unroll
+    for (int p = 0; p < KPER; ++p) {
+      const int c = ptid + p * NP, key = c / DCH, ch = c % DCH;
+      kg[p] = key * row_b + ch * 16;
+      kl[p] = key * D + ((ch ^ swz_k<D>(key)) << 3);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      vg[kk] = (16 * (vg8 >> 1) + 4 * (vg8 & 1) + (kk & 3) + 8 * (kk >> 2)) * row_b + vd4 * 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = vd4 * 4 + r;
+      vl[r] = d * KVB + ((vg8 ^ swz_v(d)) << 3);
+    }
     u32x4 kreg[KPER];
     uint2 vreg[8];
     auto load_kv = [&](int kv0) __attribute__((always_inline)) {
-      const int pt = opaque(ptid);
+      const __amdgpu_buffer_rsrc_t rk = rsrc_at(kbase, kv0);
 #pragma unroll
-      for (int p = 0; p < KPER; ++p) {
-        const int c = pt + p * NP;
-        kreg[p] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (kv0 + c / DCH) * row_b + (c % DCH) * 16, 0, 0));
-      }
-      if (NVT == NP || pt < NVT) {
-        // Task (vd4, vg8): d = 4*vd4 .. 4*vd4+3 of the 8 keys that V^T chunk vg8 holds.
-        const int vd4 = pt % (D / 4), vg8 = pt / (D / 4);
-        const int vbase = (kv0 + 16 * (vg8 >> 1) + 4 * (vg8 & 1)) * row_b + vd4 * 8;
+      for (int p = 0; p < KPER; ++p)
+        kreg[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, kg[p], 0, 0));
+      if (vtask) {
+        const __amdgpu_buffer_rsrc_t rv = rsrc_at(vbase, kv0);
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
-          vreg[kk] = __builtin_bit_cast(
-              uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vbase + ((kk & 3) + 8 * (kk >> 2)) * row_b, 0, 0));
+          vreg[kk] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vg[kk], 0, 0));
       }
     };
     auto store_kv = [&](int buf) __attribute__((always_inline)) {
-      const int pt = opaque(ptid);
       uint16_t* sK = smem + buf * 2 * SK;
       uint16_t* sV = sK + SK;
 #pragma unroll
-      for (int p = 0; p < KPER; ++p) {
-        const int c = pt + p * NP, key = c / DCH, ch = c % DCH;
-        *reinterpret_cast<u32x4*>(sK + key * D + ((ch ^ swz_k<D>(key)) << 3)) = kreg[p];
-      }
-      if (NVT == NP || pt < NVT) {
-        const int vd4 = pt % (D / 4), vg8 = pt / (D / 4);
-        // V^T chunk vg8 of row d: keys 16*(vg8/2) + 4*(vg8%2) + {0..3, 8..11}.
+      for (int p = 0; p < KPER; ++p) *reinterpret_cast<u32x4*>(sK + kl[p]) = kreg[p];
+      if (vtask) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int d = vd4 * 4 + r;
           u32x4 w;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -163,7 +175,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
             const uint32_t b = (r < 2) ? vreg[2 * j + 1].x : vreg[2 * j + 1].y;
             w[j] = __builtin_amdgcn_perm(b, a, (r & 1) ? 0x07060302u : 0x05040100u);
           }
-          *reinterpret_cast<u32x4*>(sV + d * KVB + ((vg8 ^ swz_v(d)) << 3)) = w;
+          *reinterpret_cast<u32x4*>(sV + vl[r]) = w;
         }
       }
     };
@@ -372,43 +384,50 @@ __global__ __launch_bounds__(NT) void attn_fwd_wide_kernel(const uint16_t* __res
   if (wave >= 4) {
     // ---------------- loader waves ----------------
     const int ptid = tid - (NT - NP);
+    // As in attn_fwd_kernel: each stage's descriptors start at its first key, the
+    // per-thread offsets stay fixed. V is the chunk's 128 columns.
     const int seq_bytes = (s - 1) * (int)ld * 2 + D * 2;
-    const __amdgpu_buffer_rsrc_t rk =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + (int64_t)Hl * D), (short)0, seq_bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(Qg + 2LL * Hl * D + dc * DC), (short)0, seq_bytes - dc * DC * 2,
-                                          0x00020000);
     const int row_b = (int)ld * 2;
+    const char* kbase = reinterpret_cast<const char*>(Qg + (int64_t)Hl * D);
+    const char* vbase = reinterpret_cast<const char*>(Qg + 2LL * Hl * D + dc * DC);
+    const int vbytes = seq_bytes - dc * DC * 2;
+    const int vd4 = ptid % (DC / 4), vg8 = ptid / (DC / 4);
+    int kg[KPER], kl[KPER], vg[8], vl[4];
+#pragma unroll
+    for (int p = 0; p < KPER; ++p) {
+      const int c = ptid + p * NP, key = c / DCH, ch = c % DCH;
+      kg[p] = key * row_b + ch * 16;
+      kl[p] = key * D + ((ch ^ (key & 15)) << 3);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      vg[kk] = (16 * (vg8 >> 1) + 4 * (vg8 & 1) + (kk & 3) + 8 * (kk >> 2)) * row_b + vd4 * 8;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int d = vd4 * 4 + r;
+      vl[r] = d * KVB + ((vg8 ^ swz_v(d)) << 3);
+    }
     u32x4 kreg[KPER];
     uint2 vreg[8];
     auto load_kv = [&](int kv0) __attribute__((always_inline)) {
-      const int pt = opaque(ptid);
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(kbase + (int64_t)kv0 * row_b), (short)0, seq_bytes - kv0 * row_b, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(vbase + (int64_t)kv0 * row_b), (short)0, vbytes - kv0 * row_b, 0x00020000);
 #pragma unroll
-      for (int p = 0; p < KPER; ++p) {
-        const int c = pt + p * NP;
-        kreg[p] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, (kv0 + c / DCH) * row_b + (c % DCH) * 16, 0, 0));
-      }
-      const int vd4 = pt % (DC / 4), vg8 = pt / (DC / 4);
-      const int vbase = (kv0 + 16 * (vg8 >> 1) + 4 * (vg8 & 1)) * row_b + vd4 * 8;
+      for (int p = 0; p < KPER; ++p)
+        kreg[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, kg[p], 0, 0));
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk)
-        vreg[kk] = __builtin_bit_cast(
-            uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vbase + ((kk & 3) + 8 * (kk >> 2)) * row_b, 0, 0));
+        vreg[kk] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(rv, vg[kk], 0, 0));
     };
     auto store_kv = [&](int buf) __attribute__((always_inline)) {
-      const int pt = opaque(ptid);
       uint16_t* sK = smem + buf * (SKK + SVV);
       uint16_t* sV = sK + SKK;
 #pragma unroll
-      for (int p = 0; p < KPER; ++p) {
-        const int c = pt + p * NP, key = c / DCH, ch = c % DCH;
-        *reinterpret_cast<u32x4*>(sK + key * D + ((ch ^ (key & 15)) << 3)) = kreg[p];
-      }
-      const int vd4 = pt % (DC / 4), vg8 = pt / (DC / 4);
+      for (int p = 0; p < KPER; ++p) *reinterpret_cast<u32x4*>(sK + kl[p]) = kreg[p];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int d = vd4 * 4 + r;
         u32x4 w;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -416,7 +435,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_wide_kernel(const uint16_t* __res
           const uint32_t b = (r < 2) ? vreg[2 * j + 1].x : vreg[2 * j + 1].y;
           w[j] = __builtin_amdgcn_perm(b, a, (r & 1) ? 0x07060302u : 0x05040100u);
         }
-        *reinterpret_cast<u32x4*>(sV + d * KVB + ((vg8 ^ swz_v(d)) << 3)) = w;
+        *reinterpret_cast<u32x4*>(sV + vl[r]) = w;
       }
     };
     load_kv(0);
