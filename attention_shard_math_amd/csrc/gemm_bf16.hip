@@ -55,11 +55,16 @@ constexpr int kBM = 256, kBN = 192;     // tile of every product
 // for up to kSkMaxTiles tiles. With a fuller last round the split does not pay:
 // the GEMMs run power-limited, so the CUs that would idle mostly let the busy ones
 // clock higher, while the split adds the partials' traffic and a second kernel
-// (measured: a 192-tile product took 6% longer, a 264-tile one 5% less).
+// (measured: a 192-tile product took 6% longer, a 264-tile one 5% less). Nor does
+// it pay for tiles of fewer than kSkMinStages k-stages: a split tile's partials
+// (192 KB written and read back per piece) then cost as much traffic as its
+// operands (measured: the per-head [4096, 4096] score products of 384-wide heads,
+// 12 stages per tile, made the whole PaLM-shaped attention backward 5% slower).
 constexpr int kSkMaxTiles = 4096;
+constexpr int kSkMinStages = 48;
 __host__ __device__ constexpr bool sk_applies(int64_t tiles, int K) {
-  return K > 0 && tiles > 0 && tiles % kGrid != 0 && tiles % kGrid <= kGrid / 2 && tiles <= kSkMaxTiles &&
-         tiles * ((K + BK - 1) / BK) < (int64_t(1) << 30);
+  return K >= kSkMinStages * BK && tiles > 0 && tiles % kGrid != 0 && tiles % kGrid <= kGrid / 2 &&
+         tiles <= kSkMaxTiles && tiles * ((K + BK - 1) / BK) < (int64_t(1) << 30);
 }
 
 // s_waitcnt immediate that waits until at most n vector-memory operations are
@@ -685,19 +690,36 @@ __global__ __launch_bounds__(64 * NCW) void gemm_bf16_sk_fixup_kernel(GemmArgs g
   const f32x4* part = reinterpret_cast<const f32x4*>(g.sk_part);
   const int64_t wofs = (int64_t)wave * TM * TN * 4 * 64;
   f32x16 acc[TM][TN];
-  for (int u = vf; u <= vl; ++u) {
-    const f32x4* src = part + (2LL * u + (ti == u * per / nk ? 0 : 1)) * SLOT + wofs;
+  // Per row block i, the partials are loaded FG at a time before they are added, so
+  // a tile cut into many pieces waits for one load latency per group rather than
+  // per piece. The sum is still ((P_vf + P_vf+1) + ...) in run order.
+  constexpr int FG = 3;
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i)
+    for (int u0 = vf; u0 <= vl; u0 += FG) {
+      f32x4 x[FG][TN][4];
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
+      for (int gi = 0; gi < FG; ++gi)
+        if (u0 + gi <= vl) {
+          const int u = u0 + gi;
+          const f32x4* src = part + (2LL * u + (ti == u * per / nk ? 0 : 1)) * SLOT + wofs;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 x = src[((i * TN + j) * 4 + q) * 64 + lane];
+          for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[i][j][4 * q + r] = u == vf ? x[r] : acc[i][j][4 * q + r] + x[r];
+            for (int q = 0; q < 4; ++q) x[gi][j][q] = src[((i * TN + j) * 4 + q) * 64 + lane];
         }
-  }
+#pragma unroll
+      for (int gi = 0; gi < FG; ++gi)
+        if (u0 + gi <= vl) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                acc[i][j][4 * q + r] = u0 + gi == vf ? x[gi][j][q][r] : acc[i][j][4 * q + r] + x[gi][j][q][r];
+        }
+    }
   int tm, tn;
   tile_rc(ti, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;

@@ -62,24 +62,27 @@ class TestValidation:
         assert f(1, 1 << 31, 8, 8, P, P, None, P, 1, None, 0, None) == UNSUPPORTED  # too large
 
     def test_linear_workspace(self):
-        # 4 x 8 x 8: one tile, a nearly empty round: the stream-K area
-        assert lib.tp_linear_workspace(1, 4, 8, 8) == SK_BYTES
-        assert lib.tp_linear_workspace(0, 4, 8, 8) == 0                      # float32: never
+        # 4 x 1536 x 8: one tile of 48 k-stages, a nearly empty round: the stream-K area
+        assert lib.tp_linear_workspace(1, 4, 1536, 8) == SK_BYTES
+        assert lib.tp_linear_workspace(1, 4, 1528, 8) == 0                   # under 48 k-stages: never
+        assert lib.tp_linear_workspace(1, 4, 8, 8) == 0
+        assert lib.tp_linear_workspace(0, 4, 1536, 8) == 0                   # float32: never
         assert lib.tp_linear_workspace(1, 2048, 12288, 6144) == 0            # 256 tiles: one whole round
         assert lib.tp_linear_workspace(1, 2048, 18432, 9216) == SK_BYTES     # 384 tiles: 1.5 rounds
         assert lib.tp_linear_workspace(1, 4096, 18432, 9216) == 0            # 768 tiles: 3 rounds
         f = lib.tp_column_linear
         # a workspace is optional, but a given one must be large enough
-        assert f(1, 4, 8, 8, P, P, None, P, 1, P, SK_BYTES - 1, None) == WORKSPACE
+        assert f(1, 4, 1536, 8, P, P, None, P, 1, P, SK_BYTES - 1, None) == WORKSPACE
         assert "workspace" in _err()
-        assert f(1, 4, 8, 8, P, P, None, P, 1, MIS, SK_BYTES, None) == UNSUPPORTED
+        assert f(1, 4, 1536, 8, P, P, None, P, 1, MIS, SK_BYTES, None) == UNSUPPORTED
         r = lib.tp_row_linear
-        assert r(1, 4, 8, 8, P, P, P, P, SK_BYTES - 256, None) == WORKSPACE
+        assert r(1, 4, 1536, 8, P, P, P, P, SK_BYTES - 256, None) == WORKSPACE
         assert lib.tp_mlp_fwd_workspace(1, 2048, 12288, 6144) == 0
         assert lib.tp_mlp_fwd_workspace(1, 2048, 18432, 9216) == SK_BYTES
         assert lib.tp_mlp_fwd_workspace(0, 8, 64, 64) == 0
         m = lib.tp_mlp_fwd
-        assert m(1, 4, 16, 24, P, P, P, None, P, P, P, SK_BYTES - 1, None) == WORKSPACE
+        assert lib.tp_mlp_fwd_workspace(1, 4, 16, 24) == 0                  # under 48 k-stages
+        assert m(1, 4, 1536, 1536, P, P, P, None, P, P, P, SK_BYTES - 1, None) == WORKSPACE
 
     def test_operands_of_two_gib_are_rejected_before_any_launch(self):
         # [131072, 8192] bf16 is exactly 2 GiB: the kernels address operands with 32-bit offsets
@@ -104,11 +107,12 @@ class TestValidation:
         assert lib.tp_mlp_fwd(1, 4, 16, 20, P, P, P, None, P, P, None, 0, None) == UNSUPPORTED
 
     def test_mlp_bwd(self):
-        M, h, f = 32, 64, 128
+        M, h, f = 32, 1536, 1536
         need = lib.tp_mlp_bwd_workspace(M, h, f)
-        # dU, then the stream-K area (these products have fewer tiles than the grid)
+        # dU, then the stream-K area (these products have fewer tiles than the grid, and
+        # dU = dZ B_i^T and dX have 48 k-stages)
         assert need == M * f * 2 + SK_BYTES and need % 256 == 0
-        assert lib.tp_mlp_bwd_workspace(3, 8, 8) == 256 + SK_BYTES
+        assert lib.tp_mlp_bwd_workspace(3, 8, 8) == 256                     # under 48 k-stages: no area
         # 2048 x 6144 / 6144 x 12288 / 12288 x 6144 / 2048 x 12288 fill whole rounds: no area
         assert lib.tp_mlp_bwd_workspace(2048, 12288, 6144) == 2048 * 6144 * 2
         b = lib.tp_mlp_bwd
@@ -140,9 +144,11 @@ class TestValidation:
         assert lib.tp_attn_core(1, 16, 2, 96, 1, P, P, None) == UNSUPPORTED  # d_head
         assert lib.tp_attn_core(1, 16, 0, 128, 1, P, P, None) == INVALID
         assert lib.tp_attn_core(-1, 16, 2, 128, 1, P, P, None) == INVALID
-        ws = lib.tp_attn_fwd_workspace(2, 100, 256, 3, 64)
+        ws = lib.tp_attn_fwd_workspace(2, 100, 256, 3, 64)   # K = 256 and 192: no stream-K area
         assert ws == (2 * 100 * 9 * 64 * 2 + 2 * 100 * 3 * 64 * 2 + (-(2 * 100 * 9 * 64 * 2) % 256)
-                      + (-(2 * 100 * 3 * 64 * 2) % 256) + SK_BYTES)
+                      + (-(2 * 100 * 3 * 64 * 2) % 256))
+        assert lib.tp_attn_fwd_workspace(1, 100, 2048, 3, 64) == (
+            100 * 9 * 64 * 2 + (-(100 * 9 * 64 * 2) % 256) + 100 * 3 * 64 * 2 + (-(100 * 3 * 64 * 2) % 256) + SK_BYTES)
         # the GPT-3 shard's QKV (192 tiles) and Wo (512 tiles) products use no stream-K area
         t, w = 2048, 12 * 128
         assert lib.tp_attn_fwd_workspace(1, 2048, 12288, 12, 128) == t * 3 * w * 2 + t * w * 2
@@ -170,7 +176,10 @@ class TestValidation:
         need = lib.tp_attn_bwd_workspace(1, 64, 256, 2, 64)
         t, w = 64, 128
         assert need == (-(-t * w * 2 // 256) * 256 + -(-t * 3 * w * 2 // 256) * 256
-                        + -(-lib.tp_attn_core_bwd_workspace(1, 64, 2, 64) // 256) * 256 + SK_BYTES)
+                        + -(-lib.tp_attn_core_bwd_workspace(1, 64, 2, 64) // 256) * 256)  # no product has 48 k-stages
+        assert lib.tp_attn_bwd_workspace(1, 64, 2048, 2, 64) == (
+            -(-t * w * 2 // 256) * 256 + -(-t * 3 * w * 2 // 256) * 256
+            + -(-lib.tp_attn_core_bwd_workspace(1, 64, 2, 64) // 256) * 256 + SK_BYTES)  # dO = dOut Wo^T: K = 2048
         b = lib.tp_attn_bwd
         args = [P] * 10  # X, Wqkv_i, Wo_i, QKV, O, lse, dOut, dX_i, dWqkv_i, dWo_i
         assert b(1, 64, 256, 2, 64, 1, *args, P, need - 1, None) == WORKSPACE
@@ -196,8 +205,9 @@ class TestValidation:
         # up to 256 bytes, then the stream-K area when the logits GEMM uses one
         M, h, lo, hi = 16, 64, 40, 104
         need = lib.tp_vocab_ce_workspace(M, h, lo, hi)
-        assert need == 512 + SK_BYTES and need % 256 == 0             # 16 rows x 4 slots
-        assert lib.tp_vocab_ce_workspace(3, 64, 0, 8) == 256 + SK_BYTES
+        assert need == 512 and need % 256 == 0                        # 16 rows x 4 slots; h = 64: no stream-K
+        assert lib.tp_vocab_ce_workspace(3, 64, 0, 8) == 256
+        assert lib.tp_vocab_ce_workspace(16, 2048, lo, hi) == 512 + SK_BYTES
         assert lib.tp_vocab_ce_workspace(2048, 12288, 0, 6144) == 2048 * 128 * 8  # 256 tiles: no area
         assert lib.tp_vocab_ce_workspace(2048, 12288, 0, 6288) == 2048 * 132 * 8 + SK_BYTES  # 264 tiles
         assert lib.tp_vocab_ce_workspace(3, 64, 8, 8) == 0
