@@ -95,11 +95,22 @@ __device__ __forceinline__ int swk(int row) { return (row >> 2) & 3; }
 __device__ __forceinline__ int kc_off(int row, int c) { return row * BK + ((c ^ swk(row)) << 3); }
 
 // ---- MN-contiguous operand: LDS [k][r], R/8 chunks per k-row. Physical chunk =
-// logical chunk ^ (2 * (k & 3)), which spreads the 4 k-rows read by one 16-lane
-// group (and the 4 x 64 bytes read by 32 lanes) over distinct banks.
+// logical chunk ^ mn_swz<R>(k). A transposing fragment read serves 32 lanes at a
+// time: two 16-lane groups, each reading 32 bytes (2 chunks) of 4 consecutive
+// k-rows, 4 consecutive chunks in all. With R = 192 a k-row is 384 bytes, so
+// consecutive k-rows already fall half a bank line apart, and 2 * (k & 3) spreads
+// the rest over distinct banks. With R = 256 a k-row is 512 bytes, two whole bank
+// lines, so every k-row starts at the same bank. There 4 * (k & 3) places the 4
+// k-rows' chunk quads on the 4 quarters of the 256-byte line (2 * (k & 3) put two
+// k-rows on each chunk position: a 2-way conflict on every read, 0.8 conflict
+// cycles per LDS instruction on the products with an M-contiguous A).
+template <int R>
+__device__ __forceinline__ int mn_swz(int k) {
+  return (R % 256 == 0) ? (k & 3) << 2 : (k & 3) << 1;
+}
 template <int R>
 __device__ __forceinline__ int mn_off(int k, int r) {
-  return k * R + ((((r >> 3) ^ ((k & 3) << 1))) << 3) + (r & 7);
+  return k * R + (((r >> 3) ^ mn_swz<R>(k)) << 3) + (r & 7);
 }
 
 // Issues the DMA of one stage of one operand. R = tile rows (M or N extent).
@@ -121,7 +132,8 @@ struct Dma {
         base[o] = (row0 + r < rows) ? (uint32_t)((int64_t)(row0 + r) * ld + kc * 8) : kOOB;
       } else {
         constexpr int CPR = R / 8;  // chunks per k-row
-        const int k = q / CPR, c = (q % CPR) ^ ((k & 3) << 1);
+        static_assert(R % 256 == 0 || R % 64 == 0, "chunk swizzle must stay inside the k-row");
+        const int k = q / CPR, c = (q % CPR) ^ mn_swz<R>(k);
         kofs[o] = k;
         base[o] = (row0 + c * 8 < rows) ? (uint32_t)((int64_t)k * ld + row0 + c * 8) : kOOB;
       }
