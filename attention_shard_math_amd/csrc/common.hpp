@@ -1,5 +1,6 @@
 // Device helpers shared by the gfx950 kernels of libtpshard: vector types,
-// bfloat16 conversion, the erf-form GeLU and its derivative.
+// bfloat16 conversion, the erf-form GeLU and its derivative (with the device erff
+// for float32 results, and from a published erfc fit for results rounded to bf16).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -40,6 +41,42 @@ __device__ __forceinline__ float gelu_erf_prime(float u) {
   const float cdf = 0.5f * (1.0f + erff(u * 0.70710678118654752440f));
   const float pdf = 0.39894228040143267794f * __expf(-0.5f * u * u);
   return cdf + u * pdf;
+}
+
+// Phi(u) and exp(-u^2/2) for epilogues whose results are rounded to bf16, from the
+// rational-exponential fit of erfc in Abramowitz and Stegun, Handbook of Mathematical
+// Functions, formula 7.1.26 (after Hastings): for x >= 0 and t = 1 / (1 + p x),
+// erfc(x) = t (a1 + t (a2 + t (a3 + t (a4 + t a5)))) exp(-x^2) + e(x) with |e| <= 1.5e-7.
+// With x = |u| / sqrt 2, exp(-x^2) = exp(-u^2/2); the coefficients below are the published
+// a1..a5 halved, so the product is erfc(x) / 2 = Phi(-|u|). Phi(u) takes that value for
+// u < 0 (the tail without cancellation) and 1 minus it otherwise. Evaluated in float32
+// the error on Phi stays under 3e-7 (0.75e-7 from the fit, the rest from rounding in
+// the alternating sum near u = 0), far below the bf16 rounding of what the epilogues
+// store (2^-9 relative).
+struct PhiExp {
+  float phi;  // Phi(u)
+  float e;    // exp(-u^2 / 2)
+};
+__device__ __forceinline__ PhiExp phi_as7126(float u) {
+  const float x = fabsf(u) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float q = fmaf(t, 0.5307027145f, -0.7265760135f);
+  q = fmaf(t, q, 0.7107068705f);
+  q = fmaf(t, q, -0.142248368f);
+  q = fmaf(t, q, 0.127414796f);
+  const float e = __builtin_amdgcn_exp2f((x * -1.44269504088896340736f) * x);
+  const float h = (q * t) * e;
+  return PhiExp{u < 0.0f ? h : 1.0f - h, e};
+}
+
+// GeLU(u) = u Phi(u) and GeLU'(u) = Phi(u) + u phi(u), phi(u) = exp(-u^2/2) / sqrt(2 pi),
+// from phi_as7126: for results rounded to bf16.
+__device__ __forceinline__ float gelu_bf16out(float u) {
+  return u * phi_as7126(u).phi;
+}
+__device__ __forceinline__ float gelu_prime_bf16out(float u) {
+  const PhiExp p = phi_as7126(u);
+  return fmaf(u * 0.39894228040143267794f, p.e, p.phi);
 }
 
 }  // namespace tps

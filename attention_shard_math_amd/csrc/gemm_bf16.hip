@@ -205,11 +205,11 @@ __device__ __forceinline__ void store_tile_scalar(const f32x16 a, const GemmArgs
     } else if constexpr (EPI == EPI_BF16) {
       static_cast<uint16_t*>(g.C)[o] = (uint16_t)f32_to_bf16_bits(x);
     } else if constexpr (EPI == EPI_GELU) {
-      static_cast<uint16_t*>(g.C)[o] = (uint16_t)f32_to_bf16_bits(gelu_erf(x));
+      static_cast<uint16_t*>(g.C)[o] = (uint16_t)f32_to_bf16_bits(gelu_bf16out(x));
       if (g.U) g.U[(int64_t)row * g.ldu + col] = (uint16_t)f32_to_bf16_bits(x);
     } else {  // EPI_DGELU
       const float u = bf16_bits_to_f32(g.Uin[(int64_t)row * g.ldu + col]);
-      static_cast<uint16_t*>(g.C)[o] = (uint16_t)f32_to_bf16_bits(x * gelu_erf_prime(u));
+      static_cast<uint16_t*>(g.C)[o] = (uint16_t)f32_to_bf16_bits(x * gelu_prime_bf16out(u));
     }
   }
 }
@@ -264,11 +264,11 @@ __device__ __forceinline__ void store_tile(const f32x16 a, const GemmArgs& g, in
           const uint2 uu = *reinterpret_cast<const uint2*>(g.Uin + (int64_t)row * g.ldu + c4);
           const float u0 = bf16_bits_to_f32(uu.x & 0xffffu), u1 = bf16_bits_to_f32(uu.x >> 16);
           const float u2 = bf16_bits_to_f32(uu.y & 0xffffu), u3 = bf16_bits_to_f32(uu.y >> 16);
-          *dst = uint2{pack_bf16x2(w[0] * gelu_erf_prime(u0), w[1] * gelu_erf_prime(u1)),
-                       pack_bf16x2(w[2] * gelu_erf_prime(u2), w[3] * gelu_erf_prime(u3))};
+          *dst = uint2{pack_bf16x2(w[0] * gelu_prime_bf16out(u0), w[1] * gelu_prime_bf16out(u1)),
+                       pack_bf16x2(w[2] * gelu_prime_bf16out(u2), w[3] * gelu_prime_bf16out(u3))};
         } else if constexpr (EPI == EPI_GELU) {
-          store_nt(reinterpret_cast<uint16_t*>(dst), pack_bf16x2(gelu_erf(w[0]), gelu_erf(w[1])),
-                   pack_bf16x2(gelu_erf(w[2]), gelu_erf(w[3])));
+          store_nt(reinterpret_cast<uint16_t*>(dst), pack_bf16x2(gelu_bf16out(w[0]), gelu_bf16out(w[1])),
+                   pack_bf16x2(gelu_bf16out(w[2]), gelu_bf16out(w[3])));
           if (g.U) store_nt(g.U + (int64_t)row * g.ldu + c4, pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]));
         } else {
           store_nt(reinterpret_cast<uint16_t*>(dst), pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]));
