@@ -68,12 +68,6 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
-// Two floats -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t cvt_bf16x2(float lo, float hi) {
-  typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
-  const bf2 v = {(__bf16)lo, (__bf16)hi};
-  return __builtin_bit_cast(uint32_t, v);
-}
 // Returns x unchanged but hides its value from the optimizer, so address math
 // built on it is redone where used instead of occupying registers throughout.
 __device__ __forceinline__ int opaque(int x) {
@@ -286,9 +280,9 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w], scale_log2, -mref));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w + 1], scale_log2, -mref));
             rs += p0 + p1;
-            u[w] = cvt_bf16x2(p0, p1);
+            u[w] = pack_bf16x2(p0, p1);
             if constexpr (SPLIT)
-              ul[w] = cvt_bf16x2(p0 - bf16_bits_to_f32(u[w] & 0xffffu), p1 - bf16_bits_to_f32(u[w] >> 16));
+              ul[w] = pack_bf16x2(p0 - bf16_bits_to_f32(u[w] & 0xffffu), p1 - bf16_bits_to_f32(u[w] >> 16));
           }
           pb[t][s2] = __builtin_bit_cast(bf16x8, u);
           if constexpr (SPLIT) pl[t][s2] = __builtin_bit_cast(bf16x8, ul);
@@ -332,8 +326,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 u;
-        u.x = cvt_bf16x2(ot[i][4 * g] * inv, ot[i][4 * g + 1] * inv);
-        u.y = cvt_bf16x2(ot[i][4 * g + 2] * inv, ot[i][4 * g + 3] * inv);
+        u.x = pack_bf16x2(ot[i][4 * g] * inv, ot[i][4 * g + 1] * inv);
+        u.y = pack_bf16x2(ot[i][4 * g + 2] * inv, ot[i][4 * g + 3] * inv);
         *reinterpret_cast<uint2*>(orow + 32 * i + 8 * g + 4 * hh2) = u;
       }
   }
@@ -522,9 +516,9 @@ __global__ __launch_bounds__(NT) void attn_fwd_wide_kernel(const uint16_t* __res
             const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w], scale_log2, -mref));
             const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * s2 + 2 * w + 1], scale_log2, -mref));
             rs += p0 + p1;
-            u[w] = cvt_bf16x2(p0, p1);
+            u[w] = pack_bf16x2(p0, p1);
             if constexpr (SPLIT)
-              ul[w] = cvt_bf16x2(p0 - bf16_bits_to_f32(u[w] & 0xffffu), p1 - bf16_bits_to_f32(u[w] >> 16));
+              ul[w] = pack_bf16x2(p0 - bf16_bits_to_f32(u[w] & 0xffffu), p1 - bf16_bits_to_f32(u[w] >> 16));
           }
           pb[t][s2] = __builtin_bit_cast(bf16x8, u);
           if constexpr (SPLIT) pl[t][s2] = __builtin_bit_cast(bf16x8, ul);
@@ -559,8 +553,8 @@ __global__ __launch_bounds__(NT) void attn_fwd_wide_kernel(const uint16_t* __res
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 u;
-        u.x = cvt_bf16x2(ot[i][4 * g] * inv, ot[i][4 * g + 1] * inv);
-        u.y = cvt_bf16x2(ot[i][4 * g + 2] * inv, ot[i][4 * g + 3] * inv);
+        u.x = pack_bf16x2(ot[i][4 * g] * inv, ot[i][4 * g + 1] * inv);
+        u.y = pack_bf16x2(ot[i][4 * g + 2] * inv, ot[i][4 * g + 3] * inv);
         *reinterpret_cast<uint2*>(orow + 32 * i + 8 * g + 4 * hh2) = u;
       }
   }

@@ -83,18 +83,12 @@ __device__ __forceinline__ bf16x8 frag_tr(const uint16_t* t, int kb, int nb, int
   return __builtin_bit_cast(bf16x8, v);
 }
 
-// Two floats to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t cvt2(float a, float b) {
-  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-  const bf16x2 v = {(__bf16)a, (__bf16)b};
-  return __builtin_bit_cast(uint32_t, v);
-}
 
 // Score registers e0..e0+7 as a bf16 k-operand.
 __device__ __forceinline__ bf16x8 pack8(const float* v) {
   u32x4 u;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) u[w] = cvt2(v[2 * w], v[2 * w + 1]);
+  for (int w = 0; w < 4; ++w) u[w] = pack_bf16x2(v[2 * w], v[2 * w + 1]);
   return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -104,7 +98,7 @@ __device__ __forceinline__ bf16x8 pack8_lo(const float* v, bf16x8 hi) {
   u32x4 u;
 #pragma unroll
   for (int w = 0; w < 4; ++w)
-    u[w] = cvt2(v[2 * w] - bf16_bits_to_f32(h[w] & 0xffffu), v[2 * w + 1] - bf16_bits_to_f32(h[w] >> 16));
+    u[w] = pack_bf16x2(v[2 * w] - bf16_bits_to_f32(h[w] & 0xffffu), v[2 * w + 1] - bf16_bits_to_f32(h[w] >> 16));
   return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -215,8 +209,8 @@ __device__ __forceinline__ void combine_part(const float* __restrict__ part, uin
     f32x4 a = *reinterpret_cast<const f32x4*>(pb + (int64_t)v * 4);
     for (int c = 1; c < nc; ++c) a = a + *reinterpret_cast<const f32x4*>(pb + (int64_t)c * R * D + v * 4);
     uint2 u;
-    u.x = cvt2(a[0] * scale, a[1] * scale);
-    u.y = cvt2(a[2] * scale, a[3] * scale);
+    u.x = pack_bf16x2(a[0] * scale, a[1] * scale);
+    u.y = pack_bf16x2(a[2] * scale, a[3] * scale);
     *reinterpret_cast<uint2*>(out + ((int64_t)bi * s + row) * ld + (int64_t)(col_block * Hl + head) * D + d) = u;
   }
 }
@@ -549,8 +543,8 @@ __device__ __forceinline__ void dq_item(int item, const uint16_t* __restrict__ q
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         uint2 u;
-        u.x = cvt2(dq[i][4 * g] * scale, dq[i][4 * g + 1] * scale);
-        u.y = cvt2(dq[i][4 * g + 2] * scale, dq[i][4 * g + 3] * scale);
+        u.x = pack_bf16x2(dq[i][4 * g] * scale, dq[i][4 * g + 1] * scale);
+        u.y = pack_bf16x2(dq[i][4 * g + 2] * scale, dq[i][4 * g + 3] * scale);
         *reinterpret_cast<uint2*>(dQg + 32 * i + 8 * g + 4 * hh) = u;
       }
   }
@@ -669,9 +663,9 @@ __global__ __launch_bounds__(256) void p_split_kernel(const float* __restrict__ 
 #pragma unroll
     for (int e = 0; e < 4; ++e)
       p[e] = (CAUSAL && k + e > q) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -L));
-    const uint32_t h0 = cvt2(p[0], p[1]), h1 = cvt2(p[2], p[3]);
-    const uint32_t l0 = cvt2(p[0] - bf16_bits_to_f32(h0 & 0xffffu), p[1] - bf16_bits_to_f32(h0 >> 16));
-    const uint32_t l1 = cvt2(p[2] - bf16_bits_to_f32(h1 & 0xffffu), p[3] - bf16_bits_to_f32(h1 >> 16));
+    const uint32_t h0 = pack_bf16x2(p[0], p[1]), h1 = pack_bf16x2(p[2], p[3]);
+    const uint32_t l0 = pack_bf16x2(p[0] - bf16_bits_to_f32(h0 & 0xffffu), p[1] - bf16_bits_to_f32(h0 >> 16));
+    const uint32_t l1 = pack_bf16x2(p[2] - bf16_bits_to_f32(h1 & 0xffffu), p[3] - bf16_bits_to_f32(h1 >> 16));
     *reinterpret_cast<uint2*>(Pst + (int64_t)q * s + k) = uint2{h0, h1};
     *reinterpret_cast<uint2*>(Pst + ((int64_t)s + q) * s + k) = uint2{l0, l1};
   }
@@ -695,9 +689,9 @@ __global__ __launch_bounds__(256) void ds_split_kernel(const float* __restrict__
     float g[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) g[e] = p[e] * (x[e] - D) * scale;
-    const uint32_t h0 = cvt2(g[0], g[1]), h1 = cvt2(g[2], g[3]);
-    const uint32_t l0 = cvt2(g[0] - bf16_bits_to_f32(h0 & 0xffffu), g[1] - bf16_bits_to_f32(h0 >> 16));
-    const uint32_t l1 = cvt2(g[2] - bf16_bits_to_f32(h1 & 0xffffu), g[3] - bf16_bits_to_f32(h1 >> 16));
+    const uint32_t h0 = pack_bf16x2(g[0], g[1]), h1 = pack_bf16x2(g[2], g[3]);
+    const uint32_t l0 = pack_bf16x2(g[0] - bf16_bits_to_f32(h0 & 0xffffu), g[1] - bf16_bits_to_f32(h0 >> 16));
+    const uint32_t l1 = pack_bf16x2(g[2] - bf16_bits_to_f32(h1 & 0xffffu), g[3] - bf16_bits_to_f32(h1 >> 16));
     *reinterpret_cast<uint2*>(dSr + (int64_t)q * s + k) = uint2{h0, h1};
     *reinterpret_cast<uint2*>(dSr + ((int64_t)s + q) * s + k) = uint2{l0, l1};
     *reinterpret_cast<uint2*>(dSc + (int64_t)q * 2 * s + k) = uint2{h0, h1};

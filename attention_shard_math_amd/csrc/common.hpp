@@ -14,21 +14,21 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// float32 -> bfloat16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+// float32 -> bfloat16 bits with gfx950's v_cvt_pk_bf16_f32: round to nearest, ties to
+// even; a NaN stays a NaN.
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
   return __uint_as_float(b << 16);
 }
 
-// Two floats -> packed bf16 pair (lo in bits 0..15).
+// Two floats -> packed bf16 pair (lo in bits 0..15), one v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // GeLU(u) = u * Phi(u) = 0.5 u (1 + erf(u / sqrt 2)), with the device erff.
