@@ -469,17 +469,6 @@ TP_API tp_status tp_attn_fwd_train(int64_t b, int64_t s, int64_t h, int64_t n_he
   return ok();
 }
 
-namespace {
-// The backward of 384-wide heads runs per-head products whose [2s, s] operands
-// are read 16 bytes at a time: s must be a multiple of 8, and 4 s^2 bytes below 2 GiB.
-tp_status check_wide_bwd(const char* fn, int64_t s, int64_t d) {
-  if (d == 384 && (s % 8 != 0 || 4 * s * s >= ((int64_t)1 << 31) - 16))
-    return fail(TP_ERR_UNSUPPORTED, "%s: with d_head 384 the backward needs s %% 8 == 0 and s <= 23170 (got s=%lld)",
-                fn, (long long)s);
-  return TP_OK;
-}
-}  // namespace
-
 TP_API size_t tp_attn_core_bwd_workspace(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head) {
   if (b <= 0 || s <= 0 || n_heads_local <= 0) return 0;
   if (b * s > kMaxDim || n_heads_local > kMaxDim) return 0;
@@ -493,7 +482,6 @@ TP_API tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, i
                                   void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "tp_attn_core_bwd";
   TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
-  TRY(check_wide_bwd(fn, s, d_head));
   if (b * s == 0) return ok();
   TRY(check_ptr(fn, "QKV", QKV));
   TRY(check_ptr(fn, "O", O));
@@ -533,7 +521,6 @@ TP_API tp_status tp_attn_bwd(int64_t b, int64_t s, int64_t h, int64_t n_heads_lo
                              size_t ws_bytes, void* stream) {
   const char* fn = "tp_attn_bwd";
   TRY(check_attn_shape(fn, b, s, n_heads_local, d_head));
-  TRY(check_wide_bwd(fn, s, d_head));
   TRY(check_dims(fn, b * s, h, 3 * n_heads_local * d_head));
   TRY(check_ptr(fn, "dWqkv_i", dWqkv_i));
   TRY(check_ptr(fn, "dWo_i", dWo_i));

@@ -36,14 +36,17 @@
 // entries, which keeps the weight gradients formed from them (X^T dQKV over
 // thousands of tokens) within the bf16 bar.
 //
-// LDS rows are 256 bytes (128 bf16); 16-byte chunk c of row r is stored at
-// c ^ swz(r), swz(r) = ((r & 7) << 1) | ((r >> 3) & 1), conflict-free for the
-// 16-row ds_read_b128 fragment reads and for the 4-row x 2-chunk transposing reads.
+// LDS rows hold one head's d columns; 16-byte chunk c of row r is stored at
+// c ^ swz(r), swz(r) = ((r & 7) << 1) | ((r >> 3) & 1) (for 384-wide rows inside
+// each group of 16 chunks), conflict-free for the 16-row ds_read_b128 fragment
+// reads and for the 4-row x 2-chunk transposing reads.
+//
+// Heads of d = 384 take the same walks with the work of a step split over four
+// waves (see dkdv_wide_item).
 #include <type_traits>
 
 #include "attn.hpp"
 #include "common.hpp"
-#include "gemm_bf16.hpp"
 
 
 namespace tps {
@@ -60,7 +63,10 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 
 // for transposing reads; any c inside its 16-byte chunk).
 template <int D>
 __device__ __forceinline__ int toff(int r, int c) {
-  return r * D + ((((c >> 3) ^ swz(r)) & (D / 8 - 1)) << 3) + (c & 7);
+  if constexpr (D == 384)  // 48 chunks a row: the xor (< 16) stays inside each group of 16
+    return r * D + (((c >> 3) ^ swz(r)) << 3) + (c & 7);
+  else
+    return r * D + ((((c >> 3) ^ swz(r)) & (D / 8 - 1)) << 3) + (c & 7);
 }
 
 // ds_read_b128 fragment: lane gets row rb + l%32, columns 16kk + 8(l/32) .. +8.
@@ -626,115 +632,514 @@ hipError_t launch_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO
 }
 
 // ------------------------------------------------------------------ wide heads
-// Heads of d = 384 run the backward as per-head products on the bf16 GEMM: a
-// fused walk would need the K and V fragments of its keys over all 384 d
-// (192 registers per lane) next to its dK and dV accumulators. Per sequence and
-// head, with S and dP held in a float32 [s, s] buffer:
-//   S = Q K^T; P = exp(S / sqrt(d) - lse) (0 above the diagonal), as hi and lo
-//   bf16 halves; dV = [P_hi; P_lo]^T [dO; dO] (the pair as one product of depth
-//   2s); dP = dO V^T; dS = (P_hi + P_lo)(dP - D) / sqrt(d) as hi and lo halves;
-//   dK = [dS_hi; dS_lo]^T [Q; Q]; dQ = [dS_hi | dS_lo] [K; K].
-// The products of depth 2s have few output tiles (s/256 x 2 at s = 4096), so they
-// run stream-K over all workgroups.
+// Heads of d = 384 walk the same way, but one wave cannot hold the K and V
+// fragments of 32 keys over all 384 d (192 registers per lane) next to 384-wide
+// dK and dV accumulators. A workgroup of four waves takes a block of 64 keys
+// (dK/dV walk) or 64 queries (dQ walk), two halves of 32, and each step's work
+// splits two ways:
+//   * scores: wave h (h = 0, 1) forms S for half h over all d from fragments it
+//     holds for the whole walk (K for the dK/dV walk, Q for the dQ walk), wave
+//     2 + h forms dP for half h (from V, or dO); the S wave turns S into P and
+//     hands it through LDS to the dP wave of its half, which forms dS; both
+//     leave their bf16 hi/lo operand fragments in LDS;
+//   * products: wave w accumulates the d columns [96w, 96w + 96) of the
+//     gradients of both halves from those fragments and the staged tile.
+// Three barriers a step: P ready, dS ready, next tile staged. A half whose
+// keys all lie above the step's queries (or past the end) is skipped by every
+// wave. Walks are cut into chunks as above, and combine_kernel adds the
+// chunks' partials.
 constexpr int kWideD = 384;
+constexpr int kWideTileB = 32 * kWideD * 2;             // bytes of a [32][384] bf16 tile
+constexpr int kWideOffB = 2 * kWideTileB;               // second pair of tiles (dO or V)
+constexpr int kWideOffXP = 4 * kWideTileB;              // P, float32 [half][4][lane] x4
+constexpr int kWideOffXPb = kWideOffXP + 2 * 4 * 64 * 16;   // P hi/lo fragments [half][4][lane]
+constexpr int kWideOffXSb = kWideOffXPb + 2 * 4 * 64 * 16;  // dS hi/lo fragments [half][4][lane]
+constexpr int kWideOffL = kWideOffXSb + 2 * 4 * 64 * 16;    // lse (log2 units) and D [2][64]
+constexpr int kWideLds = kWideOffL + 2 * 64 * 4;            // 123392 bytes
 
-// dst [2*rows, D] = [src; src] for one head's [rows, D] slice of a row-major tensor
-// with leading dimension ld (elements).
-__global__ __launch_bounds__(256) void stack2_kernel(const uint16_t* __restrict__ src, int64_t ld, int rows,
-                                                     uint16_t* __restrict__ dst) {
-  constexpr int CPR = kWideD / 8;
-  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (v >= (int64_t)rows * CPR) return;
-  const int64_t r = v / CPR, c = v % CPR;
-  const u32x4 x = *reinterpret_cast<const u32x4*>(src + r * ld + c * 8);
-  *reinterpret_cast<u32x4*>(dst + r * kWideD + c * 8) = x;
-  *reinterpret_cast<u32x4*>(dst + (r + rows) * kWideD + c * 8) = x;
+// Block rows are 64 (two halves of 32) in both wide walks.
+constexpr int kWideR = 64;
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+constexpr uint32_t kDmaOOB = 0x7ffffff0u;  // buffer offset past every range: reads as zero
+
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 
-// P from the scores: Pst rows [0, s) hold bf16(P), rows [s, 2s) bf16(P - bf16(P)).
+// Rows [r0, r0 + 32) of one head's 384 columns of a [rows][ld] bf16 tensor,
+// straight from memory into a swizzled [32][384] LDS tile with
+// buffer_load_dwordx4 ... lds (rows at or past `rows` read as zero). Wave w of
+// four issues 6 of the tile's 24 1-KB pieces; physical chunk P of the tile (row
+// P / 48, position P % 48) receives logical chunk (P % 48) ^ swz(row). The loads
+// complete asynchronously: s_waitcnt vmcnt(0) before the barrier that publishes
+// the tile. Issued as inline asm (no register outputs), so the compiler does
+// not wait for them before unrelated LDS reads.
+__device__ __forceinline__ void dma_tile384(const uint16_t* g, int64_t ld, int r0, int rows, uint16_t* tile,
+                                            int wave, int lane) {
+  const uint64_t a = reinterpret_cast<uint64_t>(g + (int64_t)r0 * ld);
+  const i32x4 rs = {(int)(uint32_t)a, (int)((a >> 32) & 0xffff), (int)(uint32_t)(32 * ld * 2), 0x00020000};
+  const uint32_t base = lds_u32(tile);
+#pragma unroll
+  for (int o = 0; o < 6; ++o) {
+    const int P = (wave * 6 + o) * 64 + lane, r = P / 48, c = (P % 48) ^ swz(r);
+    const uint32_t off = (r0 + r < rows) ? (uint32_t)(r * ld * 2 + c * 16) : kDmaOOB;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (uint32_t)((wave * 6 + o) * 1024));
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs), "{m0}"(dst) : "memory");
+  }
+}
+
+// A score tile over all 384 d: 24 MFMAs from the staged tile t (row operand)
+// and the fragments fr held for the walk (column operand), with the tile's
+// fragment reads issued four ahead of the MFMAs that use them.
+__device__ __forceinline__ f32x16 score384(const uint16_t* t, const bf16x8 (&fr)[kWideD / 16], int lane) {
+  constexpr int KS = kWideD / 16, AHEAD = 4;
+  f32x16 acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+  bf16x8 a[KS];
+#pragma unroll
+  for (int kk = 0; kk < AHEAD; ++kk) a[kk] = frag_rows<kWideD>(t, 0, kk, lane);
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+    if (kk + AHEAD < KS) a[kk + AHEAD] = frag_rows<kWideD>(t, 0, kk + AHEAD, lane);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], fr[kk], acc, 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD, 0);  // DS reads
+#pragma unroll
+  for (int kk = 0; kk < KS - AHEAD; ++kk) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+  return acc;
+}
+
 template <bool CAUSAL>
-__global__ __launch_bounds__(256) void p_split_kernel(const float* __restrict__ S, const float* __restrict__ lse,
-                                                      int s, float scale_log2, uint16_t* __restrict__ Pst) {
-  const int q = blockIdx.y;
-  const float L = lse[q] * kLog2e;
-  for (int k = (blockIdx.x * 256 + threadIdx.x) * 4; k < s; k += gridDim.x * 256 * 4) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(S + (int64_t)q * s + k);
-    float p[4];
+__device__ __forceinline__ void dkdv_wide_item(int item, char* lds, const uint16_t* __restrict__ qkv,
+                                               const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                                               const float* __restrict__ Dv, uint16_t* __restrict__ dqkv,
+                                               float* __restrict__ partK, float* __restrict__ partV, int s, int Hl,
+                                               int BH, int nkb, int C, float scale_log2, float scale) {
+  constexpr int D = kWideD, KS = D / 16;
+  uint16_t* const sQ0 = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* const sdO0 = reinterpret_cast<uint16_t*>(lds + kWideOffB);
+  f32x4* const xP = reinterpret_cast<f32x4*>(lds + kWideOffXP);
+  u32x4* const xPb = reinterpret_cast<u32x4*>(lds + kWideOffXPb);
+  u32x4* const xSb = reinterpret_cast<u32x4*>(lds + kWideOffXSb);
+  float* const sLD = reinterpret_cast<float*>(lds + kWideOffL);  // [buf][lse (log2 units) x 32 | D x 32]
+
+  const int bh = item % BH;
+  int kb, chunk;
+  chunk_of<CAUSAL, false>(item / BH, nkb, kWideR, s, C, kb, chunk);
+  if (kb < 0) return;
+  const int bi = bh / Hl, head = bh % Hl;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
+  const int half = wave & 1;
+  const bool sw = wave < 2;  // S wave; else dP wave
+  const int64_t ld = 3LL * Hl * D, ldo = (int64_t)Hl * D;
+  const uint16_t* Qg = qkv + (int64_t)bi * s * ld + (int64_t)head * D;
+  const uint16_t* Kg = Qg + (int64_t)Hl * D;
+  const uint16_t* Vg = Qg + 2LL * Hl * D;
+  const uint16_t* dOg = dO + (int64_t)bi * s * ldo + (int64_t)head * D;
+  const float* lseg = lse + (int64_t)bh * s;
+  const float* Dg = Dv + (int64_t)bh * s;
+  const int k0 = kb * kWideR, kh = k0 + 32 * half;
+
+  // K (S wave) or V (dP wave) of key kh + lr over all d: the score product's column operand
+  bf16x8 fr[KS];
+  {
+    const bool ok = kh + lr < s;
+    const uint16_t* src = (sw ? Kg : Vg) + (int64_t)(ok ? kh + lr : 0) * ld + 8 * hh;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      p[e] = (CAUSAL && k + e > q) ? 0.f : __builtin_amdgcn_exp2f(__builtin_fmaf(x[e], scale_log2, -L));
-    const uint32_t h0 = pack_bf16x2(p[0], p[1]), h1 = pack_bf16x2(p[2], p[3]);
-    const uint32_t l0 = pack_bf16x2(p[0] - bf16_bits_to_f32(h0 & 0xffffu), p[1] - bf16_bits_to_f32(h0 >> 16));
-    const uint32_t l1 = pack_bf16x2(p[2] - bf16_bits_to_f32(h1 & 0xffffu), p[3] - bf16_bits_to_f32(h1 >> 16));
-    *reinterpret_cast<uint2*>(Pst + (int64_t)q * s + k) = uint2{h0, h1};
-    *reinterpret_cast<uint2*>(Pst + ((int64_t)s + q) * s + k) = uint2{l0, l1};
+    for (int kk = 0; kk < KS; ++kk) fr[kk] = ok ? *reinterpret_cast<const bf16x8*>(src + 16 * kk) : bf16x8{};
+    // consume the loads here: a first use inside the walk would make the compiler
+    // wait there on every step, and so for the tile DMAs still in flight
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(fr[kk]));
+  }
+
+  const int nsteps = kv_steps<CAUSAL>(kb, kWideR, s), nch = (nsteps + C - 1) / C;
+  const int qstart = (CAUSAL ? k0 : 0) + 32 * C * chunk;
+  const int nq = min(C, nsteps - C * chunk);
+  // the next query block: Q and dO tiles by DMA into LDS buffer buf, lse and D through registers
+  // (thread t < 32 loads the lse of query q0 + t, thread 32 + t its D; the value is
+  // first used at put, after the tiles' own wait)
+  float rx = 0.f;
+  auto fetch = [&](int q0, int buf) __attribute__((always_inline)) {
+    const int q = q0 + (tid & 31);
+    if (tid < 64) rx = q < s ? (tid < 32 ? lseg[q] : Dg[q]) : (tid < 32 ? __builtin_inff() : 0.f);
+    dma_tile384(Qg, ld, q0, s, sQ0 + buf * 32 * D, wave, lane);
+    dma_tile384(dOg, ldo, q0, s, sdO0 + buf * 32 * D, wave, lane);
+  };
+  auto put = [&](int buf) __attribute__((always_inline)) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (tid < 64) sLD[buf * 64 + tid] = tid < 32 ? rx * kLog2e : rx;
+  };
+  fetch(qstart, 0);
+  put(0);
+  __syncthreads();
+
+  f32x16 dk[2][3], dv[2][3];
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dk[hv][i][e] = dv[hv][i][e] = 0.f;
+
+  for (int j = 0; j < nq; ++j) {
+    const int q0 = qstart + 32 * j, buf = j & 1;
+    if (j + 1 < nq) fetch(q0 + 32, buf ^ 1);
+    const uint16_t* tq = sQ0 + buf * 32 * D;
+    const uint16_t* td = sdO0 + buf * 32 * D;
+    // half hv takes part unless all its keys lie above every query of the block or past the end
+    const bool mine = kh < s && !(CAUSAL && kh > q0 + 31);
+
+    // scores: S = Q K^T (S waves) or dP = dO V^T (dP waves) for this half;
+    // lane: key kh + lr, register e: query q0 + 8(e/4) + 4hh + e%4
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    if (mine) acc = score384(sw ? tq : td, fr, lane);
+    if (sw) {
+      const int key = kh + lr;
+      float p[16];
+      auto softmax = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float4 L = *reinterpret_cast<const float4*>(&sLD[buf * 64 + 8 * g + 4 * hh]);
+          const float Lv[4] = {L.x, L.y, L.z, L.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const int e = 4 * g + c, q = q0 + 8 * g + 4 * hh + c;
+            float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], scale_log2, -Lv[c]));
+            if constexpr (decltype(masked)::value)
+              if ((CAUSAL && key > q) || key >= s) pv = 0.f;
+            p[e] = pv;
+          }
+        }
+      };
+      if (!mine) {  // a dead half hands on zeros
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[e] = 0.f;
+      } else if (!CAUSAL || kh + 31 > q0 || kh + 31 >= s) {
+        softmax(std::true_type{});
+      } else {
+        softmax(std::false_type{});
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) xP[(half * 4 + g) * 64 + lane] = f32x4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+      const bf16x8 a0 = pack8(p), a1 = pack8(p + 8);
+      xPb[(half * 4 + 0) * 64 + lane] = __builtin_bit_cast(u32x4, a0);
+      xPb[(half * 4 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, a1);
+      xPb[(half * 4 + 2) * 64 + lane] = __builtin_bit_cast(u32x4, pack8_lo(p, a0));
+      xPb[(half * 4 + 3) * 64 + lane] = __builtin_bit_cast(u32x4, pack8_lo(p + 8, a1));
+    }
+    __syncthreads();
+    if (!sw) {
+      float ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 pv = xP[(half * 4 + g) * 64 + lane];
+        const float4 Dd = *reinterpret_cast<const float4*>(&sLD[buf * 64 + 32 + 8 * g + 4 * hh]);
+        ds[4 * g + 0] = pv[0] * (acc[4 * g + 0] - Dd.x);
+        ds[4 * g + 1] = pv[1] * (acc[4 * g + 1] - Dd.y);
+        ds[4 * g + 2] = pv[2] * (acc[4 * g + 2] - Dd.z);
+        ds[4 * g + 3] = pv[3] * (acc[4 * g + 3] - Dd.w);
+      }
+      const bf16x8 a0 = pack8(ds), a1 = pack8(ds + 8);
+      xSb[(half * 4 + 0) * 64 + lane] = __builtin_bit_cast(u32x4, a0);
+      xSb[(half * 4 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, a1);
+      xSb[(half * 4 + 2) * 64 + lane] = __builtin_bit_cast(u32x4, pack8_lo(ds, a0));
+      xSb[(half * 4 + 3) * 64 + lane] = __builtin_bit_cast(u32x4, pack8_lo(ds + 8, a1));
+    }
+    __syncthreads();
+
+    // dV += P^T dO and dK += dS^T Q over this wave's 96 d columns, both halves
+    // (a dead half's fragments are zero), one 16-query k-slice t at a time (P and
+    // dS fragments: hi, lo)
+    auto products = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 ph[2], pl[2], sh[2], sl[2];
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv)
+          {
+            ph[hv] = __builtin_bit_cast(bf16x8, xPb[(hv * 4 + t) * 64 + lane]);
+            pl[hv] = __builtin_bit_cast(bf16x8, xPb[(hv * 4 + 2 + t) * 64 + lane]);
+            sh[hv] = __builtin_bit_cast(bf16x8, xSb[(hv * 4 + t) * 64 + lane]);
+            sl[hv] = __builtin_bit_cast(bf16x8, xSb[(hv * 4 + 2 + t) * 64 + lane]);
+          }
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const bf16x8 fo = frag_tr<D>(td, 16 * t, 96 * wave + 32 * i, lane);
+          const bf16x8 fq = frag_tr<D>(tq, 16 * t, 96 * wave + 32 * i, lane);
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv)
+            {
+              dv[hv][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ph[hv], fo, dv[hv][i], 0, 0, 0);
+              dv[hv][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pl[hv], fo, dv[hv][i], 0, 0, 0);
+              dk[hv][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sh[hv], fq, dk[hv][i], 0, 0, 0);
+              dk[hv][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sl[hv], fq, dk[hv][i], 0, 0, 0);
+            }
+        }
+      }
+    };
+    products();
+    if (j + 1 < nq) put(buf ^ 1);
+    __syncthreads();
+  }
+
+  // accumulator lane: d column 96w + 32i + lr; register e: key k0 + 32hv + 8(e/4) + 4hh + e%4
+  if (nch > 1) {
+    const int64_t slot = ((int64_t)bh * nkb + kb) * kMaxChunks + chunk;
+    float* pk = partK + slot * kWideR * D;
+    float* pv = partV + slot * kWideR * D;
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kr = 32 * hv + 8 * (e >> 2) + 4 * hh + (e & 3);
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          pk[kr * D + 96 * wave + 32 * i + lr] = dk[hv][i][e];
+          pv[kr * D + 96 * wave + 32 * i + lr] = dv[hv][i][e];
+        }
+      }
+    return;
+  }
+  uint16_t* dKg = dqkv + (int64_t)bi * s * ld + (int64_t)(Hl + head) * D;
+  uint16_t* dVg = dqkv + (int64_t)bi * s * ld + (int64_t)(2 * Hl + head) * D;
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int key = k0 + 32 * hv + 8 * (e >> 2) + 4 * hh + (e & 3);
+      if (key < s) {
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          dKg[(int64_t)key * ld + 96 * wave + 32 * i + lr] = (uint16_t)f32_to_bf16_bits(dk[hv][i][e] * scale);
+          dVg[(int64_t)key * ld + 96 * wave + 32 * i + lr] = (uint16_t)f32_to_bf16_bits(dv[hv][i][e]);
+        }
+      }
+    }
+}
+
+template <bool CAUSAL>
+__device__ __forceinline__ void dq_wide_item(int item, char* lds, const uint16_t* __restrict__ qkv,
+                                             const uint16_t* __restrict__ dO, const float* __restrict__ lse,
+                                             const float* __restrict__ Dv, uint16_t* __restrict__ dqkv,
+                                             float* __restrict__ partQ, int s, int Hl, int BH, int nqb, int C,
+                                             float scale_log2, float scale) {
+  constexpr int D = kWideD, KS = D / 16;
+  uint16_t* const sK0 = reinterpret_cast<uint16_t*>(lds);
+  uint16_t* const sV0 = reinterpret_cast<uint16_t*>(lds + kWideOffB);
+  f32x4* const xP = reinterpret_cast<f32x4*>(lds + kWideOffXP);
+  u32x4* const xSb = reinterpret_cast<u32x4*>(lds + kWideOffXSb);
+
+  const int bh = item % BH;
+  int qb, chunk;
+  chunk_of<CAUSAL, true>(item / BH, nqb, kWideR, s, C, qb, chunk);
+  if (qb < 0) return;
+  const int bi = bh / Hl, head = bh % Hl;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 31, hh = lane >> 5;
+  const int half = wave & 1;
+  const bool sw = wave < 2;
+  const int64_t ld = 3LL * Hl * D, ldo = (int64_t)Hl * D;
+  const uint16_t* Qg = qkv + (int64_t)bi * s * ld + (int64_t)head * D;
+  const uint16_t* Kg = Qg + (int64_t)Hl * D;
+  const uint16_t* Vg = Qg + 2LL * Hl * D;
+  const uint16_t* dOg = dO + (int64_t)bi * s * ldo + (int64_t)head * D;
+  const int q0 = qb * kWideR, qh = q0 + 32 * half, qrow = qh + lr;
+
+  // Q (S wave) or dO (dP wave) of query qrow over all d: the score product's column operand
+  bf16x8 fr[KS];
+  float Lq = __builtin_inff(), Dq = 0.f;
+  {
+    const bool ok = qrow < s;
+    const uint16_t* src = (sw ? Qg + (int64_t)(ok ? qrow : 0) * ld : dOg + (int64_t)(ok ? qrow : 0) * ldo) + 8 * hh;
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) fr[kk] = ok ? *reinterpret_cast<const bf16x8*>(src + 16 * kk) : bf16x8{};
+    if (ok) {
+      if (sw) Lq = lse[(int64_t)bh * s + qrow] * kLog2e;
+      else Dq = Dv[(int64_t)bh * s + qrow];
+    }
+    // consume the loads before the walk (see dkdv_wide_item)
+#pragma unroll
+    for (int kk = 0; kk < KS; ++kk) asm volatile("" : "+v"(fr[kk]));
+    asm volatile("" : "+v"(Lq), "+v"(Dq));
+  }
+
+  const int nsteps = q_steps<CAUSAL>(qb, kWideR, s), nch = (nsteps + C - 1) / C;
+  const int kbase = 32 * C * chunk;
+  const int nk = min(C, nsteps - C * chunk);
+  // the next key block: K and V tiles by DMA into LDS buffer buf
+  auto fetch = [&](int k0, int buf) __attribute__((always_inline)) {
+    dma_tile384(Kg, ld, k0, s, sK0 + buf * 32 * D, wave, lane);
+    dma_tile384(Vg, ld, k0, s, sV0 + buf * 32 * D, wave, lane);
+  };
+  auto put = [&]() __attribute__((always_inline)) { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); };
+  fetch(kbase, 0);
+  put();
+  __syncthreads();
+
+  f32x16 dq[2][3];
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv)
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dq[hv][i][e] = 0.f;
+
+  for (int j = 0; j < nk; ++j) {
+    const int k0 = kbase + 32 * j, buf = j & 1;
+    if (j + 1 < nk) fetch(k0 + 32, buf ^ 1);
+    const uint16_t* tk = sK0 + buf * 32 * D;
+    const uint16_t* tv = sV0 + buf * 32 * D;
+    // half hv takes part unless all its queries lie past the end or below every key of the block
+    const bool mine = qh < s && !(CAUSAL && k0 > qh + 31);
+
+    // scores, transposed: S^T = K Q^T (S waves) or dP^T = V dO^T (dP waves) for this half;
+    // lane: query qrow, register e: key k0 + 8(e/4) + 4hh + e%4
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+    if (mine) acc = score384(sw ? tk : tv, fr, lane);
+    if (sw) {
+      float p[16];
+      auto softmax = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + 8 * (e >> 2) + 4 * hh + (e & 3);
+          float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[e], scale_log2, -Lq));
+          if constexpr (decltype(masked)::value)
+            if ((CAUSAL && key > qrow) || key >= s) pv = 0.f;
+          p[e] = pv;
+        }
+      };
+      if (!mine) {  // a dead half hands on zeros
+#pragma unroll
+        for (int e = 0; e < 16; ++e) p[e] = 0.f;
+      } else if (!CAUSAL || k0 + 31 > qh || k0 + 31 >= s) {
+        softmax(std::true_type{});
+      } else {
+        softmax(std::false_type{});
+      }
+#pragma unroll
+      for (int g = 0; g < 4; ++g) xP[(half * 4 + g) * 64 + lane] = f32x4{p[4 * g], p[4 * g + 1], p[4 * g + 2], p[4 * g + 3]};
+    }
+    __syncthreads();
+    if (!sw) {
+      float ds[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 pv = xP[(half * 4 + g) * 64 + lane];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) ds[4 * g + c] = pv[c] * (acc[4 * g + c] - Dq);
+      }
+      const bf16x8 a0 = pack8(ds), a1 = pack8(ds + 8);
+      xSb[(half * 4 + 0) * 64 + lane] = __builtin_bit_cast(u32x4, a0);
+      xSb[(half * 4 + 1) * 64 + lane] = __builtin_bit_cast(u32x4, a1);
+      xSb[(half * 4 + 2) * 64 + lane] = __builtin_bit_cast(u32x4, pack8_lo(ds, a0));
+      xSb[(half * 4 + 3) * 64 + lane] = __builtin_bit_cast(u32x4, pack8_lo(ds + 8, a1));
+    }
+    __syncthreads();
+
+    // dQ^T += K^T dS^T over this wave's 96 d rows, both halves (a dead half's
+    // fragments are zero), one 16-key k-slice t at a time
+    auto products = [&]() __attribute__((always_inline)) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        bf16x8 sh[2], sl[2];
+#pragma unroll
+        for (int hv = 0; hv < 2; ++hv)
+          {
+            sh[hv] = __builtin_bit_cast(bf16x8, xSb[(hv * 4 + t) * 64 + lane]);
+            sl[hv] = __builtin_bit_cast(bf16x8, xSb[(hv * 4 + 2 + t) * 64 + lane]);
+          }
+#pragma unroll
+        for (int i = 0; i < 3; ++i) {
+          const bf16x8 fk = frag_tr<D>(tk, 16 * t, 96 * wave + 32 * i, lane);
+#pragma unroll
+          for (int hv = 0; hv < 2; ++hv)
+            {
+              dq[hv][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, sh[hv], dq[hv][i], 0, 0, 0);
+              dq[hv][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fk, sl[hv], dq[hv][i], 0, 0, 0);
+            }
+        }
+      }
+    };
+    products();
+    if (j + 1 < nk) put();
+    __syncthreads();
+  }
+
+  // dQ^T accumulator lane: query q0 + 32hv + lr; register e of tile i: d = 96w + 32i + 8(e/4) + 4hh + e%4
+  if (nch > 1) {
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      const int row = 32 * hv + lr;
+      if (q0 + row >= s) continue;
+      float* pq = partQ + ((((int64_t)bh * nqb + qb) * kMaxChunks + chunk) * kWideR + row) * D;
+#pragma unroll
+      for (int i = 0; i < 3; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f32x4*>(pq + 96 * wave + 32 * i + 8 * g + 4 * hh) =
+              f32x4{dq[hv][i][4 * g], dq[hv][i][4 * g + 1], dq[hv][i][4 * g + 2], dq[hv][i][4 * g + 3]};
+    }
+    return;
+  }
+#pragma unroll
+  for (int hv = 0; hv < 2; ++hv) {
+    const int q = q0 + 32 * hv + lr;
+    if (q >= s) continue;
+    uint16_t* dQg = dqkv + ((int64_t)bi * s + q) * ld + (int64_t)head * D;
+#pragma unroll
+    for (int i = 0; i < 3; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 u;
+        u.x = pack_bf16x2(dq[hv][i][4 * g] * scale, dq[hv][i][4 * g + 1] * scale);
+        u.y = pack_bf16x2(dq[hv][i][4 * g + 2] * scale, dq[hv][i][4 * g + 3] * scale);
+        *reinterpret_cast<uint2*>(dQg + 96 * wave + 32 * i + 8 * g + 4 * hh) = u;
+      }
   }
 }
 
-// dS = (P_hi + P_lo)(dP - D_q) / sqrt(d), as hi/lo halves in two layouts: rows
-// stacked (dSr [2s, s], for dK) and columns side by side (dSc [s, 2s], for dQ).
-__global__ __launch_bounds__(256) void ds_split_kernel(const float* __restrict__ dP, const uint16_t* __restrict__ Pst,
-                                                       const float* __restrict__ Dq, int s, float scale,
-                                                       uint16_t* __restrict__ dSr, uint16_t* __restrict__ dSc) {
-  const int q = blockIdx.y;
-  const float D = Dq[q];
-  for (int k = (blockIdx.x * 256 + threadIdx.x) * 4; k < s; k += gridDim.x * 256 * 4) {
-    const f32x4 x = *reinterpret_cast<const f32x4*>(dP + (int64_t)q * s + k);
-    const uint2 ph = *reinterpret_cast<const uint2*>(Pst + (int64_t)q * s + k);
-    const uint2 pl = *reinterpret_cast<const uint2*>(Pst + ((int64_t)s + q) * s + k);
-    const float p[4] = {bf16_bits_to_f32(ph.x & 0xffffu) + bf16_bits_to_f32(pl.x & 0xffffu),
-                        bf16_bits_to_f32(ph.x >> 16) + bf16_bits_to_f32(pl.x >> 16),
-                        bf16_bits_to_f32(ph.y & 0xffffu) + bf16_bits_to_f32(pl.y & 0xffffu),
-                        bf16_bits_to_f32(ph.y >> 16) + bf16_bits_to_f32(pl.y >> 16)};
-    float g[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) g[e] = p[e] * (x[e] - D) * scale;
-    const uint32_t h0 = pack_bf16x2(g[0], g[1]), h1 = pack_bf16x2(g[2], g[3]);
-    const uint32_t l0 = pack_bf16x2(g[0] - bf16_bits_to_f32(h0 & 0xffffu), g[1] - bf16_bits_to_f32(h0 >> 16));
-    const uint32_t l1 = pack_bf16x2(g[2] - bf16_bits_to_f32(h1 & 0xffffu), g[3] - bf16_bits_to_f32(h1 >> 16));
-    *reinterpret_cast<uint2*>(dSr + (int64_t)q * s + k) = uint2{h0, h1};
-    *reinterpret_cast<uint2*>(dSr + ((int64_t)s + q) * s + k) = uint2{l0, l1};
-    *reinterpret_cast<uint2*>(dSc + (int64_t)q * 2 * s + k) = uint2{h0, h1};
-    *reinterpret_cast<uint2*>(dSc + (int64_t)q * 2 * s + s + k) = uint2{l0, l1};
-  }
+// The wide dK/dV walks (items 0 .. nk_items - 1) and dQ walks in one grid; the
+// two kinds share one LDS area.
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) void dkdv_dq_wide_kernel(const uint16_t* __restrict__ qkv,
+                                                           const uint16_t* __restrict__ dO,
+                                                           const float* __restrict__ lse,
+                                                           const float* __restrict__ Dv, uint16_t* __restrict__ dqkv,
+                                                           float* __restrict__ partQ, float* __restrict__ partK,
+                                                           float* __restrict__ partV, int s, int Hl, int BH, int nblk,
+                                                           int C, int nk_items, float scale_log2, float scale) {
+  __shared__ __attribute__((aligned(16))) char lds[kWideLds];
+  const int item = (int)blockIdx.x;
+  if (item < nk_items)
+    dkdv_wide_item<CAUSAL>(item, lds, qkv, dO, lse, Dv, dqkv, partK, partV, s, Hl, BH, nblk, C, scale_log2, scale);
+  else
+    dq_wide_item<CAUSAL>(item - nk_items, lds, qkv, dO, lse, Dv, dqkv, partQ, s, Hl, BH, nblk, C, scale_log2,
+                         scale);
 }
 
-struct WideLayout {
-  int64_t d_bytes, s_bytes, p_bytes, stack_bytes, sk_bytes;
-  int64_t total() const { return d_bytes + s_bytes + 3 * p_bytes + 3 * stack_bytes + sk_bytes; }
-};
-
-inline WideLayout wide_layout(int b, int s, int Hl) {
-  WideLayout L;
-  L.d_bytes = r256((int64_t)b * Hl * s * 4);
-  L.s_bytes = r256((int64_t)s * s * 4);
-  L.p_bytes = r256((int64_t)2 * s * s * 2);
-  L.stack_bytes = r256((int64_t)2 * s * kWideD * 2);
-  L.sk_bytes = (int64_t)kSkBytes;
+inline BwdLayout bwd_layout_wide(int b, int s, int Hl) {
+  BwdLayout L;
+  const int64_t BH = (int64_t)b * Hl;
+  L.nqb = (s + kWideR - 1) / kWideR;
+  L.nkb = L.nqb;
+  const int max_steps = (s + 31) / 32;
+  L.C = max(16, (max_steps + kMaxChunks - 1) / kMaxChunks);
+  L.d_bytes = r256(BH * s * 4);
+  const int64_t slots = L.C >= max_steps ? 0 : BH * L.nqb * kMaxChunks;
+  L.q_bytes = r256(slots * kWideR * kWideD * 4);
+  L.kv_bytes = L.q_bytes;
   return L;
 }
-
-GemmArgs wide_args(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K, void* C, int64_t ldc,
-                   void* sk) {
-  GemmArgs g{};
-  g.A = static_cast<const uint16_t*>(A);
-  g.B = static_cast<const uint16_t*>(B);
-  g.lda = lda;
-  g.ldb = ldb;
-  g.M = M;
-  g.N = N;
-  g.K = K;
-  g.C = C;
-  g.ldc = ldc;
-  gemm_bf16_sk_attach(g, sk);
-  return g;
-}
-
-#define TPS_TRY_HIP(expr)                  \
-  do {                                     \
-    const hipError_t _e = (expr);          \
-    if (_e != hipSuccess) return _e;       \
-  } while (0)
 
 template <bool CAUSAL>
 hipError_t launch_bwd_wide(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO, const float* lse,
@@ -742,52 +1147,33 @@ hipError_t launch_bwd_wide(const uint16_t* qkv, const uint16_t* O, const uint16_
   constexpr int D = kWideD;
   const int64_t rows = (int64_t)b * s * Hl;
   if (rows == 0) return hipSuccess;
-  // the [2s, s] bf16 pair buffers are GEMM operands: below 2 GiB
-  if ((int64_t)2 * s * s * 2 >= (1LL << 31) - 16) return hipErrorInvalidValue;
-  const WideLayout L = wide_layout(b, s, Hl);
+  const BwdLayout L = bwd_layout_wide(b, s, Hl);
   char* w = static_cast<char*>(ws);
   float* Dws = reinterpret_cast<float*>(w);
-  float* Sbuf = reinterpret_cast<float*>(w + L.d_bytes);
-  uint16_t* Pst = reinterpret_cast<uint16_t*>(w + L.d_bytes + L.s_bytes);
-  uint16_t* dSr = reinterpret_cast<uint16_t*>(w + L.d_bytes + L.s_bytes + L.p_bytes);
-  uint16_t* dSc = reinterpret_cast<uint16_t*>(w + L.d_bytes + L.s_bytes + 2 * L.p_bytes);
-  uint16_t* Q2 = reinterpret_cast<uint16_t*>(w + L.d_bytes + L.s_bytes + 3 * L.p_bytes);
-  uint16_t* K2 = Q2 + L.stack_bytes / 2;
-  uint16_t* dO2 = K2 + L.stack_bytes / 2;
-  void* sk = w + L.d_bytes + L.s_bytes + 3 * L.p_bytes + 3 * L.stack_bytes;
+  float* partQ = reinterpret_cast<float*>(w + L.d_bytes);
+  float* partK = reinterpret_cast<float*>(w + L.d_bytes + L.q_bytes);
+  float* partV = reinterpret_cast<float*>(w + L.d_bytes + L.q_bytes + L.kv_bytes);
+  const int BH = b * Hl;
+  int items_q = 0, items_k = 0, max_nc = 1;
+  for (int i = 0; i < L.nqb; ++i) {
+    const int nq = (q_steps<CAUSAL>(i, kWideR, s) + L.C - 1) / L.C;
+    const int nk = (kv_steps<CAUSAL>(i, kWideR, s) + L.C - 1) / L.C;
+    items_q += nq;
+    items_k += nk;
+    max_nc = max(max_nc, max(nq, nk));
+  }
+  if (max_nc > 1 && L.q_bytes == 0) return hipErrorInvalidValue;
+  if ((int64_t)BH * (items_q + items_k) > 0x7fffffffLL) return hipErrorInvalidValue;
   const float scale = 1.f / sqrtf((float)D), scale_log2 = kLog2e * scale;
-  const int64_t ld = 3LL * Hl * D, ldo = (int64_t)Hl * D;
   hipLaunchKernelGGL(rowdot_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, st, dO, O, Dws, s, Hl, D, rows);
-  TPS_TRY_HIP(hipGetLastError());
-  const unsigned stack_blocks = (unsigned)(((int64_t)s * (D / 8) + 255) / 256);
-  const dim3 row_grid((unsigned)min(16, (s / 4 + 255) / 256), (unsigned)s);
-  for (int bi = 0; bi < b; ++bi)
-    for (int j = 0; j < Hl; ++j) {
-      const uint16_t* Qh = qkv + (int64_t)bi * s * ld + (int64_t)j * D;
-      const uint16_t* Kh = Qh + (int64_t)Hl * D;
-      const uint16_t* Vh = Qh + 2LL * Hl * D;
-      const uint16_t* dOh = dO + (int64_t)bi * s * ldo + (int64_t)j * D;
-      const float* lseh = lse + ((int64_t)bi * Hl + j) * s;
-      const float* Dh = Dws + ((int64_t)bi * Hl + j) * s;
-      uint16_t* dQh = dqkv + (int64_t)bi * s * ld + (int64_t)j * D;
-      uint16_t* dKh = dQh + (int64_t)Hl * D;
-      uint16_t* dVh = dQh + 2LL * Hl * D;
-      hipLaunchKernelGGL(stack2_kernel, dim3(stack_blocks), dim3(256), 0, st, Qh, ld, s, Q2);
-      hipLaunchKernelGGL(stack2_kernel, dim3(stack_blocks), dim3(256), 0, st, Kh, ld, s, K2);
-      hipLaunchKernelGGL(stack2_kernel, dim3(stack_blocks), dim3(256), 0, st, dOh, ldo, s, dO2);
-      // S = Q K^T: A = Q [s, D] (K-contig), B(k, n) = K[n, k] (K-contig)
-      TPS_TRY_HIP(gemm_bf16(wide_args(Qh, ld, Kh, ld, s, s, D, Sbuf, s, sk), true, true, EPI_F32, st));
-      hipLaunchKernelGGL((p_split_kernel<CAUSAL>), row_grid, dim3(256), 0, st, Sbuf, lseh, s, scale_log2, Pst);
-      // dV = [P_hi; P_lo]^T [dO; dO]: A(m, k) = Pst[k, m] (M-contig), B(k, n) = dO2[k, n] (N-contig)
-      TPS_TRY_HIP(gemm_bf16(wide_args(Pst, s, dO2, D, s, D, 2 * s, dVh, ld, sk), false, false, EPI_BF16, st));
-      // dP = dO V^T: A = dO [s, D] (K-contig), B(k, n) = V[n, k] (K-contig)
-      TPS_TRY_HIP(gemm_bf16(wide_args(dOh, ldo, Vh, ld, s, s, D, Sbuf, s, sk), true, true, EPI_F32, st));
-      hipLaunchKernelGGL(ds_split_kernel, row_grid, dim3(256), 0, st, Sbuf, Pst, Dh, s, scale, dSr, dSc);
-      // dK = [dS_hi; dS_lo]^T [Q; Q]: A(m, k) = dSr[k, m] (M-contig), B(k, n) = Q2[k, n] (N-contig)
-      TPS_TRY_HIP(gemm_bf16(wide_args(dSr, s, Q2, D, s, D, 2 * s, dKh, ld, sk), false, false, EPI_BF16, st));
-      // dQ = [dS_hi | dS_lo] [K; K]: A = dSc [s, 2s] (K-contig), B(k, n) = K2[k, n] (N-contig)
-      TPS_TRY_HIP(gemm_bf16(wide_args(dSc, 2LL * s, K2, D, s, D, 2 * s, dQh, ld, sk), true, false, EPI_BF16, st));
-    }
+  hipLaunchKernelGGL((dkdv_dq_wide_kernel<CAUSAL>), dim3((unsigned)((int64_t)BH * (items_k + items_q))), dim3(256),
+                     0, st, qkv, dO, lse, Dws, dqkv, partQ, partK, partV, s, Hl, BH, L.nqb, L.C, BH * items_k,
+                     scale_log2, scale);
+  if (max_nc > 1) {
+    const dim3 grid((unsigned)((int64_t)BH * L.nqb), (unsigned)((kWideR * D / 4 + 255) / 256), 3);
+    hipLaunchKernelGGL((combine_kernel<D, CAUSAL>), grid, dim3(256), 0, st, partQ, partK, partV, dqkv, s, Hl, L.nqb,
+                       kWideR, L.C, scale);
+  }
   return hipGetLastError();
 }
 
@@ -795,7 +1181,10 @@ hipError_t launch_bwd_wide(const uint16_t* qkv, const uint16_t* O, const uint16_
 
 size_t attn_bwd_workspace(int b, int s, int Hl, int d) {
   if (b <= 0 || s <= 0 || Hl <= 0) return 0;
-  if (d == kWideD) return (size_t)wide_layout(b, s, Hl).total();
+  if (d == kWideD) {
+    const BwdLayout L = bwd_layout_wide(b, s, Hl);
+    return (size_t)(L.d_bytes + L.q_bytes + 2 * L.kv_bytes);
+  }
   const BwdLayout L = bwd_layout(b, s, Hl, d);
   return (size_t)(L.d_bytes + L.q_bytes + 2 * L.kv_bytes);
 }

@@ -237,10 +237,8 @@ tp_status tp_attn_fwd_train(int64_t b, int64_t s, int64_t h, int64_t n_heads_loc
  *   P = exp(q.k / sqrt(d) - lse), dV = P^T dO, dP = dO V^T, dS = P * (dP - rowsum(dO*O)),
  *   dQ = dS K / sqrt(d), dK = dS^T Q / sqrt(d); written as bf16 dQKV [b*s, 3*Hl*d] in the
  *   [Q | K | V] layout of QKV. dO bf16 [b*s, Hl*d]; lse from tp_attn_fwd_train.
- *   Deterministic (no atomics). ws: tp_attn_core_bwd_workspace(b, s, Hl, d) bytes.
- *   d = 384 runs per-head products with float32 [s, s] scores and bf16 [2s, s]
- *   probability and gradient pairs in the workspace (about 16 s^2 bytes plus the
- *   100.7 MB stream-K area); it needs s % 8 == 0 (TP_ERR_UNSUPPORTED otherwise). */
+ *   Deterministic (no atomics). ws: tp_attn_core_bwd_workspace(b, s, Hl, d) bytes
+ *   (rowsum(dO*O) and the float32 partials of walks cut into chunks). */
 tp_status tp_attn_core_bwd(int64_t b, int64_t s, int64_t n_heads_local, int64_t d_head, int causal,
                            const void* QKV, const void* O, const void* dO, const float* lse,
                            void* dQKV, void* ws, size_t ws_bytes, void* stream);

@@ -45,14 +45,17 @@ def _core_case(b, s, Hl, d, causal, seed):
 
 # Walks longer than 16 key (or query) tiles of 32 are cut into chunks whose fp32
 # partials a combine pass adds: s = 513 and 530 (causal) and s = 600 (every block,
-# not causal) cover that path for both head sizes.
-# d = 384 runs the per-head product path (s % 8 == 0).
+# not causal) cover that path for both head sizes. d = 384 (blocks of 64 rows, a
+# step's work split over four waves): ragged lengths (301, 200, 1, 8), chunked walks
+# (700 causal, 530 not), and blocks whose second half lies past the end.
 @pytest.mark.parametrize("b,s,Hl,d,causal", [(2, 300, 2, 128, True), (1, 77, 3, 64, True),
                                               (2, 200, 2, 128, False), (1, 1, 1, 128, True),
                                               (3, 129, 1, 64, False), (1, 513, 1, 128, True),
                                               (2, 530, 1, 64, True), (1, 600, 2, 64, False),
                                               (1, 304, 2, 384, True), (2, 200, 1, 384, False),
-                                              (1, 8, 1, 384, True)])
+                                              (1, 8, 1, 384, True), (1, 301, 2, 384, True),
+                                              (1, 1, 1, 384, True), (1, 700, 1, 384, True),
+                                              (2, 530, 1, 384, False), (1, 100, 1, 384, True)])
 def test_core_backward(b, s, Hl, d, causal):
     note(f"attn_core_bwd b={b} s={s} Hl={Hl} d={d} causal={causal}")
     qkv, dO, O, lse, dq, _ = _core_case(b, s, Hl, d, causal, 90 + s + d)
@@ -68,9 +71,10 @@ def test_core_backward(b, s, Hl, d, causal):
     assert_grad_close(g[:, 2 * w:], rv, "dV")
 
 
-def test_core_backward_is_deterministic():
-    b, s, Hl, d = 1, 700, 2, 128
-    note("attn_core_bwd twice, bit-identical")
+@pytest.mark.parametrize("Hl,d", [(2, 128), (1, 384)])
+def test_core_backward_is_deterministic(Hl, d):
+    b, s = 1, 700
+    note(f"attn_core_bwd twice, bit-identical, d={d}")
     qkv, dO, O, lse, dq, (Q, dOd, ws) = _core_case(b, s, Hl, d, True, 99)
     dq2 = torch.empty_like(dq)
     tp.attn_core_bwd(Q, O, dOd, lse, dq2, ws, b, s, Hl, d, True)
