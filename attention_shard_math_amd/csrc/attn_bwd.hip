@@ -37,9 +37,9 @@
 // thousands of tokens) within the bf16 bar.
 //
 // LDS rows hold one head's d columns; 16-byte chunk c of row r is stored at
-// c ^ swz(r), swz(r) = ((r & 7) << 1) | ((r >> 3) & 1) (for 384-wide rows inside
-// each group of 16 chunks), conflict-free for the 16-row ds_read_b128 fragment
-// reads and for the 4-row x 2-chunk transposing reads.
+// c ^ swz(r), swz(r) = ((r & 7) << 1) | ((r >> 3) & 1), conflict-free for the
+// 16-row ds_read_b128 fragment reads (384-wide rows use swz384, inside each group
+// of 16 chunks).
 //
 // Heads of d = 384 take the same walks with the work of a step split over four
 // waves (see dkdv_wide_item).
@@ -61,10 +61,16 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 
 
 // Element offset of (row r, column c) in a [rows][D] bf16 LDS tile (c % 4 == 0
 // for transposing reads; any c inside its 16-byte chunk).
+// Chunk swizzle of the 384-wide tiles: a permutation of the row's low 4 bits, so
+// that 16 consecutive rows take 16 distinct chunk positions (the ds_read_b128
+// fragment reads) and 4 consecutive rows 4 distinct aligned groups of 4 positions
+// (the 4-row x 4-chunk transposing reads, which swz gives 2-way bank conflicts).
+__device__ __forceinline__ int swz384(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
 template <int D>
 __device__ __forceinline__ int toff(int r, int c) {
   if constexpr (D == 384)  // 48 chunks a row: the xor (< 16) stays inside each group of 16
-    return r * D + (((c >> 3) ^ swz(r)) << 3) + (c & 7);
+    return r * D + (((c >> 3) ^ swz384(r)) << 3) + (c & 7);
   else
     return r * D + ((((c >> 3) ^ swz(r)) & (D / 8 - 1)) << 3) + (c & 7);
 }
@@ -671,7 +677,7 @@ __device__ __forceinline__ uint32_t lds_u32(const void* p) {
 // straight from memory into a swizzled [32][384] LDS tile with
 // buffer_load_dwordx4 ... lds (rows at or past `rows` read as zero). Wave w of
 // four issues 6 of the tile's 24 1-KB pieces; physical chunk P of the tile (row
-// P / 48, position P % 48) receives logical chunk (P % 48) ^ swz(row). The loads
+// P / 48, position P % 48) receives logical chunk (P % 48) ^ swz384(row). The loads
 // complete asynchronously: s_waitcnt vmcnt(0) before the barrier that publishes
 // the tile. Issued as inline asm (no register outputs), so the compiler does
 // not wait for them before unrelated LDS reads.
@@ -682,7 +688,7 @@ __device__ __forceinline__ void dma_tile384(const uint16_t* g, int64_t ld, int r
   const uint32_t base = lds_u32(tile);
 #pragma unroll
   for (int o = 0; o < 6; ++o) {
-    const int P = (wave * 6 + o) * 64 + lane, r = P / 48, c = (P % 48) ^ swz(r);
+    const int P = (wave * 6 + o) * 64 + lane, r = P / 48, c = (P % 48) ^ swz384(r);
     const uint32_t off = (r0 + r < rows) ? (uint32_t)(r * ld * 2 + c * 16) : kDmaOOB;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(base + (uint32_t)((wave * 6 + o) * 1024));
     asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(rs), "{m0}"(dst) : "memory");
