@@ -55,7 +55,8 @@ def _core_case(b, s, Hl, d, causal, seed):
                                               (1, 304, 2, 384, True), (2, 200, 1, 384, False),
                                               (1, 8, 1, 384, True), (1, 301, 2, 384, True),
                                               (1, 1, 1, 384, True), (1, 700, 1, 384, True),
-                                              (2, 530, 1, 384, False), (1, 100, 1, 384, True)])
+                                              (2, 530, 1, 384, False), (1, 100, 1, 384, True),
+                                              (2, 150, 2, 384, True)])
 def test_core_backward(b, s, Hl, d, causal):
     note(f"attn_core_bwd b={b} s={s} Hl={Hl} d={d} causal={causal}")
     qkv, dO, O, lse, dq, _ = _core_case(b, s, Hl, d, causal, 90 + s + d)

@@ -7,7 +7,7 @@ import torch
 import oracle
 from oracle.bf16 import bf16_bits_to_f64
 from tests.gpu_util import (DEV, assert_bf16_close, assert_f32_close, bf16_dev, f32_dev, f64_host, note)
-from workloads import CONFIGS, mlp_inputs, shard_sum_inputs
+from workloads import CONFIGS, bf16_bits, mlp_inputs, shard_sum_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -129,6 +129,73 @@ def test_column_linear_without_activation():
     from oracle.bf16 import round_to_bf16
     ref = round_to_bf16(bf16_bits_to_f64(Xb) @ bf16_bits_to_f64(Wb))
     assert_bf16_close(f64_host(Y), ref, "X W")
+
+
+def _gelu_grid():
+    """u over [-40, 40] and the small and special values, rounded to bf16 (so that a
+    product with one unit weight forms u exactly), padded to a multiple of 8."""
+    u = np.concatenate([np.linspace(-40.0, 40.0, 1601), [0.0, -0.0, 1e-3, -1e-3, 0.5, -0.5, 3.5, -3.5, -4.0,
+                                                        -6.0, -9.0, -13.0, -88.0, 88.0]])
+    u = bf16_bits_to_f64(bf16_bits(u.astype(np.float32)))
+    u = np.unique(u)
+    pad = -len(u) % 8
+    return np.concatenate([u, np.zeros(pad)])
+
+
+def _gelu_tolerance(u, ref):
+    # bf16 rounding of the stored result, plus the epilogue's own error: Phi from the
+    # Abramowitz-Stegun 7.1.26 erfc fit in float32 stays within 4e-7 max(1, |u|) of the
+    # exact erf form (its bound is absolute: in the far negative tail, where |GeLU| is
+    # below ~1e-4, the relative error exceeds bf16 rounding)
+    return 2.0 ** -8 * np.abs(ref) + 4e-7 * np.maximum(1.0, np.abs(u))
+
+
+def test_gelu_epilogue_over_the_range():
+    """The column GEMM's GeLU epilogue against the exact erf GeLU, u in [-40, 40]:
+    X[:, 0] = u, W[0, :] = 1, every other entry 0, so U = X W = u exactly."""
+    u = _gelu_grid()
+    M, K, N = len(u), 64, 64
+    note(f"GeLU epilogue over {M} values of u")
+    X = np.zeros((M, K), np.float32)
+    X[:, 0] = u
+    W = np.zeros((K, N), np.float32)
+    W[0, :] = 1.0
+    U = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=DEV)
+    tp.column_linear(bf16_dev(bf16_bits(X)), bf16_dev(bf16_bits(W)), Y, U=U, act="gelu")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(f64_host(U), np.repeat(u[:, None], N, axis=1))
+    ref = oracle.gelu(u)[:, None]
+    err = np.abs(f64_host(Y) - ref)
+    tol = _gelu_tolerance(u, oracle.gelu(u))[:, None]
+    assert np.all(err <= tol), f"worst u = {u[np.argmax((err / tol).max(axis=1))]}, err/tol = {(err / tol).max():.3f}"
+
+
+def test_gelu_prime_epilogue_over_the_range():
+    """The backward's GeLU' epilogue, dU = (dZ B^T) * GeLU'(U), against the exact form:
+    dZ[:, 0] = 1 and B[:, 0] = 1 (else 0) make dZ B^T = 1, and X = I makes dA = X^T dU = dU."""
+    u = _gelu_grid()
+    h, f = 64, len(u)
+    M = h
+    note(f"GeLU' epilogue over {f} values of u")
+    X = np.eye(M, h, dtype=np.float32)
+    Ub = np.repeat(u[None, :], M, axis=0).astype(np.float32)
+    dZ = np.zeros((M, h), np.float32)
+    dZ[:, 0] = 1.0
+    B = np.zeros((f, h), np.float32)
+    B[:, 0] = 1.0
+    A = np.zeros((h, f), np.float32)
+    dX = torch.empty(M, h, dtype=torch.float32, device=DEV)
+    dA = torch.empty(h, f, dtype=torch.float32, device=DEV)
+    dB = torch.empty(f, h, dtype=torch.float32, device=DEV)
+    ws = torch.empty(tp.mlp_bwd_workspace(M, h, f), dtype=torch.uint8, device=DEV)
+    tp.mlp_bwd(bf16_dev(bf16_bits(X)), bf16_dev(bf16_bits(A)), bf16_dev(bf16_bits(B)), bf16_dev(bf16_bits(Ub)),
+               bf16_dev(bf16_bits(np.zeros((M, f), np.float32))), bf16_dev(bf16_bits(dZ)), dX, dA, dB, ws)
+    torch.cuda.synchronize()
+    refp = oracle.gelu_prime(u)
+    err = np.abs(f64_host(dA) - refp[None, :])
+    tol = _gelu_tolerance(u, refp)[None, :]
+    assert np.all(err <= tol), f"worst u = {u[np.argmax((err / tol).max(axis=0))]}, err/tol = {(err / tol).max():.3f}"
 
 
 class TestGpt3MlpShardFullSize:
