@@ -650,10 +650,12 @@ hipError_t launch_bwd(const uint16_t* qkv, const uint16_t* O, const uint16_t* dO
 //     leave their bf16 hi/lo operand fragments in LDS;
 //   * products: wave w accumulates the d columns [96w, 96w + 96) of the
 //     gradients of both halves from those fragments and the staged tile.
-// Three barriers a step: P ready, dS ready, next tile staged. A half whose
-// keys all lie above the step's queries (or past the end) is skipped by every
-// wave. Walks are cut into chunks as above, and combine_kernel adds the
-// chunks' partials.
+// Three barriers a step: P ready, dS ready, next tile staged. For a half whose
+// keys all lie above the step's queries (or past the end) the score waves skip
+// their MFMAs and hand on zero fragments; the products run for both halves
+// regardless (per-half branches there split the MFMA stream into small blocks).
+// Walks are cut into chunks as above, and combine_kernel adds the chunks'
+// partials.
 constexpr int kWideD = 384;
 constexpr int kWideTileB = 32 * kWideD * 2;             // bytes of a [32][384] bf16 tile
 constexpr int kWideOffB = 2 * kWideTileB;               // second pair of tiles (dO or V)
