@@ -52,15 +52,23 @@ constexpr int kGrid = 256;              // persistent grid: one workgroup per CU
 constexpr int kBM = 256, kBN = 192;     // tile of every product
 
 // Stream-K is used when the last round of tiles fills at most half of the grid,
-// for up to kSkMaxTiles tiles. With a fuller last round the split does not pay:
-// the GEMMs run power-limited, so the CUs that would idle mostly let the busy ones
-// clock higher, while the split adds the partials' traffic and a second kernel
-// (measured: a 192-tile product took 6% longer, a 264-tile one 5% less). Nor does
-// it pay for tiles of fewer than kSkMinStages k-stages: a split tile's partials
-// (192 KB written and read back per piece) then cost as much traffic as its
-// operands (measured: the per-head [4096, 4096] score products of 384-wide heads,
-// 12 stages per tile, made the whole PaLM-shaped attention backward 5% slower).
-constexpr int kSkMaxTiles = 4096;
+// for fewer than four rounds of tiles (kSkMaxTiles), and for tiles of at least
+// kSkMinStages k-stages.
+// - With a fuller last round the split does not pay: the GEMMs run power-limited,
+//   so the CUs that would idle mostly let the busy ones clock higher, while the
+//   split adds the partials' traffic and a second kernel (measured: a 192-tile
+//   product took 6% longer, a 264-tile one 5% less).
+// - Each workgroup's run is a contiguous stretch of the tile order, so the 32 runs
+//   side by side on an XCD sit a run's length apart in it and share few operand
+//   panels in its L2, where the tile kernel deals an XCD consecutive tiles. The
+//   longer the runs, the more that costs, while the last round's idle share
+//   shrinks (measured: 2592 tiles took 1339 us with stream-K against 924 us in the
+//   tile kernel, 864 tiles the same in both, 576 tiles 10% less with stream-K).
+// - With tiles of fewer than kSkMinStages k-stages, a split tile's partials (192 KB
+//   written and read back per piece) cost as much traffic as its operands
+//   (measured: the per-head [4096, 4096] score products of an earlier 384-wide
+//   attention backward, 12 stages per tile, made that backward 5% slower).
+constexpr int kSkMaxTiles = 1023;
 constexpr int kSkMinStages = 48;
 __host__ __device__ constexpr bool sk_applies(int64_t tiles, int K) {
   return K >= kSkMinStages * BK && tiles > 0 && tiles % kGrid != 0 && tiles % kGrid <= kGrid / 2 &&

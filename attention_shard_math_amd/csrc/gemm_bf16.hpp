@@ -55,7 +55,7 @@ constexpr size_t kSkBytes = (size_t)2 * 256 * 256 * 192 * 4;
 
 // Workspace bytes a launch of an M x N x K product uses: kSkBytes when it runs
 // stream-K (the last round of its 256 x 192 tiles fills at most half of the
-// 256-workgroup grid; at most 4096 tiles), else 0.
+// 256-workgroup grid; fewer than 1024 tiles; tiles of at least 48 k-stages), else 0.
 size_t gemm_bf16_sk_workspace(int M, int N, int K);
 
 // Points g's stream-K area at `area` (kSkBytes, 256-byte aligned), or clears it

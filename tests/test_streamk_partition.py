@@ -12,9 +12,12 @@ import pytest
 GRID, BK = 256, 32
 
 
+MIN_STAGES, MAX_TILES = 48, 1023
+
+
 def sk_applies(tiles, K):
-    return (K > 0 and tiles > 0 and tiles % GRID != 0 and tiles % GRID <= GRID // 2 and tiles <= 4096
-            and tiles * ((K + BK - 1) // BK) < (1 << 30))
+    return (K >= MIN_STAGES * BK and tiles > 0 and tiles % GRID != 0 and tiles % GRID <= GRID // 2
+            and tiles <= MAX_TILES and tiles * ((K + BK - 1) // BK) < (1 << 30))
 
 
 def runs(T, nk):
@@ -65,6 +68,9 @@ def test_partition(T, nk):
 def test_rule():
     assert not sk_applies(256, 12288) and not sk_applies(512, 6144)     # whole rounds
     assert sk_applies(64, 12288) and sk_applies(264, 12288)             # last round <= half full
-    assert sk_applies(384, 12288) and sk_applies(3456, 2048)
+    assert sk_applies(384, 12288) and sk_applies(576, 18432) and sk_applies(864, 4096)
     assert not sk_applies(192, 12288)                                    # 3/4 full: tile kernel
+    assert not sk_applies(1152, 2048) and not sk_applies(2592, 4096)    # four rounds or more: tile kernel
+    assert not sk_applies(3456, 4096)
+    assert not sk_applies(64, 1504) and sk_applies(64, 1536)            # at least 48 k-stages
     assert not sk_applies(5000, 64) and not sk_applies(64, 0)
