@@ -525,15 +525,18 @@ void gemm_bf16_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------- stream-K
 // Used when the last round of tiles would fill at most half of the 256
-// workgroups (see sk_applies). The
-// T x nk (tile, k-stage) units, tiles in the order above, are cut into 256 equal
-// runs, one per workgroup (XCD-contiguous: workgroup b has virtual index
-// v = (b % 8) * 32 + b / 8). A tile whose units all fall in one run is finished
-// as in the tile kernel. For a tile split over several runs, each run writes its
-// float32 accumulators to a workspace slot of its own (2 slots per run: its first
-// and its last segment); a second kernel adds a split tile's partials in run order
-// and runs the epilogue. No workgroup waits for another, and the sum order is
-// fixed, so the result is reproducible.
+// workgroups (see sk_applies). The whole rounds (D = 256 * floor(T / 256) tiles,
+// the first D of the order above) run as in the tile kernel: workgroup b takes
+// tiles (b % 8) * D / 8 + b / 8 + 32 i, so an XCD works on consecutive tiles. The
+// remaining (T - D) x nk (tile, k-stage) units are cut into 256 equal runs, one
+// per workgroup (XCD-contiguous: workgroup b has virtual index
+// v = (b % 8) * 32 + b / 8), which each workgroup takes after its whole tiles. A
+// tile whose units all fall in one run is finished as in the tile kernel. For a
+// tile split over several runs, each run writes its float32 accumulators to a
+// workspace slot of its own (2 slots per run: its first and its last segment); a
+// second kernel adds a split tile's partials in run order and runs the epilogue.
+// No workgroup waits for another, and the sum order is fixed, so the result is
+// reproducible.
 template <int BM, int BN, bool A_K, bool B_K, int EPI>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gemm_bf16_sk_kernel(GemmArgs g) {
@@ -553,12 +556,18 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
 
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int nk = (g.K + BK - 1) / BK;
-  const int U = tiles_m * tiles_n * nk;  // the host keeps U below 2^31
   const int G = gridDim.x;
-  const int v = (int)(blockIdx.x & 7) * (G >> 3) + (int)(blockIdx.x >> 3);
+  const int T = tiles_m * tiles_n, rounds = T / G, D = rounds * G;
+  // whole tiles: workgroup b's i-th is xcd * D / 8 + jw + i * G / 8
+  const int xcd = (int)(blockIdx.x & 7), jw = (int)(blockIdx.x >> 3);
+  auto dp_tile = [&](int i) { return xcd * (D >> 3) + jw + i * (G >> 3); };
+  // the remainder's units, tiles D .. T - 1 (the host keeps T * nk below 2^31)
+  const int U = (T - D) * nk;
+  const int v = xcd * (G >> 3) + jw;
   const int per = (U + G - 1) / G;
   const int g0 = min(U, v * per), g1 = min(U, g0 + per);
-  const int total = g1 - g0;
+  const int whole = rounds * nk;  // units of this workgroup's whole tiles
+  const int total = whole + (g1 - g0);
   auto tile_m0 = [&](int t) {
     int m, n;
     tile_rc(t, tiles_m, tiles_n, m, n);
@@ -569,7 +578,7 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
     tile_rc(t, tiles_m, tiles_n, m, n);
     return n * BN;
   };
-  // first tile of run u (its slot 0 holds the partial of that tile)
+  // first remainder tile (counted from D) of run u (its slot 0 holds the partial of that tile)
   auto first_tile = [&](int u) { return u * per / nk; };
 
   const int64_t a_elems = A_K ? (int64_t)g.M * g.lda : (int64_t)g.K * g.lda;
@@ -588,8 +597,17 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
     Dma<BN, B_K> db;
     int itile = -1;
     auto issue_stage = [&](int st, int sl) __attribute__((always_inline)) {
-      const int gs = g0 + st;
-      const int ti = gs / nk, kt = gs - ti * nk;
+      int ti, kt;
+      if (st < whole) {
+        const int i = st / nk;
+        ti = dp_tile(i);
+        kt = st - i * nk;
+      } else {
+        const int gs = g0 + st - whole;
+        ti = gs / nk;
+        kt = gs - ti * nk;
+        ti += D;
+      }
       if (ti != itile) {
         da.init(tile_m0(ti), g.M, g.lda, pw, lane);
         db.init(tile_n0(ti), g.N, g.ldb, pw, lane);
@@ -621,18 +639,15 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
     return;
   }
 
-  // ---- MFMA waves: one segment (a tile's k-range inside this run) at a time.
+  // ---- MFMA waves: this workgroup's whole tiles, then one segment (a tile's
+  // k-range inside this run) at a time.
   const int am = wm * WTM, bn = wn * WTN;
   const int fk = lane >> 5, fr = lane & 31;
   f32x4* part = reinterpret_cast<f32x4*>(g.sk_part);
   const int64_t wofs = (int64_t)wave * TM * TN * 4 * 64;  // this wave's float4 inside a slot
   int slot = 0;
-  int gs = g0;
-  while (gs < g1) {
-    const int ti = gs / nk;
-    const int kb = gs - ti * nk;
-    const int ke = min(nk, g1 - ti * nk);
-    f32x16 acc[TM][TN];
+  // k-stages [kb, ke) of one tile into acc (zeroed first), one ring slot per stage
+  auto k_range = [&](f32x16 (&acc)[TM][TN], int kb, int ke) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -668,7 +683,20 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
       }
       slot = slot == NS - 1 ? 0 : slot + 1;
     }
-    const int m0 = tile_m0(ti), n0 = tile_n0(ti);
+  };
+  for (int i = 0; i < rounds; ++i) {
+    f32x16 acc[TM][TN];
+    k_range(acc, 0, nk);
+    const int ti = dp_tile(i);
+    epilogue<EPI>(acc, g, tile_m0(ti) + am, tile_n0(ti) + bn, lane);
+  }
+  int gs = g0;
+  while (gs < g1) {
+    const int ti = gs / nk;  // counted from D
+    const int kb = gs - ti * nk;
+    const int ke = min(nk, g1 - ti * nk);
+    f32x16 acc[TM][TN];
+    k_range(acc, kb, ke);
     const bool split = kb != 0 || ke != nk;
     if (split) {
       // This run's share of a split tile: to its slot, in accumulator order.
@@ -682,15 +710,16 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
             mine[((i * TN + j) * 4 + q) * 64 + lane] =
                 f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]};
     }
-    if (!split) epilogue<EPI>(acc, g, m0 + am, n0 + bn, lane);
+    if (!split) epilogue<EPI>(acc, g, tile_m0(D + ti) + am, tile_n0(D + ti) + bn, lane);
     gs = ti * nk + ke;
   }
 }
 
-// Finishes the split tiles of a stream-K launch: one workgroup per tile, laid out
-// like the MFMA waves of the product kernel (8 waves, the same accumulator tiles per
-// lane), adds the partials of the runs that cover the tile in run order and runs the
-// same epilogue. Workgroups of tiles that one run finished exit at once.
+// Finishes the split tiles of a stream-K launch: one workgroup per remainder tile
+// (tiles D .. T - 1), laid out like the MFMA waves of the product kernel (8 waves,
+// the same accumulator tiles per lane), adds the partials of the runs that cover
+// the tile in run order and runs the same epilogue. Workgroups of tiles that one
+// run finished exit at once.
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(64 * NCW) void gemm_bf16_sk_fixup_kernel(GemmArgs g) {
   constexpr int WM = NCW / 2, WN = 2;
@@ -701,9 +730,10 @@ __global__ __launch_bounds__(64 * NCW) void gemm_bf16_sk_fixup_kernel(GemmArgs g
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int nk = (g.K + BK - 1) / BK;
-  const int U = tiles_m * tiles_n * nk;
+  const int T = tiles_m * tiles_n, D = T / kGrid * kGrid;
+  const int U = (T - D) * nk;
   const int per = (U + kGrid - 1) / kGrid;
-  const int ti = blockIdx.x;
+  const int ti = blockIdx.x;  // counted from D
   const int ua = ti * nk;
   const int vf = ua / per, vl = (ua + nk - 1) / per;
   if (vf == vl) return;
@@ -741,7 +771,7 @@ __global__ __launch_bounds__(64 * NCW) void gemm_bf16_sk_fixup_kernel(GemmArgs g
         }
     }
   int tm, tn;
-  tile_rc(ti, tiles_m, tiles_n, tm, tn);
+  tile_rc(D + ti, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int am = wm * WTM, bn = wn * WTN;
   epilogue<EPI>(acc, g, m0 + am, n0 + bn, lane);
@@ -753,7 +783,7 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (g.sk_part && sk_applies(tiles, g.K)) {
     hipLaunchKernelGGL((gemm_bf16_sk_kernel<BM, BN, A_K, B_K, EPI>), dim3(kGrid), dim3(NT), 0, s, g);
-    hipLaunchKernelGGL((gemm_bf16_sk_fixup_kernel<BM, BN, EPI>), dim3(tiles), dim3(64 * NCW), 0, s, g);
+    hipLaunchKernelGGL((gemm_bf16_sk_fixup_kernel<BM, BN, EPI>), dim3(tiles % kGrid), dim3(64 * NCW), 0, s, g);
     return hipGetLastError();
   }
   // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split

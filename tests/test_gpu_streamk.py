@@ -39,11 +39,13 @@ def _inputs(M, K, N, seed):
 
 
 # (M, K, N): 2 tiles split 48 ways (one k-stage per run); 64 tiles split 4 ways; 2 tiles
-# split 128 ways (runs on two XCDs); 120 tiles over two or three runs each; and 264
-# tiles (the GPT-3 cross-entropy shape's count: one round and 8 more), most split over
-# two runs. Every K has at least the 48 k-stages below which stream-K is not used.
+# split 128 ways (runs on two XCDs); 120 tiles over two or three runs each; 264 tiles
+# (the GPT-3 cross-entropy shape's count: one whole round, then 8 tiles split 32 ways);
+# 576 tiles (two whole rounds, then 64 tiles split 4 ways) and 864 (three rounds, then
+# 96 tiles split over 2-3 runs). Every K has at least the 48 k-stages below which
+# stream-K is not used.
 @pytest.mark.parametrize("M,K,N", [(300, 1536, 136), (2048, 2048, 1536), (64, 12288, 384), (1920, 4096, 2880),
-                                   (2048, 1536, 6288)])
+                                   (2048, 1536, 6288), (4096, 2048, 6912), (2304, 1536, 18432)])
 def test_streamk_matches_tile_kernel(M, K, N):
     note(f"stream-K row linear M={M} K={K} N={N}")
     Y, W = _inputs(M, K, N, M + K + N)

@@ -1,10 +1,11 @@
 """Host model of the stream-K work split of the bf16 GEMM (the same integer formulas
 the product and fixup kernels evaluate per workgroup and per tile), checked for the
-properties the kernels rely on: every (tile, k-stage) unit is covered by exactly one
-run; a run has at most two partial segments (its first and its last), so two
-workspace slots per run suffice; the slots the fixup reads for a split tile are
-distinct and are the ones its runs wrote; and the split is used only when the last
-round of tiles is at most half full."""
+properties the kernels rely on: the whole rounds' tiles are each taken by exactly one
+workgroup, in the tile kernel's XCD order; every (tile, k-stage) unit of the
+remaining tiles is covered by exactly one run; a run has at most two partial
+segments (its first and its last), so two workspace slots per run suffice; the slots
+the fixup reads for a split tile are distinct and are the ones its runs wrote; and
+the split is used only when the last round of tiles is at most half full."""
 import itertools
 
 import pytest
@@ -20,8 +21,17 @@ def sk_applies(tiles, K):
             and tiles <= MAX_TILES and tiles * ((K + BK - 1) // BK) < (1 << 30))
 
 
+def whole_tiles(T):
+    """Workgroup b's whole tiles: (b % 8) * D / 8 + b / 8 + 32 i, D = 256 * floor(T / 256)."""
+    rounds = T // GRID
+    D = rounds * GRID
+    return D, [[(b % 8) * (D // 8) + b // 8 + i * (GRID // 8) for i in range(rounds)] for b in range(GRID)]
+
+
 def runs(T, nk):
-    U = T * nk
+    """The runs over the remainder's units (tiles counted from D)."""
+    R = T - T // GRID * GRID
+    U = R * nk
     per = (U + GRID - 1) // GRID
     return U, per, [(min(U, v * per), min(U, min(U, v * per) + per)) for v in range(GRID)]
 
@@ -44,9 +54,22 @@ def written_slots(T, nk):
     return out
 
 
-@pytest.mark.parametrize("T,nk", list(itertools.product([1, 2, 8, 64, 120, 264, 384, 1152, 3456], [1, 3, 16, 64, 384])))
+@pytest.mark.parametrize("T", [1, 2, 8, 64, 120, 264, 384, 576, 864, 1152, 3456])
+def test_whole_tiles(T):
+    D, lists = whole_tiles(T)
+    taken = sorted(t for l in lists for t in l)
+    assert taken == list(range(D))
+    # an XCD's workgroups take consecutive tiles in each round
+    for b in range(GRID):
+        for i, t in enumerate(lists[b]):
+            assert t == lists[b % 8][i] + b // 8
+
+
+@pytest.mark.parametrize("T,nk", list(itertools.product([1, 2, 8, 64, 120, 264, 384, 576, 864, 1152, 3456],
+                                                        [1, 3, 16, 64, 384])))
 def test_partition(T, nk):
     U, per, rr = runs(T, nk)
+    T = T - T // GRID * GRID  # the remainder's tiles, counted from D
     cover = [0] * U
     for g0, g1 in rr:
         assert 0 <= g0 <= g1 <= U
