@@ -715,65 +715,68 @@ void gemm_bf16_sk_kernel(GemmArgs g) {
   }
 }
 
-// Finishes the split tiles of a stream-K launch: one workgroup per remainder tile
-// (tiles D .. T - 1), laid out like the MFMA waves of the product kernel (8 waves,
-// the same accumulator tiles per lane), adds the partials of the runs that cover
-// the tile in run order and runs the same epilogue. Workgroups of tiles that one
-// run finished exit at once.
+// Finishes the split tiles of a stream-K launch. The remainder tiles (D .. T - 1)
+// are summed in 32-row blocks of the MFMA waves' sub-tiles: workgroup
+// (8 t + w) TM + i is one wave laid out like MFMA wave w of the product kernel (the
+// same accumulator tiles per lane), adds row block i of that wave's share of the
+// partials of the runs covering tile D + t in run order, and runs the same epilogue
+// on it. The blocks are independent (the cross-entropy statistics are per row), and
+// a few tiles cut into many pieces are read by as many single-wave workgroups as
+// possible, since each wave's sum is bound by its loads' latency. Workgroups of
+// tiles that one run finished exit at once.
 template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(64 * NCW) void gemm_bf16_sk_fixup_kernel(GemmArgs g) {
+__global__ __launch_bounds__(64) void gemm_bf16_sk_fixup_kernel(GemmArgs g) {
   constexpr int WM = NCW / 2, WN = 2;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int64_t SLOT = (int64_t)BM * BN / 4;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x;
+  const int i = blockIdx.x % TM, wave = (blockIdx.x / TM) % NCW;
+  const int ti = blockIdx.x / (TM * NCW);  // counted from D
   const int wm = wave / WN, wn = wave % WN;
   const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.N + BN - 1) / BN;
   const int nk = (g.K + BK - 1) / BK;
   const int T = tiles_m * tiles_n, D = T / kGrid * kGrid;
   const int U = (T - D) * nk;
   const int per = (U + kGrid - 1) / kGrid;
-  const int ti = blockIdx.x;  // counted from D
   const int ua = ti * nk;
   const int vf = ua / per, vl = (ua + nk - 1) / per;
   if (vf == vl) return;
   const f32x4* part = reinterpret_cast<const f32x4*>(g.sk_part);
-  const int64_t wofs = (int64_t)wave * TM * TN * 4 * 64;
-  f32x16 acc[TM][TN];
-  // Per row block i, the partials are loaded FG at a time before they are added, so
-  // a tile cut into many pieces waits for one load latency per group rather than
-  // per piece. The sum is still ((P_vf + P_vf+1) + ...) in run order.
-  constexpr int FG = 3;
+  const int64_t bofs = ((int64_t)wave * TM + i) * TN * 4 * 64;
+  f32x16 acc[1][TN];
+  // The partials are loaded FG pieces at a time before they are added, so a tile cut
+  // into many pieces waits for one load latency per group rather than per piece.
+  // The sum is still ((P_vf + P_vf+1) + ...) in run order.
+  constexpr int FG = 4;
+  for (int u0 = vf; u0 <= vl; u0 += FG) {
+    f32x4 x[FG][TN][4];
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
-    for (int u0 = vf; u0 <= vl; u0 += FG) {
-      f32x4 x[FG][TN][4];
+    for (int gi = 0; gi < FG; ++gi)
+      if (u0 + gi <= vl) {
+        const int u = u0 + gi;
+        const f32x4* src = part + (2LL * u + (ti == u * per / nk ? 0 : 1)) * SLOT + bofs;
 #pragma unroll
-      for (int gi = 0; gi < FG; ++gi)
-        if (u0 + gi <= vl) {
-          const int u = u0 + gi;
-          const f32x4* src = part + (2LL * u + (ti == u * per / nk ? 0 : 1)) * SLOT + wofs;
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
+          for (int q = 0; q < 4; ++q) x[gi][j][q] = src[(j * 4 + q) * 64 + lane];
+      }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) x[gi][j][q] = src[((i * TN + j) * 4 + q) * 64 + lane];
-        }
+    for (int gi = 0; gi < FG; ++gi)
+      if (u0 + gi <= vl) {
 #pragma unroll
-      for (int gi = 0; gi < FG; ++gi)
-        if (u0 + gi <= vl) {
+        for (int j = 0; j < TN; ++j)
 #pragma unroll
-          for (int j = 0; j < TN; ++j)
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-              for (int r = 0; r < 4; ++r)
-                acc[i][j][4 * q + r] = u0 + gi == vf ? x[gi][j][q][r] : acc[i][j][4 * q + r] + x[gi][j][q][r];
-        }
-    }
+            for (int r = 0; r < 4; ++r)
+              acc[0][j][4 * q + r] = u0 + gi == vf ? x[gi][j][q][r] : acc[0][j][4 * q + r] + x[gi][j][q][r];
+      }
+  }
   int tm, tn;
   tile_rc(D + ti, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int am = wm * WTM, bn = wn * WTN;
+  const int am = wm * WTM + i * 32, bn = wn * WTN;
   epilogue<EPI>(acc, g, m0 + am, n0 + bn, lane);
 }
 
@@ -783,7 +786,10 @@ hipError_t launch(const GemmArgs& g, hipStream_t s) {
   if (tiles == 0) return hipSuccess;
   if (g.sk_part && sk_applies(tiles, g.K)) {
     hipLaunchKernelGGL((gemm_bf16_sk_kernel<BM, BN, A_K, B_K, EPI>), dim3(kGrid), dim3(NT), 0, s, g);
-    hipLaunchKernelGGL((gemm_bf16_sk_fixup_kernel<BM, BN, EPI>), dim3(tiles % kGrid), dim3(64 * NCW), 0, s, g);
+    // one single-wave workgroup per (remainder tile, MFMA wave, 32-row block)
+    constexpr int fix_per_tile = NCW * (BM / (NCW / 2) / 32);
+    hipLaunchKernelGGL((gemm_bf16_sk_fixup_kernel<BM, BN, EPI>), dim3((tiles % kGrid) * fix_per_tile), dim3(64), 0, s,
+                       g);
     return hipGetLastError();
   }
   // one workgroup per CU (the LDS ring allows no more), a multiple of 8 for the XCD split
