@@ -9,15 +9,15 @@
 // only move data: they load the next 64-key stage from global memory into
 // registers (buffer loads, which read as zero past the last key) and write it
 // to LDS, K as [key][d] and V transposed to [d][key] through a register
-// transpose, while the compute waves work on the current stage (three LDS
+// transpose, while the compute waves work on the current stages (four LDS
 // slots, one barrier per stage). Each SIMD thus runs one compute wave, whose
 // MFMAs and softmax arithmetic overlap with the other wave's loads and LDS
 // writes.
 //
-// The compute wave is software-pipelined by one stage: the scores of stage
-// i + 1 (whose K is already in LDS) are issued in the same basic block as the
-// softmax of stage i, so the MFMA unit works on them while the VALU forms
-// exp2 and the bf16 P of stage i; the P V product of stage i follows. The
+// The compute wave is software-pipelined two stages deep: the P V product of
+// stage i - 1 and the scores of stage i + 1 (whose K is already in LDS) are
+// issued in the same basic block as the softmax of stage i, so the MFMA unit
+// works on them while the VALU forms exp2 and the bf16 P of stage i. The
 // order of every accumulation is unchanged, so the output is bit-identical to
 // the unpipelined schedule.
 //
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
   constexpr int NVT = (KVB / 8) * (D / 4);  // V tasks of 8 keys x 4 d
   constexpr int SK = KVB * D;               // elements per K (and per V^T) stage
   static_assert(KPER >= 1 && NVT <= NP && NVT % 64 == 0, "stage shape");
-  __shared__ __attribute__((aligned(16))) uint16_t smem[3 * 2 * SK];  // [slot][K | V^T], stage i in slot i % 3
+  __shared__ __attribute__((aligned(16))) uint16_t smem[4 * 2 * SK];  // [slot][K | V^T], stage i in slot i % 4
 
   const int item = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (item >= n_items) return;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
     if (nkv > 2) load_kv(2 * KVB);
     __syncthreads();
     for (int it = 0; it < nkv; ++it) {
-      if (it + 2 < nkv) store_kv((it + 2) % 3);
+      if (it + 2 < nkv) store_kv((it + 2) % 4);
       if (it + 3 < nkv) load_kv((it + 3) * KVB);
       __syncthreads();
     }
@@ -228,19 +228,55 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
       }
   };
 
-  // Software pipeline: while the softmax of stage i runs on the VALU, the scores
-  // of stage i + 1 run on the MFMA unit (its K is already in LDS).
+  // O^T += V^T P^T of one stage over its 16-key groups 2t + s2; P^T lane (lr, hh)
+  // holds keys {4hh + 0..3, 8 + 4hh + 0..3} of the group = V^T chunk 2(2t + s2) + hh.
+  auto pv = [&](const uint16_t* sV, const bf16x8(&pb)[2][2], const bf16x8(&pl)[2][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int i = 0; i < DT; ++i) {
+          const int d = 32 * i + lr;
+          const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((4 * t + 2 * s2 + hh) ^ swz_v(d)) << 3));
+          ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][s2], ot[i], 0, 0, 0);
+          if constexpr (SPLIT) ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[t][s2], ot[i], 0, 0, 0);
+        }
+  };
+
+  // Software pipeline, two stages deep: one basic block holds the softmax of stage
+  // i (VALU), the P V product of stage i - 1 and the scores of stage i + 1 (MFMA),
+  // so the MFMA unit works while the VALU forms the exponentials. The stage's K and
+  // V sit in LDS slot i % 4: K(i + 1) and V(i - 1) are read while the loaders write
+  // stage i + 2. When stage i raises the exponent reference, O (then summed through
+  // stage i - 1) is rescaled at the top of the next step, before the P V product of
+  // stage i: every accumulation keeps the order of the one-stage schedule.
   f32x16 sc[2];
+  bf16x8 pp[2][2], ppl[2][2];  // P of the previous stage (hi, lo); zeros before stage 0
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) pp[t][s2] = ppl[t][s2] = bf16x8{};
+  bool pending = false;     // wave-uniform: the previous stage's P V product is still to run
+  bool rescale = false;     // wave-uniform: O is to be scaled by alpha_prev first
+  float alpha_prev = 1.f;
   __syncthreads();
   scores(smem, sc);
   for (int it = 0; it < nkv; ++it) {
     const int kv0 = it * KVB;
-    const uint16_t* sV = smem + (it % 3) * 2 * SK + SK;
-    // K of the next stage; on the last stage a stale slot whose scores go unused.
-    const uint16_t* sKn = smem + ((it + 1) % 3) * 2 * SK;
-    f32x16 sn[2];
-    // Wave-uniform: skip the stage if its first key is above the diagonal or past the end.
-    if (!((CAUSAL && kv0 > qw) || kv0 >= s)) {
+    if (rescale) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ot[i][e] *= alpha_prev;
+      rescale = false;
+    }
+    // V of the previous stage (before stage 0: stage 0's V, multiplied by zero P)
+    const uint16_t* sVp = smem + (it == 0 ? 0 : (it + 3) % 4) * 2 * SK + SK;
+    const uint16_t* sKn = smem + ((it + 1) % 4) * 2 * SK;  // K of the next stage
+    // Wave-uniform: skip the stage if its first key is above the diagonal. Such stages
+    // only follow the wave's last live one. (Every stage of the walk starts below s.)
+    if (!(CAUSAL && kv0 > qw)) {
       // S^T accumulator lane (lr, hh), reg e of tile t: key kv0 + 32t + 8(e/4) + 4hh + e%4, query qrow.
       if ((CAUSAL && kv0 + KVB - 1 > qw) || kv0 + KVB > s) {
         // key - (kv0 + 4hh) = 32t + 8(e/4) + e%4 may not exceed lim.
@@ -257,16 +293,11 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
       const float mt = xhalf_max(mx) * scale_log2;
       // Raise the reference only when some row's maximum has passed it by more
       // than kTau; rows that have not keep their reference (factor 1).
-      if (__builtin_amdgcn_ballot_w64(mt > m_i + kTau) != 0) {
-        const float mn = fmaxf(m_i, mt);
-        const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_i - mn);
-        l_i *= alpha;
-#pragma unroll
-        for (int i = 0; i < DT; ++i)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) ot[i][e] *= alpha;
-        m_i = mn;
-      }
+      const bool raise = __builtin_amdgcn_ballot_w64(mt > m_i + kTau) != 0;
+      const float mn = raise ? fmaxf(m_i, mt) : m_i;
+      const float alpha = (mn == kNegInf) ? 1.f : __builtin_amdgcn_exp2f(m_i - mn);
+      l_i = raise ? l_i * alpha : l_i;
+      m_i = mn;
       const float mref = m_i == kNegInf ? 0.f : m_i;
       float rs = 0.f;
       bf16x8 pb[2][2], pl[2][2];
@@ -287,28 +318,36 @@ __global__ __launch_bounds__(NT) void attn_fwd_kernel(const uint16_t* __restrict
           pb[t][s2] = __builtin_bit_cast(bf16x8, u);
           if constexpr (SPLIT) pl[t][s2] = __builtin_bit_cast(bf16x8, ul);
         }
+      pv(sVp, pp, ppl);
+      f32x16 sn[2];
       scores(sKn, sn);
-      // O^T += V^T P^T over the 16-key groups 2t + s2; P^T lane (lr, hh) holds
-      // keys {4hh + 0..3, 8 + 4hh + 0..3} of the group = V^T chunk 2(2t + s2) + hh.
+      sc[0] = sn[0];
+      sc[1] = sn[1];
+      l_i += rs;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2)
-#pragma unroll
-          for (int i = 0; i < DT; ++i) {
-            const int d = 32 * i + lr;
-            const bf16x8 vf = *reinterpret_cast<const bf16x8*>(sV + d * KVB + (((4 * t + 2 * s2 + hh) ^ swz_v(d)) << 3));
-            ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[t][s2], ot[i], 0, 0, 0);
-            if constexpr (SPLIT) ot[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[t][s2], ot[i], 0, 0, 0);
-          }
-      l_i += rs;
-    } else {
-      scores(sKn, sn);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          pp[t][s2] = pb[t][s2];
+          if constexpr (SPLIT) ppl[t][s2] = pl[t][s2];
+        }
+      pending = true;
+      rescale = raise;
+      alpha_prev = alpha;
+    } else if (pending) {
+      pv(sVp, pp, ppl);
+      pending = false;
     }
-    sc[0] = sn[0];
-    sc[1] = sn[1];
     __syncthreads();
   }
+  // the last live stage's P V product (its V is still in its slot: the loaders are done)
+  if (rescale) {
+#pragma unroll
+    for (int i = 0; i < DT; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) ot[i][e] *= alpha_prev;
+  }
+  if (pending) pv(smem + ((nkv - 1) % 4) * 2 * SK + SK, pp, ppl);
 
   if (qrow < s) {
     const int ln = opaque(lane), lr2 = ln & 31, hh2 = ln >> 5;
