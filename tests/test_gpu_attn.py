@@ -31,9 +31,9 @@ def test_attn_core(b, s, Hl, d, causal):
     assert_bf16_close(f64_host(O), ref, "O")
 
 
-# The kernel keeps up to three 64-key stages of K and V in LDS: sequences of one,
-# two, three and four stages, and lengths one key past a stage boundary, exercise
-# every start-up and drain path of that ring.
+# The kernels keep a ring of 64-key stages of K and V in LDS (four stages for
+# d <= 128, two for d = 384): sequences of one to five stages, and lengths one key
+# past a stage boundary, exercise every start-up, wrap and drain path of that ring.
 @pytest.mark.parametrize("s", [63, 64, 65, 128, 129, 192, 193, 256, 257])
 @pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, True), (384, True), (384, False)])
 def test_attn_core_stage_counts(s, d, causal):
@@ -48,6 +48,27 @@ def test_attn_core_stage_counts(s, d, causal):
     w = Hl * d
     ref = oracle.attn_core(q[:, :w], q[:, w:2 * w], q[:, 2 * w:], b, s, Hl, d, causal)
     assert_bf16_close(f64_host(O), ref, "O")
+
+
+# The training variant (P as a hi/lo bf16 pair, and the log-sum-exp written for the
+# backward) over the same ring paths, including the wrap of the four-stage ring.
+@pytest.mark.parametrize("s", [64, 65, 192, 257, 320, 321])
+@pytest.mark.parametrize("d,causal", [(128, True), (128, False), (64, False), (384, True)])
+def test_attn_core_train_stage_counts(s, d, causal):
+    note(f"attn_core_train stages s={s} d={d} causal={causal}")
+    b, Hl = 1, 2
+    rng = np.random.default_rng(900 + s + d)
+    qkv = bf16_bits(draw_normal_f32(rng, (b * s, 3 * Hl * d), 1.0))
+    O = torch.empty(b * s, Hl * d, dtype=torch.bfloat16, device=DEV)
+    lse = torch.full((b, Hl, s), float("nan"), dtype=torch.float32, device=DEV)
+    tp.attn_core_train(bf16_dev(qkv), O, lse, b, s, Hl, d, causal)
+    torch.cuda.synchronize()
+    q = bf16_bits_to_f64(qkv)
+    w = Hl * d
+    ref = oracle.attn_core(q[:, :w], q[:, w:2 * w], q[:, 2 * w:], b, s, Hl, d, causal)
+    assert_bf16_close(f64_host(O), ref, "O")
+    ref_lse = oracle.attn_lse(q[:, :w], q[:, w:2 * w], b, s, Hl, d, causal)
+    np.testing.assert_allclose(f64_host(lse), ref_lse, rtol=0, atol=1e-4)
 
 
 # Ragged lengths of one to sixteen 64-key stages per query block, d = 64 and 128.
