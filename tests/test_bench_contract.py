@@ -53,14 +53,16 @@ def test_traffic_follows_the_committed_record():
 
 
 def test_traffic_is_null_once_a_source_changes(tmp_path):
-    # a copy of the tree's record and sources, one source edited
+    # a copy of the record and its sources, the record's hashes taken from the copies;
+    # then one source is edited
     (tmp_path / "profiles").mkdir()
-    shutil.copy(os.path.join(ROOT, "profiles", "hbm_traffic.json"), tmp_path / "profiles" / "hbm_traffic.json")
     csrc = tmp_path / "attention_shard_math_amd" / "csrc"
     csrc.mkdir(parents=True)
     rec = json.load(open(os.path.join(ROOT, "profiles", "hbm_traffic.json")))
     for name in rec["source_sha256"]:
         shutil.copy(os.path.join(ROOT, "attention_shard_math_amd", "csrc", name), csrc / name)
+        rec["source_sha256"][name] = hashlib.sha256((csrc / name).read_bytes()).hexdigest()
+    (tmp_path / "profiles" / "hbm_traffic.json").write_text(json.dumps(rec))
     bench = _bench_module()
     bench.ROOT = str(tmp_path)
     assert bench.traffic_from_profiles("mlp_col_gemm_gelu") is not None
