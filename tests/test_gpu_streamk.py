@@ -56,6 +56,24 @@ def test_streamk_matches_tile_kernel(M, K, N):
     assert err < 1e-5, err
 
 
+# Ragged shapes drawn once from a seeded generator (M any size, N and K multiples of 8),
+# kept where the last round is at most half full: 9 to 108 remainder tiles, two with a
+# whole round first (286 and 265 tiles), 58 to 140 k-stages, and M = 1. Each split
+# tile's pieces are summed by the fixup's single-wave row blocks.
+@pytest.mark.parametrize("M,K,N", [(767, 2616, 472), (475, 1864, 6712), (731, 3680, 6728), (2816, 3640, 4808),
+                                   (1, 2200, 5384), (1792, 2272, 776), (215, 1832, 6144), (202, 2080, 2696),
+                                   (2303, 4480, 1624), (1279, 4456, 10168), (512, 2848, 2296),
+                                   (1281, 3544, 3080)])
+def test_streamk_ragged_shapes(M, K, N):
+    note(f"stream-K ragged row linear M={M} K={K} N={N}")
+    Y, W = _inputs(M, K, N, 7 * M + K + N)
+    sk = _row_linear(Y, W, True)
+    tile = _row_linear(Y, W, False)
+    assert not torch.isnan(sk).any()
+    err = float((sk.double() - tile.double()).abs().max() / tile.double().abs().max())
+    assert err < 1e-5, err
+
+
 def test_streamk_repeatable():
     note("stream-K repeatability")
     Y, W = _inputs(64, 12288, 384, 5)
