@@ -103,6 +103,32 @@ def test_ragged_multi_tile(M, h, f_full, N):
     _bf16_mlp_case(M, h, f_full, N, 2000 + M, 0.05)
 
 
+def test_streamk_epilogues():
+    """A shard whose column GEMM, row GEMM, dU and dX products all take the stream-K
+    path (16 tiles of 48 k-stages, M = 300, h = f = 1536): the erf-GeLU epilogue (U, Y),
+    the float32 one (Z, dX) and the GeLU' one (dU) then run on summed partials in the
+    fixup kernel, and every output is compared with the oracle."""
+    M, h, f = 300, 1536, 1536
+    note(f"bf16 mlp through stream-K M={M} h={h} f={f}")
+    fws = tp.mlp_fwd_workspace(M, h, f)
+    assert fws > 0, "the column and row GEMMs of this shape should take the stream-K path"
+    inp = mlp_inputs(M, h, f, 1, "bf16", 4242, 1.0, 0.05, 1.0)
+    A_i, B_i = inp["shards"][0]
+    X, dZ, A, B = bf16_dev(inp["X"]), bf16_dev(inp["dZ"]), bf16_dev(A_i), bf16_dev(B_i)
+    U, Y, Z = _alloc(M, h, f, torch.bfloat16)
+    ws = torch.empty(fws, dtype=torch.uint8, device=DEV)
+    tp.mlp_fwd(X, A, B, Y, Z, U_i=U, ws=ws)
+    dX, dA, dB, _ = _run_bwd(X, A, B, U, Y, dZ, M, h, f)
+    torch.cuda.synchronize()
+    Xo, dZo = bf16_bits_to_f64(inp["X"]), bf16_bits_to_f64(inp["dZ"])
+    Ao, Bo = bf16_bits_to_f64(A_i), bf16_bits_to_f64(B_i)
+    r = oracle.mlp_fwd_shard(Xo, Ao, Bo)
+    g = oracle.mlp_bwd_shard(Xo, Ao, Bo, r["U"], r["Y"], dZo)
+    for name, got, want in (("U", U, r["U"]), ("Y", Y, r["Y"]), ("Z", Z, r["Z"]), ("dX", dX, g["dX"]),
+                            ("dA", dA, g["dA"]), ("dB", dB, g["dB"])):
+        assert_bf16_close(f64_host(got), want, name)
+
+
 def test_empty_batch():
     note("mlp M=0")
     h, f = 64, 128
