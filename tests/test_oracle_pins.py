@@ -459,6 +459,24 @@ class TestVocabCrossEntropy:
         np.testing.assert_allclose(r["loss_rows"], want, rtol=1e-12, atol=1e-12)
         assert abs(r["loss"] - want.sum()) < 1e-10
 
+    @pytest.mark.parametrize("N", [1, 3, 5])
+    def test_combine_of_column_slices_is_the_full_cross_entropy(self, N):
+        # per-slice sums of exp and target logits, formed here from a logits matrix cut
+        # into N column slices, combine to scipy's cross-entropy over all the columns
+        from scipy.special import log_softmax
+        rng = np.random.default_rng(80 + N)
+        logits = rng.standard_normal((7, 30)) * 3
+        t = rng.integers(0, 30, 7)
+        cuts = np.linspace(0, 30, N + 1).astype(int)
+        sums, tls = [], []
+        for lo, hi in zip(cuts[:-1], cuts[1:]):
+            sums.append(np.exp(logits[:, lo:hi]).sum(axis=1))
+            tls.append(np.where((t >= lo) & (t < hi), logits[np.arange(7), np.clip(t, lo, hi - 1)], 0.0))
+        r = oracle.vocab_ce_combine(sums, tls)
+        want = -log_softmax(logits, axis=1)[np.arange(7), t]
+        np.testing.assert_allclose(r["loss_rows"], want, rtol=1e-12, atol=1e-12)
+        assert abs(r["loss"] - want.sum()) < 1e-10
+
     def test_shift_invariance(self):
         # adding one vector u to every row of E adds H u to every logit of a row,
         # which the softmax cancels
@@ -528,6 +546,12 @@ class TestSequenceParallel:
         np.testing.assert_array_equal(seqpar.all_gather(scattered), full)
         for i in range(N):
             np.testing.assert_array_equal(scattered[i], full[3 * i:3 * (i + 1)])
+
+    @pytest.mark.parametrize("s,N", [(16, 1), (16, 2), (16, 4), (24, 8)])
+    def test_row_slices_partition_the_rows_in_rank_order(self, s, N):
+        rows = [np.arange(s)[seqpar.row_slice(s, N, i)] for i in range(N)]
+        assert all(len(r) == s // N for r in rows)
+        np.testing.assert_array_equal(np.concatenate(rows), np.arange(s))
 
     def test_dropout_residual(self):
         rng = np.random.default_rng(15)
@@ -666,6 +690,19 @@ class TestSequenceParallelBackward:
     """Backward of the sequence-parallel block: LayerNorm's backward against torch
     float64 autograd and finite differences; the whole block's gradients against
     autograd of the unsharded block."""
+
+    def test_dropout_bwd_is_the_adjoint_of_dropout(self):
+        # Dropout with a fixed mask is linear in its input, so its backward is the
+        # adjoint: dropout_bwd(dY)[k] = <dY, Dropout(e_k)> for every unit input e_k
+        rng = np.random.default_rng(74)
+        keep = (rng.random((3, 5)) < 0.6).astype(np.uint8)
+        dY = rng.standard_normal((3, 5))
+        for kp, p in ((keep, 0.7), (None, 1.0)):
+            got = seqpar.dropout_bwd(dY, kp, p)
+            for idx in np.ndindex(3, 5):
+                e = np.zeros((3, 5))
+                e[idx] = 1.0
+                assert abs(got[idx] - (dY * seqpar.dropout_residual(np.zeros((3, 5)), e, kp, p)).sum()) < 1e-15
 
     def test_layernorm_bwd_torch(self):
         rng = np.random.default_rng(71)
